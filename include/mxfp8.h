@@ -1,0 +1,180 @@
+/*
+ * mxfp8.h -- C ABI of the MI355X (gfx950) MXFP8 routed-experts SwiGLU MLP library.
+ *
+ * What the library computes, with the passages that define it:
+ *
+ *  - MXFP8 block quantization: tensors are split in groups of 32 consecutive
+ *    elements (afd-plugin PR #475 "quantize the A2E FFN transport to MXFP8",
+ *    sections "Purpose" and "Test Plan"); each group stores one E8M0 scale byte
+ *    and 32 E4M3 codes. The scale exponent is floor(log2(amax)) - 8 clamped to
+ *    [-127, 127] and the codes are round-to-nearest-even saturated to +-448 (the
+ *    OCP MX v1.0 MXFP8 rule). An all-zero group gets scale byte 0x00; a group
+ *    holding NaN or Inf gets 0xFF and NaN codes (0x7F | sign).
+ *    E8M0 byte b means 2^(b-127); 0x00 is 2^-127 and 0xFF is NaN (PR #475,
+ *    review on E8M0 endpoint decoding).
+ *  - "Dual" quantization (torchtitan PR #12 "Wire the fully-fused grouped-GEMM
+ *    MXFP8 plan behind fusion_plan", section "What it adds"): the same matrix
+ *    quantized along rows (q_row [rows, cols], s_row [rows, cols/32]) and along
+ *    columns, stored transposed (q_col [cols, rows], s_col [cols, rows/32]).
+ *  - The routed-experts SwiGLU MLP as four fused ops (same section): FC1
+ *    grouped GEMM + SwiGLU + dual MXFP8 quantization, FC2 GEMM, fused dSwiGLU
+ *    backward, wgrad -- over a padded expert-major token layout with per-expert
+ *    alignment pad_multiple (128 or 256). Parameters are stock: w1 (gate) and
+ *    w3 (up) [E, F, D], w2 [E, D, F], all BF16; the library packs w1/w3 into a
+ *    [E, 2F, D] 32-block order internally. The BF16 post-activation is never
+ *    written (torchtitan PR #2 "fused gated-activation (SwiGLU) + MXFP8
+ *    quantization kernel override", section "Summary").
+ *
+ * Conventions (torchtitan PR #2, section "Fail-loud contract"):
+ *  - Every pointer argument is a DEVICE pointer unless marked "host".
+ *  - The caller owns every buffer. The library never allocates or frees device
+ *    memory, never synchronises (except mxf_read_status) and keeps no pointer
+ *    after a call returns.
+ *  - All arguments are validated on the host before anything is launched. On
+ *    failure nothing is launched, a status code is returned and
+ *    mxf_last_error() names the offending argument and value. There is no
+ *    fallback path: an unsupported configuration is an error.
+ *  - Token offsets live on the device and are checked there (non-decreasing,
+ *    multiples of pad_multiple, within capacity, counts <= segment). A
+ *    violation makes every kernel of the call skip its work and records a
+ *    non-zero status word in the workspace, read with mxf_read_status.
+ *  - All work is enqueued on the given stream (a hipStream_t passed as void*;
+ *    NULL is the default stream). Calls that share a workspace must not overlap.
+ */
+#ifndef MXFP8_H
+#define MXFP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXF_ABI_VERSION 1
+
+typedef enum {
+  MXF_OK = 0,
+  MXF_E_NULL = 1,      /* a required pointer is NULL */
+  MXF_E_SHAPE = 2,     /* a dimension is negative, not a required multiple, or too large */
+  MXF_E_ALIGN = 3,     /* a pointer is not 16-byte aligned */
+  MXF_E_DEVICE = 4,    /* the current device is not a gfx950 GPU */
+  MXF_E_ARG = 5,       /* an enum/flag argument is out of range */
+  MXF_E_HIP = 6        /* the HIP runtime reported an error (message in mxf_last_error) */
+} mxf_status;
+
+/* Device-side status word values (mxf_read_status). */
+#define MXF_DEV_OK 0
+#define MXF_DEV_BAD_OFFSETS 1   /* offs/counts violate the layout contract; no output was written */
+
+/* ABI version of the loaded library; equals MXF_ABI_VERSION of the header it was built with. */
+int mxf_abi_version(void);
+
+/* Capability query for a device ordinal. On success *caps gets bit 0 set when the device is
+ * a gfx950 GPU (block-scaled FP8 MFMA), which every compute entry point requires.
+ * Errors: MXF_E_NULL (caps), MXF_E_HIP (bad ordinal). */
+#define MXF_CAP_GFX950 1u
+mxf_status mxf_query_device(int device, uint32_t* caps /* host */);
+
+/* Thread-local, NUL-terminated description of the last error on this thread ("" if none).
+ * Valid until the next library call on the same thread. */
+const char* mxf_last_error(void);
+
+/* ------------------------------------------------------------------ standalone quantizer */
+
+#define MXF_ROW 1u   /* groups along each row    -> q_row [rows, cols], s_row [rows, cols/32] */
+#define MXF_COL 2u   /* groups along each column -> q_col [cols, rows], s_col [cols, rows/32] */
+
+/* MXFP8 quantization of a row-major BF16 matrix x [rows, cols] (see top of file).
+ * mode: MXF_ROW, MXF_COL or both (dual: x is read once).
+ * Requires cols % 32 == 0; with MXF_COL also rows % 32 == 0; rows, cols >= 0. An empty matrix
+ * (rows or cols 0) is a no-op that accepts NULL pointers.
+ * Outputs not selected by mode may be NULL. All outputs are dense row-major u8 arrays.
+ * Pointers must be 16-byte aligned (scale arrays: any alignment).
+ * Errors: MXF_E_NULL, MXF_E_SHAPE, MXF_E_ALIGN, MXF_E_ARG (mode), MXF_E_DEVICE, MXF_E_HIP. */
+mxf_status mxfp8_quantize(const void* x, int64_t rows, int64_t cols, uint32_t mode,
+                          void* q_row, void* s_row, void* q_col, void* s_col, void* stream);
+
+/* ------------------------------------------------------------------ routed-experts MLP */
+
+#define MXF_OUT_F32 1u     /* y, dx, dw1, dw3, dw2 are FP32 instead of BF16 */
+#define MXF_DEBUG_F32 2u   /* also store the FP32 FC1 output and FP32 dh (FC2 dgrad) in the
+                              workspace (tensors MXF_T_H13_F32, MXF_T_DH_F32) */
+
+typedef struct {
+  int32_t E;             /* local experts, 1 .. 1024 */
+  int32_t D;             /* model dim, multiple of 128 */
+  int32_t F;             /* expert hidden dim, multiple of 128 */
+  int32_t pad_multiple;  /* 128 or 256: every expert segment is a multiple of this */
+  int64_t m_capacity;    /* rows allocated in x/y/dy/dx; multiple of pad_multiple */
+  uint32_t flags;        /* MXF_OUT_F32 | MXF_DEBUG_F32 */
+} mxf_mlp_desc;
+
+/* Tensors held in the caller's buffers (for tests and inspection). Region: 0 = workspace,
+ * 1 = saved (forward -> backward context). Codes u8, scales u8 (E8M0), h13 BF16. */
+typedef enum {
+  MXF_T_STATUS = 0,                                       /* int32 status word (workspace) */
+  MXF_T_XQ_R, MXF_T_XS_R,                                 /* [Mcap, D], [Mcap, D/32]       (ws)    */
+  MXF_T_XQ_C, MXF_T_XS_C,                                 /* [D, Mcap], [D, Mcap/32]       (saved) */
+  MXF_T_W13Q_R, MXF_T_W13S_R,                             /* [E, 2F, D], [E, 2F, D/32]     (ws)    */
+  MXF_T_W13Q_C, MXF_T_W13S_C,                             /* [E, D, 2F], [E, D, 2F/32]     (saved) */
+  MXF_T_W2Q_R, MXF_T_W2S_R,                               /* [E, D, F], [E, D, F/32]       (ws)    */
+  MXF_T_W2Q_C, MXF_T_W2S_C,                               /* [E, F, D], [E, F, D/32]       (saved) */
+  MXF_T_H13,                                              /* [Mcap, 2F] BF16, packed order (saved) */
+  MXF_T_HQ_R, MXF_T_HS_R,                                 /* [Mcap, F], [Mcap, F/32]       (ws)    */
+  MXF_T_HQ_C, MXF_T_HS_C,                                 /* [F, Mcap], [F, Mcap/32]       (saved) */
+  MXF_T_DYQ_R, MXF_T_DYS_R, MXF_T_DYQ_C, MXF_T_DYS_C,     /* like X                        (ws)    */
+  MXF_T_DHQ_R, MXF_T_DHS_R,                               /* [Mcap, 2F], [Mcap, 2F/32]     (ws)    */
+  MXF_T_DHQ_C, MXF_T_DHS_C,                               /* [2F, Mcap], [2F, Mcap/32]     (ws)    */
+  MXF_T_H13_F32,                                          /* [Mcap, 2F] FP32 (ws, MXF_DEBUG_F32)   */
+  MXF_T_DH_F32,                                           /* [Mcap, F] FP32  (ws, MXF_DEBUG_F32)   */
+  MXF_T_COUNT
+} mxf_tensor;
+
+/* Bytes the caller must provide for `saved` and for `workspace` (one workspace serves both
+ * grouped_mlp_fwd and grouped_mlp_bwd). Return 0 when the descriptor is invalid. */
+size_t mxf_mlp_saved_bytes(const mxf_mlp_desc* desc /* host */);
+size_t mxf_mlp_workspace_bytes(const mxf_mlp_desc* desc /* host */);
+
+/* Where tensor `which` lives: *region (0 workspace, 1 saved), *offset and *bytes in it.
+ * Errors: MXF_E_NULL, MXF_E_SHAPE (desc), MXF_E_ARG (which). */
+mxf_status mxf_mlp_tensor(const mxf_mlp_desc* desc /* host */, int which, int* region /* host */,
+                          size_t* offset /* host */, size_t* bytes /* host */);
+
+/* Forward. offs: int32 [E+1] (offs[0] = 0, non-decreasing, multiples of pad_multiple,
+ * offs[E] <= m_capacity); expert e owns rows [offs[e], offs[e+1]). counts: int32 [E] real
+ * rows per expert (counts[e] <= offs[e+1]-offs[e]) or NULL (every row real). Rows in
+ * [offs[e]+counts[e], offs[e+1]) are pad: read as zero, written as zero. Rows at or after
+ * offs[E] are never read or written.
+ * x [m_capacity, D] BF16; w1, w3 [E, F, D] BF16; w2 [E, D, F] BF16;
+ * y [m_capacity, D] BF16 (FP32 with MXF_OUT_F32).
+ * saved: mxf_mlp_saved_bytes; keep it unchanged until grouped_mlp_bwd has run.
+ * workspace: mxf_mlp_workspace_bytes. All pointers 16-byte aligned. */
+mxf_status grouped_mlp_fwd(const mxf_mlp_desc* desc /* host */, const int32_t* offs,
+                           const int32_t* counts, const void* x, const void* w1, const void* w3,
+                           const void* w2, void* y, void* saved, void* workspace, void* stream);
+
+/* Backward (straight-through quantization). dy [m_capacity, D] BF16 (pad rows read as zero);
+ * saved as written by grouped_mlp_fwd with the same desc/offs/counts.
+ * dx [m_capacity, D]; dw1, dw3 [E, F, D]; dw2 [E, D, F] -- BF16, or FP32 with MXF_OUT_F32.
+ * Weight gradients are overwritten (not accumulated); an expert with no routed rows gets
+ * exact zeros. */
+mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc /* host */, const int32_t* offs,
+                           const int32_t* counts, const void* dy, const void* saved, void* dx,
+                           void* dw1, void* dw3, void* dw2, void* workspace, void* stream);
+
+/* Synchronises `stream` and copies the device status word of the last fwd/bwd call that
+ * used `workspace` into *device_status (MXF_DEV_OK or MXF_DEV_BAD_OFFSETS). */
+mxf_status mxf_read_status(const void* workspace, void* stream, int32_t* device_status /* host */);
+
+/* Test helpers for the [E, 2F, D] 32-block packing: w13[e, 64j+i] = w1[e, 32j+i] and
+ * w13[e, 64j+32+i] = w3[e, 32j+i] (i < 32), BF16, and its inverse. F % 32 == 0. */
+mxf_status mxf_pack_w13(const void* w1, const void* w3, void* w13, int32_t E, int32_t F,
+                        int32_t D, void* stream);
+mxf_status mxf_unpack_w13(const void* w13, void* w1, void* w3, int32_t E, int32_t F, int32_t D,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXFP8_H */

@@ -1,0 +1,69 @@
+"""MXFP8 routed-experts SwiGLU MLP for MI355X (gfx950).
+
+The compute lives in the HIP library ``libmxfp8.so`` (C ABI: include/mxfp8.h);
+this package is its Python binding. ``MlpContext`` allocates the caller-owned
+``saved`` and ``workspace`` buffers with torch and exposes the library's
+documented intermediate tensors as views, for tests and inspection.
+"""
+from ._abi import (CAP_GFX950, COL, DEBUG_F32, DEV_BAD_OFFSETS, DEV_OK, EXPORTS, LIB_PATH, OUT_F32,
+                   ROW, T, TENSORS, MlpDesc, MxfError, abi_version, grouped_mlp_bwd, grouped_mlp_fwd,
+                   last_error, lib, make_desc, mlp_saved_bytes, mlp_tensor, mlp_workspace_bytes,
+                   mxfp8_quantize, pack_w13, quantize, query_device, read_status, unpack_w13)
+
+# shapes of the documented tensors, as functions of (E, D, F, m_capacity)
+_SHAPES = {
+    "XQ_R": lambda E, D, F, M: (M, D), "XS_R": lambda E, D, F, M: (M, D // 32),
+    "XQ_C": lambda E, D, F, M: (D, M), "XS_C": lambda E, D, F, M: (D, M // 32),
+    "W13Q_R": lambda E, D, F, M: (E, 2 * F, D), "W13S_R": lambda E, D, F, M: (E, 2 * F, D // 32),
+    "W13Q_C": lambda E, D, F, M: (E, D, 2 * F), "W13S_C": lambda E, D, F, M: (E, D, 2 * F // 32),
+    "W2Q_R": lambda E, D, F, M: (E, D, F), "W2S_R": lambda E, D, F, M: (E, D, F // 32),
+    "W2Q_C": lambda E, D, F, M: (E, F, D), "W2S_C": lambda E, D, F, M: (E, F, D // 32),
+    "H13": lambda E, D, F, M: (M, 2 * F),
+    "HQ_R": lambda E, D, F, M: (M, F), "HS_R": lambda E, D, F, M: (M, F // 32),
+    "HQ_C": lambda E, D, F, M: (F, M), "HS_C": lambda E, D, F, M: (F, M // 32),
+    "DYQ_R": lambda E, D, F, M: (M, D), "DYS_R": lambda E, D, F, M: (M, D // 32),
+    "DYQ_C": lambda E, D, F, M: (D, M), "DYS_C": lambda E, D, F, M: (D, M // 32),
+    "DHQ_R": lambda E, D, F, M: (M, 2 * F), "DHS_R": lambda E, D, F, M: (M, 2 * F // 32),
+    "DHQ_C": lambda E, D, F, M: (2 * F, M), "DHS_C": lambda E, D, F, M: (2 * F, M // 32),
+    "H13_F32": lambda E, D, F, M: (M, 2 * F), "DH_F32": lambda E, D, F, M: (M, F),
+    "STATUS": lambda E, D, F, M: (1,),
+}
+
+
+class MlpContext:
+    """Descriptor plus caller-owned device buffers for one MLP configuration."""
+
+    def __init__(self, E, D, F, pad_multiple, m_capacity, flags=0, device="cuda"):
+        import torch
+        self.E, self.D, self.F, self.pad, self.m_capacity, self.flags = E, D, F, pad_multiple, m_capacity, flags
+        self.desc = make_desc(E, D, F, pad_multiple, m_capacity, flags)
+        nsaved = mlp_saved_bytes(self.desc)
+        nws = mlp_workspace_bytes(self.desc)
+        if nsaved == 0 or nws == 0:
+            raise MxfError(2, f"invalid descriptor E={E} D={D} F={F} pad={pad_multiple} m={m_capacity}")
+        self.saved = torch.empty(nsaved, dtype=torch.uint8, device=device)
+        self.workspace = torch.empty(nws, dtype=torch.uint8, device=device)
+
+    def view(self, name):
+        """A typed view of documented tensor `name` inside saved / workspace."""
+        import torch
+        region, off, nbytes = mlp_tensor(self.desc, name)
+        buf = self.saved if region == 1 else self.workspace
+        raw = buf[off:off + nbytes]
+        shape = _SHAPES[name](self.E, self.D, self.F, self.m_capacity)
+        if name == "H13":
+            return raw.view(torch.bfloat16).view(shape)
+        if name in ("H13_F32", "DH_F32"):
+            return raw.view(torch.float32).view(shape)
+        if name == "STATUS":
+            return raw.view(torch.int32)
+        return raw.view(shape)
+
+    def fwd(self, offs, counts, x, w1, w3, w2, y, stream=None):
+        grouped_mlp_fwd(self.desc, offs, counts, x, w1, w3, w2, y, self.saved, self.workspace, stream)
+
+    def bwd(self, offs, counts, dy, dx, dw1, dw3, dw2, stream=None):
+        grouped_mlp_bwd(self.desc, offs, counts, dy, self.saved, dx, dw1, dw3, dw2, self.workspace, stream)
+
+    def status(self, stream=None):
+        return read_status(self.workspace, stream)

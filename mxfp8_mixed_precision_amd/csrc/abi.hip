@@ -1,0 +1,375 @@
+// C ABI of the MXFP8 routed-experts MLP library: argument validation, buffer layout and
+// launch sequencing. The public contract (argument meaning, layout, ownership, errors) is
+// documented in include/mxfp8.h.
+//
+// Fail-loud contract (torchtitan PR #2 "[mxfp8 training] fused gated-activation (SwiGLU) +
+// MXFP8 quantization kernel override", section "Fail-loud contract"): every unsupported
+// configuration is rejected before anything is launched, with a message naming the offending
+// value; there is no fallback path. Data-dependent token counts are checked on the device
+// (the analogue of deferred asserts): the kernels skip their work and a status word records
+// the violation.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kernels.h"
+#include "mxfp8.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+mxf_status fail(mxf_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+mxf_status hip_fail(hipError_t e, const char* what) {
+  return fail(MXF_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define MXF_HIP(call, what)                      \
+  do {                                           \
+    hipError_t _e = (call);                      \
+    if (_e != hipSuccess) return hip_fail(_e, what); \
+  } while (0)
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_cap[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+mxf_status check_device() {
+  int dev = 0;
+  MXF_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MXF_E_DEVICE, "device ordinal %d out of range", dev);
+  int c = g_dev_cap[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    hipDeviceProp_t prop;
+    MXF_HIP(hipGetDeviceProperties(&prop, dev), "hipGetDeviceProperties");
+    c = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_dev_cap[dev].store(c, std::memory_order_relaxed);
+    if (c == 2) return fail(MXF_E_DEVICE, "device %d is %s; this library runs only on gfx950", dev, prop.gcnArchName);
+  }
+  if (c != 1) return fail(MXF_E_DEVICE, "device %d is not a gfx950 GPU", dev);
+  return MXF_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ------------------------------------------------------------------ MLP buffer layout
+
+struct Layout {
+  size_t off[MXF_T_COUNT];
+  size_t bytes[MXF_T_COUNT];
+  int region[MXF_T_COUNT];
+  size_t saved_total;
+  size_t ws_total;
+};
+
+mxf_status check_desc(const mxf_mlp_desc* d) {
+  if (!d) return fail(MXF_E_NULL, "desc is NULL");
+  if (d->E < 1 || d->E > 1024) return fail(MXF_E_SHAPE, "E = %d: must be in [1, 1024]", d->E);
+  if (d->D <= 0 || d->D % 128) return fail(MXF_E_SHAPE, "D = %d: must be a positive multiple of 128", d->D);
+  if (d->F <= 0 || d->F % 128) return fail(MXF_E_SHAPE, "F = %d: must be a positive multiple of 128", d->F);
+  if (d->pad_multiple != 128 && d->pad_multiple != 256)
+    return fail(MXF_E_SHAPE, "pad_multiple = %d: must be 128 or 256", d->pad_multiple);
+  if (d->m_capacity < 0 || d->m_capacity % d->pad_multiple)
+    return fail(MXF_E_SHAPE, "m_capacity = %lld: must be a non-negative multiple of pad_multiple (%d)",
+                (long long)d->m_capacity, d->pad_multiple);
+  if (d->m_capacity > (int64_t)1 << 30)
+    return fail(MXF_E_SHAPE, "m_capacity = %lld: larger than 2^30 rows", (long long)d->m_capacity);
+  if (d->flags & ~(uint32_t)(MXF_OUT_F32 | MXF_DEBUG_F32))
+    return fail(MXF_E_ARG, "flags = 0x%x: unknown bits", d->flags);
+  return MXF_OK;
+}
+
+void make_layout(const mxf_mlp_desc* d, Layout* L) {
+  const size_t M = (size_t)d->m_capacity, D = (size_t)d->D, F = (size_t)d->F, E = (size_t)d->E;
+  const bool dbg = (d->flags & MXF_DEBUG_F32) != 0;
+  memset(L, 0, sizeof(*L));
+  auto put = [&](int t, int region, size_t* cursor, size_t bytes) {
+    L->region[t] = region;
+    L->off[t] = *cursor;
+    L->bytes[t] = bytes;
+    *cursor += (bytes + 255) / 256 * 256;
+  };
+  size_t sv = 0;
+  put(MXF_T_XQ_C, 1, &sv, D * M);
+  put(MXF_T_XS_C, 1, &sv, D * M / 32);
+  put(MXF_T_W13Q_C, 1, &sv, E * D * 2 * F);
+  put(MXF_T_W13S_C, 1, &sv, E * D * 2 * F / 32);
+  put(MXF_T_W2Q_C, 1, &sv, E * F * D);
+  put(MXF_T_W2S_C, 1, &sv, E * F * D / 32);
+  put(MXF_T_H13, 1, &sv, M * 2 * F * 2);
+  put(MXF_T_HQ_C, 1, &sv, F * M);
+  put(MXF_T_HS_C, 1, &sv, F * M / 32);
+  L->saved_total = sv;
+  size_t fw = 0;
+  put(MXF_T_STATUS, 0, &fw, 4);
+  const size_t after_status = fw;
+  put(MXF_T_XQ_R, 0, &fw, M * D);
+  put(MXF_T_XS_R, 0, &fw, M * D / 32);
+  put(MXF_T_W13Q_R, 0, &fw, E * 2 * F * D);
+  put(MXF_T_W13S_R, 0, &fw, E * 2 * F * D / 32);
+  put(MXF_T_W2Q_R, 0, &fw, E * D * F);
+  put(MXF_T_W2S_R, 0, &fw, E * D * F / 32);
+  put(MXF_T_HQ_R, 0, &fw, M * F);
+  put(MXF_T_HS_R, 0, &fw, M * F / 32);
+  put(MXF_T_H13_F32, 0, &fw, dbg ? M * 2 * F * 4 : 0);
+  size_t bw = after_status;  // backward tensors reuse the forward-only workspace
+  put(MXF_T_DYQ_R, 0, &bw, M * D);
+  put(MXF_T_DYS_R, 0, &bw, M * D / 32);
+  put(MXF_T_DYQ_C, 0, &bw, D * M);
+  put(MXF_T_DYS_C, 0, &bw, D * M / 32);
+  put(MXF_T_DHQ_R, 0, &bw, M * 2 * F);
+  put(MXF_T_DHS_R, 0, &bw, M * 2 * F / 32);
+  put(MXF_T_DHQ_C, 0, &bw, 2 * F * M);
+  put(MXF_T_DHS_C, 0, &bw, 2 * F * M / 32);
+  put(MXF_T_DH_F32, 0, &bw, dbg ? M * F * 4 : 0);
+  L->ws_total = fw > bw ? fw : bw;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ exported entry points
+
+extern "C" {
+
+int mxf_abi_version(void) { return MXF_ABI_VERSION; }
+
+const char* mxf_last_error(void) { return g_err.c_str(); }
+
+mxf_status mxf_query_device(int device, uint32_t* caps) {
+  g_err.clear();
+  if (!caps) return fail(MXF_E_NULL, "caps is NULL");
+  *caps = 0;
+  hipDeviceProp_t prop;
+  MXF_HIP(hipGetDeviceProperties(&prop, device), "hipGetDeviceProperties");
+  if (strncmp(prop.gcnArchName, "gfx950", 6) == 0) *caps |= MXF_CAP_GFX950;
+  return MXF_OK;
+}
+
+mxf_status mxfp8_quantize(const void* x, int64_t rows, int64_t cols, uint32_t mode, void* q_row,
+                          void* s_row, void* q_col, void* s_col, void* stream) {
+  g_err.clear();
+  if (mode == 0 || (mode & ~(uint32_t)(MXF_ROW | MXF_COL)))
+    return fail(MXF_E_ARG, "mode = %u: must be MXF_ROW, MXF_COL or both", mode);
+  if (rows < 0 || cols < 0) return fail(MXF_E_SHAPE, "rows = %lld, cols = %lld: negative", (long long)rows, (long long)cols);
+  if (cols % 32) return fail(MXF_E_SHAPE, "cols = %lld: must be a multiple of 32", (long long)cols);
+  if ((mode & MXF_COL) && rows % 32)
+    return fail(MXF_E_SHAPE, "rows = %lld: must be a multiple of 32 for column-wise groups", (long long)rows);
+  if ((rows + 127) / 128 > 0x7FFFFFFFLL || (cols + 127) / 128 > 65535)
+    return fail(MXF_E_SHAPE, "rows = %lld, cols = %lld: too large", (long long)rows, (long long)cols);
+  if (rows == 0 || cols == 0) return MXF_OK;  // nothing to read or write
+  if (!x) return fail(MXF_E_NULL, "x is NULL");
+  if ((mode & MXF_ROW) && (!q_row || !s_row)) return fail(MXF_E_NULL, "q_row/s_row is NULL with MXF_ROW");
+  if ((mode & MXF_COL) && (!q_col || !s_col)) return fail(MXF_E_NULL, "q_col/s_col is NULL with MXF_COL");
+  if (!aligned16(x)) return fail(MXF_E_ALIGN, "x is not 16-byte aligned");
+  if ((mode & MXF_ROW) && !aligned16(q_row)) return fail(MXF_E_ALIGN, "q_row is not 16-byte aligned");
+  if ((mode & MXF_COL) && !aligned16(q_col)) return fail(MXF_E_ALIGN, "q_col is not 16-byte aligned");
+  mxf_status s = check_device();
+  if (s != MXF_OK) return s;
+  MXF_HIP(mxf_launch_quantize(x, rows, cols, mode, q_row, s_row, q_col, s_col, (hipStream_t)stream),
+          "quantize launch");
+  return MXF_OK;
+}
+
+size_t mxf_mlp_saved_bytes(const mxf_mlp_desc* desc) {
+  if (check_desc(desc) != MXF_OK) return 0;
+  Layout L;
+  make_layout(desc, &L);
+  return L.saved_total;
+}
+
+size_t mxf_mlp_workspace_bytes(const mxf_mlp_desc* desc) {
+  if (check_desc(desc) != MXF_OK) return 0;
+  Layout L;
+  make_layout(desc, &L);
+  return L.ws_total;
+}
+
+mxf_status mxf_mlp_tensor(const mxf_mlp_desc* desc, int which, int* region, size_t* offset, size_t* bytes) {
+  g_err.clear();
+  mxf_status s = check_desc(desc);
+  if (s != MXF_OK) return s;
+  if (!region || !offset || !bytes) return fail(MXF_E_NULL, "region/offset/bytes is NULL");
+  if (which < 0 || which >= MXF_T_COUNT) return fail(MXF_E_ARG, "tensor id %d out of range", which);
+  Layout L;
+  make_layout(desc, &L);
+  *region = L.region[which];
+  *offset = L.off[which];
+  *bytes = L.bytes[which];
+  return MXF_OK;
+}
+
+static mxf_status check_mlp_ptrs(const void* const* ptrs, const char* const* names, int n) {
+  for (int i = 0; i < n; ++i) {
+    if (!ptrs[i]) return fail(MXF_E_NULL, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(MXF_E_ALIGN, "%s is not 16-byte aligned", names[i]);
+  }
+  return MXF_OK;
+}
+
+mxf_status grouped_mlp_fwd(const mxf_mlp_desc* desc, const int32_t* offs, const int32_t* counts,
+                           const void* x, const void* w1, const void* w3, const void* w2, void* y,
+                           void* saved, void* workspace, void* stream) {
+  g_err.clear();
+  mxf_status s = check_desc(desc);
+  if (s != MXF_OK) return s;
+  const void* ptrs[] = {x, w1, w3, w2, y, saved, workspace};
+  const char* names[] = {"x", "w1", "w3", "w2", "y", "saved", "workspace"};
+  if ((s = check_mlp_ptrs(ptrs, names, 7)) != MXF_OK) return s;
+  if (!offs) return fail(MXF_E_NULL, "offs is NULL");
+  if ((s = check_device()) != MXF_OK) return s;
+
+  Layout L;
+  make_layout(desc, &L);
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* ws = (uint8_t*)workspace;
+  uint8_t* sv = (uint8_t*)saved;
+  auto T = [&](int t) -> uint8_t* { return (L.region[t] ? sv : ws) + L.off[t]; };
+  const int64_t M = desc->m_capacity, D = desc->D, F = desc->F, E = desc->E;
+  const bool dbg = (desc->flags & MXF_DEBUG_F32) != 0;
+
+  MXF_HIP(mxf_launch_quant_weights(w1, w3, true, E, 2 * F, D, T(MXF_T_W13Q_R), T(MXF_T_W13S_R),
+                                   T(MXF_T_W13Q_C), T(MXF_T_W13S_C), st), "W13 quantize launch");
+  MXF_HIP(mxf_launch_quant_weights(w2, nullptr, false, E, D, F, T(MXF_T_W2Q_R), T(MXF_T_W2S_R),
+                                   T(MXF_T_W2Q_C), T(MXF_T_W2S_C), st), "W2 quantize launch");
+  MXF_HIP(mxf_launch_quant_tokens(x, M, D, offs, counts, (int)E, desc->pad_multiple, T(MXF_T_XQ_R),
+                                  T(MXF_T_XS_R), T(MXF_T_XQ_C), T(MXF_T_XS_C), (int32_t*)T(MXF_T_STATUS), st),
+          "X quantize launch");
+
+  mxf::GemmParams p = {};
+  p.offs = offs;
+  p.counts = counts;
+  p.E = (int)E;
+  p.pad = desc->pad_multiple;
+  p.mcap = M;
+  p.M = M;
+  // FC1 + SwiGLU + dual quantization of h
+  p.A = T(MXF_T_XQ_R); p.As = T(MXF_T_XS_R); p.lda = D; p.ldas = D / 32;
+  p.B = T(MXF_T_W13Q_R); p.Bs = T(MXF_T_W13S_R); p.ldb = D; p.ldbs = D / 32;
+  p.b_es = 2 * F * D; p.bs_es = 2 * F * D / 32;
+  p.N = 2 * F; p.K = D;
+  p.h13 = (uint16_t*)T(MXF_T_H13);
+  p.q_r = T(MXF_T_HQ_R); p.s_r = T(MXF_T_HS_R); p.q_c = T(MXF_T_HQ_C); p.s_c = T(MXF_T_HS_C);
+  p.dbg = dbg ? (float*)T(MXF_T_H13_F32) : nullptr;
+  MXF_HIP(mxf_launch_gemm_mgroup(1, p, st), "FC1 launch");
+  // FC2
+  p.A = T(MXF_T_HQ_R); p.As = T(MXF_T_HS_R); p.lda = F; p.ldas = F / 32;
+  p.B = T(MXF_T_W2Q_R); p.Bs = T(MXF_T_W2S_R); p.ldb = F; p.ldbs = F / 32;
+  p.b_es = D * F; p.bs_es = D * F / 32;
+  p.N = D; p.K = F;
+  p.C = y; p.ldc = D; p.out_f32 = (desc->flags & MXF_OUT_F32) ? 1 : 0;
+  p.dbg = nullptr;
+  MXF_HIP(mxf_launch_gemm_mgroup(0, p, st), "FC2 launch");
+  return MXF_OK;
+}
+
+mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc, const int32_t* offs, const int32_t* counts,
+                           const void* dy, const void* saved, void* dx, void* dw1, void* dw3, void* dw2,
+                           void* workspace, void* stream) {
+  g_err.clear();
+  mxf_status s = check_desc(desc);
+  if (s != MXF_OK) return s;
+  const void* ptrs[] = {dy, saved, dx, dw1, dw3, dw2, workspace};
+  const char* names[] = {"dy", "saved", "dx", "dw1", "dw3", "dw2", "workspace"};
+  if ((s = check_mlp_ptrs(ptrs, names, 7)) != MXF_OK) return s;
+  if (!offs) return fail(MXF_E_NULL, "offs is NULL");
+  if ((s = check_device()) != MXF_OK) return s;
+
+  Layout L;
+  make_layout(desc, &L);
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* ws = (uint8_t*)workspace;
+  uint8_t* sv = (uint8_t*)const_cast<void*>(saved);
+  auto T = [&](int t) -> uint8_t* { return (L.region[t] ? sv : ws) + L.off[t]; };
+  const int64_t M = desc->m_capacity, D = desc->D, F = desc->F, E = desc->E;
+  const bool dbg = (desc->flags & MXF_DEBUG_F32) != 0;
+  const int of32 = (desc->flags & MXF_OUT_F32) ? 1 : 0;
+
+  MXF_HIP(mxf_launch_quant_tokens(dy, M, D, offs, counts, (int)E, desc->pad_multiple, T(MXF_T_DYQ_R),
+                                  T(MXF_T_DYS_R), T(MXF_T_DYQ_C), T(MXF_T_DYS_C), (int32_t*)T(MXF_T_STATUS), st),
+          "dY quantize launch");
+  mxf::GemmParams p = {};
+  p.offs = offs;
+  p.counts = counts;
+  p.E = (int)E;
+  p.pad = desc->pad_multiple;
+  p.mcap = M;
+  // FC2 dgrad + dSwiGLU + dual quantization of dH13
+  p.M = M;
+  p.A = T(MXF_T_DYQ_R); p.As = T(MXF_T_DYS_R); p.lda = D; p.ldas = D / 32;
+  p.B = T(MXF_T_W2Q_C); p.Bs = T(MXF_T_W2S_C); p.ldb = D; p.ldbs = D / 32;
+  p.b_es = F * D; p.bs_es = F * D / 32;
+  p.N = F; p.K = D;
+  p.h13 = (uint16_t*)T(MXF_T_H13);
+  p.q_r = T(MXF_T_DHQ_R); p.s_r = T(MXF_T_DHS_R); p.q_c = T(MXF_T_DHQ_C); p.s_c = T(MXF_T_DHS_C);
+  p.dbg = dbg ? (float*)T(MXF_T_DH_F32) : nullptr;
+  MXF_HIP(mxf_launch_gemm_mgroup(2, p, st), "FC2 dgrad launch");
+  p.dbg = nullptr;
+  p.out_f32 = of32;
+  // FC2 wgrad: dW2[e] = dY^T h over the expert's tokens
+  p.A = T(MXF_T_DYQ_C); p.As = T(MXF_T_DYS_C); p.lda = M; p.ldas = M / 32;
+  p.B = T(MXF_T_HQ_C); p.Bs = T(MXF_T_HS_C); p.ldb = M; p.ldbs = M / 32;
+  p.M = D; p.N = F; p.K = M;
+  p.C = dw2; p.ldc = F; p.c_es = D * F;
+  MXF_HIP(mxf_launch_gemm_kgroup(0, p, st), "FC2 wgrad launch");
+  // FC1 dgrad: dX = dH13 W13
+  p.M = M;
+  p.A = T(MXF_T_DHQ_R); p.As = T(MXF_T_DHS_R); p.lda = 2 * F; p.ldas = 2 * F / 32;
+  p.B = T(MXF_T_W13Q_C); p.Bs = T(MXF_T_W13S_C); p.ldb = 2 * F; p.ldbs = 2 * F / 32;
+  p.b_es = D * 2 * F; p.bs_es = D * 2 * F / 32;
+  p.N = D; p.K = 2 * F;
+  p.C = dx; p.ldc = D;
+  MXF_HIP(mxf_launch_gemm_mgroup(0, p, st), "FC1 dgrad launch");
+  // FC1 wgrad: dW13[e] = dH13^T X over the expert's tokens, unpacked into dW1 / dW3
+  p.A = T(MXF_T_DHQ_C); p.As = T(MXF_T_DHS_C); p.lda = M; p.ldas = M / 32;
+  p.B = T(MXF_T_XQ_C); p.Bs = T(MXF_T_XS_C); p.ldb = M; p.ldbs = M / 32;
+  p.M = 2 * F; p.N = D; p.K = M;
+  p.C = dw1; p.C2 = dw3; p.ldc = D; p.c_es = F * D;
+  MXF_HIP(mxf_launch_gemm_kgroup(3, p, st), "FC1 wgrad launch");
+  return MXF_OK;
+}
+
+mxf_status mxf_read_status(const void* workspace, void* stream, int32_t* device_status) {
+  g_err.clear();
+  if (!workspace || !device_status) return fail(MXF_E_NULL, "workspace/device_status is NULL");
+  MXF_HIP(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
+  MXF_HIP(hipMemcpy(device_status, workspace, sizeof(int32_t), hipMemcpyDeviceToHost), "hipMemcpy");
+  return MXF_OK;
+}
+
+static mxf_status pack_common(const void* a, const void* b, const void* c, int32_t E, int32_t F, int32_t D) {
+  if (!a || !b || !c) return fail(MXF_E_NULL, "a weight pointer is NULL");
+  if (!aligned16(a) || !aligned16(b) || !aligned16(c)) return fail(MXF_E_ALIGN, "a weight pointer is not 16-byte aligned");
+  if (E < 0 || F < 0 || D < 0 || F % 32 || D % 8)
+    return fail(MXF_E_SHAPE, "E = %d, F = %d, D = %d: need F %% 32 == 0 and D %% 8 == 0", E, F, D);
+  return check_device();
+}
+
+mxf_status mxf_pack_w13(const void* w1, const void* w3, void* w13, int32_t E, int32_t F, int32_t D, void* stream) {
+  g_err.clear();
+  mxf_status s = pack_common(w1, w3, w13, E, F, D);
+  if (s != MXF_OK) return s;
+  MXF_HIP(mxf_launch_pack13(w1, w3, w13, E, F, D, true, (hipStream_t)stream), "pack launch");
+  return MXF_OK;
+}
+
+mxf_status mxf_unpack_w13(const void* w13, void* w1, void* w3, int32_t E, int32_t F, int32_t D, void* stream) {
+  g_err.clear();
+  mxf_status s = pack_common(w1, w3, w13, E, F, D);
+  if (s != MXF_OK) return s;
+  MXF_HIP(mxf_launch_pack13(w1, w3, const_cast<void*>(w13), E, F, D, false, (hipStream_t)stream), "unpack launch");
+  return MXF_OK;
+}
+
+}  // extern "C"

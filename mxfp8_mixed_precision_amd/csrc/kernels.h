@@ -1,0 +1,48 @@
+// Internal interface between the C ABI layer and the HIP kernels (not part of the public ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxf {
+
+struct GemmParams {
+  const uint8_t* A;   // codes, rows of K bytes with pitch lda
+  const uint8_t* As;  // scales, pitch ldas
+  const uint8_t* B;
+  const uint8_t* Bs;
+  int64_t lda, ldas, ldb, ldbs;
+  int64_t b_es, bs_es;  // M-grouped: bytes between experts in B / Bs
+  int64_t M, N, K;      // M-grouped: M = m_capacity. K-grouped: output [M, N] per expert
+  const int32_t* offs;
+  const int32_t* counts;
+  int E, pad;
+  int64_t mcap;
+  // epilogue
+  void* C;           // STORE: [M, N] (+ e * c_es for K-grouped); UNPACK13: dW1
+  void* C2;          // UNPACK13: dW3
+  int64_t ldc, c_es;
+  int out_f32;
+  uint16_t* h13;     // SWIGLU: written [mcap, 2F]; DSWIGLU: read [mcap, 2F]
+  uint8_t* q_r;      // SWIGLU: hq_r [mcap, F];  DSWIGLU: dhq_r [mcap, 2F]
+  uint8_t* s_r;
+  uint8_t* q_c;      // SWIGLU: hq_c [F, mcap];  DSWIGLU: dhq_c [2F, mcap]
+  uint8_t* s_c;
+  float* dbg;        // optional fp32 copy of the accumulator ([mcap, N])
+};
+
+}  // namespace mxf
+
+// quantize.hip
+hipError_t mxf_launch_quantize(const void* x, int64_t rows, int64_t cols, uint32_t mode, void* q_row,
+                               void* s_row, void* q_col, void* s_col, hipStream_t st);
+hipError_t mxf_launch_quant_tokens(const void* x, int64_t mcap, int64_t D, const int32_t* offs,
+                                   const int32_t* counts, int E, int pad, void* q_r, void* s_r,
+                                   void* q_c, void* s_c, int32_t* status, hipStream_t st);
+hipError_t mxf_launch_quant_weights(const void* w, const void* w3, bool pack13, int64_t E, int64_t rows,
+                                    int64_t cols, void* q_r, void* s_r, void* q_c, void* s_c,
+                                    hipStream_t st);
+hipError_t mxf_launch_pack13(const void* w1, const void* w3, void* w13, int64_t E, int64_t F,
+                             int64_t D, bool pack, hipStream_t st);
+// gemm.hip
+hipError_t mxf_launch_gemm_mgroup(int epi, const mxf::GemmParams& p, hipStream_t st);
+hipError_t mxf_launch_gemm_kgroup(int epi, const mxf::GemmParams& p, hipStream_t st);

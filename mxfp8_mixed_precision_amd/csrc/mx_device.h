@@ -1,0 +1,157 @@
+// Device-side MXFP8 helpers for gfx950 (shared by the quantizer and the GEMM epilogues).
+//
+// The rule (OCP MX v1.0 MXFP8, with the formats named in afd-plugin PR #475 "quantize the
+// A2E FFN transport to MXFP8", section "Purpose"): per 32-element group, scale byte
+// = clamp(floor(log2 amax) - 8, -127, 127) + 127 and codes = E4M3 RNE(v / 2^(byte-127))
+// saturated to +-448.
+//
+// Implementation on gfx950:
+//  * amax is taken on BF16 bit patterns: with the sign cleared, the ordering of finite
+//    BF16 magnitudes is the ordering of their 15-bit integers, so packed u16 max works.
+//  * For a finite nonzero amax with exponent field ef, floor(log2 amax) - 8 + 127 = ef - 8
+//    (ef >= 1); a subnormal or zero amax has ef = 0 and the clamp gives byte 0. So the
+//    byte is max(ef - 8, 0), or 0xFF when ef = 255 (Inf/NaN present).
+//  * Conversion uses v_cvt_scalef32_pk_fp8_bf16, which divides by the power-of-two scale
+//    and rounds to nearest even with exact subnormals, but does not saturate (magnitudes
+//    above 464 become NaN). Clamping |v| to 448 * 2^e first (exact in BF16: 1.75 *
+//    2^(e+8)) makes it equal to round-then-saturate. The clamp is a packed u16 min on
+//    the magnitude bits.
+//  * The scale operand is 2^e as an fp32: bits byte << 23, and for byte 0 the fp32
+//    subnormal 2^-127 (0x00400000) -- not the zero that byte << 23 would give.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxf {
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+
+// Per-group scale state derived from the group's amax magnitude bits.
+struct Scale {
+  uint32_t lim2;     // clamp limit (magnitude bits of 448 * 2^e) in both u16 halves
+  float xf;          // 2^e as fp32 (the cvt's scale operand)
+  uint32_t nanmask;  // 0x7F7F7F7F for a non-finite group (forces NaN codes), else 0
+  uint32_t byte;     // E8M0 byte
+};
+
+__device__ __forceinline__ Scale scale_from_amax(uint32_t amax_bits) {
+  const uint32_t ef = amax_bits >> 7;
+  Scale s;
+  if (ef >= 255u) {
+    s.byte = 255u;
+    s.lim2 = 0u;
+    s.xf = 1.0f;
+    s.nanmask = 0x7F7F7F7Fu;
+  } else {
+    const uint32_t byte = ef > 8u ? ef - 8u : 0u;
+    const uint32_t lim = ((byte + 8u) << 7) | 0x60u;
+    s.byte = byte;
+    s.lim2 = lim | (lim << 16);
+    s.xf = __uint_as_float(byte ? (byte << 23) : 0x00400000u);
+    s.nanmask = 0u;
+  }
+  return s;
+}
+
+// Magnitude bits of two packed BF16 values.
+__device__ __forceinline__ uint32_t mag2(uint32_t v) { return v & 0x7FFF7FFFu; }
+
+// Two packed BF16 (lo, hi) -> two E4M3 codes written into the low (hi=false) or high
+// (hi=true) 16 bits of `old`.
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt2(uint32_t old, uint32_t v, const Scale& s) {
+  const uint32_t c = (v & 0x80008000u) | pk_min_u16(v & 0x7FFF7FFFu, s.lim2);
+  s16x2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(__builtin_bit_cast(s16x2, old),
+                                                       __builtin_bit_cast(bf16x2, c), s.xf, HI);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Four BF16 (two packed words) -> four E4M3 codes in one word (byte i = element i).
+__device__ __forceinline__ uint32_t cvt4(uint32_t v01, uint32_t v23, const Scale& s) {
+  uint32_t r = cvt2<false>(0u, v01, s);
+  r = cvt2<true>(r, v23, s);
+  return r | s.nanmask;
+}
+
+// Amax magnitude bits of 32 BF16 values held in 16 packed words.
+__device__ __forceinline__ uint32_t amax32(const uint32_t* v) {
+  uint32_t m = mag2(v[0]);
+#pragma unroll
+  for (int i = 1; i < 16; ++i) m = pk_max_u16(m, mag2(v[i]));
+  return max(m & 0xFFFFu, m >> 16);
+}
+
+// Quantize 32 BF16 values (16 packed words, element order) into 32 codes (8 words) and
+// return the scale byte.
+__device__ __forceinline__ uint32_t quant32(const uint32_t* v, uint32_t* codes) {
+  const Scale s = scale_from_amax(amax32(v));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) codes[i] = cvt4(v[2 * i], v[2 * i + 1], s);
+  return s.byte;
+}
+
+// Pack the low (or high) BF16 halves of two words: (a.lo, b.lo) or (a.hi, b.hi).
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// fp32 -> BF16 bits, round to nearest even (gfx950 hardware conversion).
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)f);
+}
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// sigmoid(g) without overflow for either sign.
+__device__ __forceinline__ float sigmoid_f(float g) {
+  const float e = expf(-fabsf(g));
+  const float r = 1.0f / (1.0f + e);
+  return g >= 0.0f ? r : e * r;
+}
+
+// Device-side check of the token-offset contract, done by one whole wavefront; every lane
+// returns the same answer. offs [E+1], counts [E] or null.
+__device__ __forceinline__ bool offsets_valid(const int32_t* offs, const int32_t* counts, int E,
+                                              int pad, int64_t mcap) {
+  const int lane = threadIdx.x & 63;
+  bool bad = false;
+  for (int i = lane; i <= E; i += 64) {
+    const int32_t o = offs[i];
+    if (o % pad != 0 || o < 0 || (int64_t)o > mcap) bad = true;
+    if (i == 0 && o != 0) bad = true;
+    if (i > 0) {
+      const int32_t p = offs[i - 1];
+      if (o < p) bad = true;
+      if (counts) {
+        const int32_t c = counts[i - 1];
+        if (c < 0 || c > o - p) bad = true;
+      }
+    }
+  }
+  return !__any(bad);
+}
+
+// Expert that owns row m (offs[e] <= m < offs[e+1]); requires m < offs[E].
+__device__ __forceinline__ int expert_of_row(const int32_t* offs, int E, int64_t m) {
+  int lo = 0, hi = E;  // invariant: offs[lo] <= m < offs[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)offs[mid] <= m) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+}  // namespace mxf

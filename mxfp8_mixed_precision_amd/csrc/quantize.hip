@@ -1,0 +1,269 @@
+// MXFP8 dual (row-wise + column-wise) quantization kernels for gfx950.
+//
+// Dual quantization is torchtitan PR #12 "Wire the fully-fused grouped-GEMM MXFP8 plan behind
+// fusion_plan", section "What it adds": each operand is quantized in 32-element groups along
+// the axis its GEMM contracts over, so one BF16 matrix yields row-wise codes [R, C] (+ scales
+// [R, C/32]) and column-wise codes stored transposed [C, R] (+ scales [C, R/32]).
+//
+// Work decomposition (HBM-bound: 2 bytes in, ~2.06 bytes out per element for dual):
+//   * block = 4 wavefronts = 128 rows x 128 columns; each wavefront owns 32 rows x 128 cols,
+//     so every column-wise 32-group lies inside one wavefront and no LDS or block barrier is
+//     needed;
+//   * lane l: row octet s = l / 16 (rows 8s .. 8s+7 of the wavefront), column octet
+//     c = l % 16 (cols 8c .. 8c+7). Each lane loads 8 rows x 16 bytes: a wavefront load
+//     instruction covers 4 rows x 256 contiguous bytes;
+//   * a row-wise group (32 cols) is 4 adjacent lanes: amax by two DPP quad swaps; the lane
+//     writes its 8 codes (8 bytes; 16 lanes write one full 128-byte line per row);
+//   * a column-wise group (32 rows) is the 4 lanes l, l^16, l^32, l^48: amax by two
+//     cross-lane swaps; each lane writes 8 contiguous codes per column (the 4 lanes, and
+//     the 4 wavefronts of the block, complete 128 contiguous bytes of every column).
+#include "kernels.h"
+#include "mx_device.h"
+
+namespace mxf {
+
+enum QuantKind { QK_PLAIN = 0, QK_MASKED = 1, QK_PACK13 = 2 };
+
+struct QuantParams {
+  const uint16_t* src;   // BF16 bits; QK_PACK13: w1 [E, F, D]
+  const uint16_t* src2;  // QK_PACK13: w3 [E, F, D]
+  int64_t rows, cols;    // logical matrix per batch entry (QK_PACK13: rows = 2F, cols = D)
+  int64_t src_bs;        // elements between batch entries of src / src2
+  uint8_t* q_r;
+  uint8_t* s_r;
+  uint8_t* q_c;
+  uint8_t* s_c;
+  int64_t qr_bs, sr_bs, qc_bs, sc_bs;  // bytes between batch entries of each output
+  int64_t ldc;                          // row pitch (bytes) of q_c; multiple of 32
+  const int32_t* offs;                  // QK_MASKED: token offsets [E+1]
+  const int32_t* counts;                // QK_MASKED: real rows per expert [E] or null
+  int E, pad;
+  int32_t* status;                      // QK_MASKED: device status word (block 0 writes it)
+};
+
+__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+}
+
+template <int KIND, bool ROW, bool COL>
+__global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int s = lane >> 4;
+  const int c = lane & 15;
+  const int64_t e = blockIdx.z;
+  const int64_t col = (int64_t)blockIdx.y * 128 + c * 8;
+  const int64_t rw0 = (int64_t)blockIdx.x * 128 + w * 32;  // first row of this wavefront
+  const int64_t r0 = rw0 + 8 * s;                           // first row of this lane
+
+  int64_t valid_end = p.rows;  // rows at or past this read as zero
+  const uint16_t* src = p.src + e * p.src_bs;
+  int64_t src_row0 = rw0;      // source row of the wavefront's first row
+  if (KIND == QK_MASKED) {
+    const bool ok = offsets_valid(p.offs, p.counts, p.E, p.pad, p.rows);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *p.status = ok ? 0 : 1;
+    if (!ok) return;
+    const int64_t mend = p.offs[p.E];
+    if (rw0 >= mend) return;  // tail rows: never read or written
+    const int ex = expert_of_row(p.offs, p.E, rw0);
+    valid_end = p.offs[ex] + (p.counts ? p.counts[ex] : p.offs[ex + 1] - p.offs[ex]);
+  } else if (KIND == QK_PACK13) {
+    // packed row n of [2F, D]: groups of 32 rows alternate between w1 and w3
+    const int64_t grp = rw0 >> 5;
+    src = ((grp & 1) ? p.src2 : p.src) + e * p.src_bs;
+    src_row0 = (grp >> 1) * 32;
+  }
+  if (rw0 >= p.rows) return;
+  const bool colok = col < p.cols;
+
+  uint32_t x[8][4];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t r = r0 + j;
+    if (colok && r < valid_end) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src + (src_row0 + 8 * s + j) * p.cols + col);
+      x[j][0] = v.x; x[j][1] = v.y; x[j][2] = v.z; x[j][3] = v.w;
+    } else {
+      x[j][0] = x[j][1] = x[j][2] = x[j][3] = 0u;
+    }
+  }
+
+  if (ROW) {
+    uint8_t* q_r = p.q_r + e * p.qr_bs;
+    uint8_t* s_r = p.s_r + e * p.sr_bs;
+    const int64_t ng = p.cols >> 5;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t m = pk_max_u16(pk_max_u16(mag2(x[j][0]), mag2(x[j][1])),
+                              pk_max_u16(mag2(x[j][2]), mag2(x[j][3])));
+      m = max(m & 0xFFFFu, m >> 16);
+      m = max(m, dpp_xor1(m));
+      m = max(m, dpp_xor2(m));
+      const Scale sc = scale_from_amax(m);
+      const uint32_t lo = cvt4(x[j][0], x[j][1], sc);
+      const uint32_t hi = cvt4(x[j][2], x[j][3], sc);
+      const int64_t r = r0 + j;
+      if (colok && r < p.rows) {
+        *reinterpret_cast<uint2*>(q_r + r * p.cols + col) = make_uint2(lo, hi);
+        if ((c & 3) == 0) s_r[r * ng + (col >> 5)] = (uint8_t)sc.byte;
+      }
+    }
+  }
+
+  if (COL) {
+    uint8_t* q_c = p.q_c + e * p.qc_bs;
+    uint8_t* s_c = p.s_c + e * p.sc_bs;
+    const int64_t ldsc = p.ldc >> 5;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t m = mag2(x[0][k]);
+#pragma unroll
+      for (int j = 1; j < 8; ++j) m = pk_max_u16(m, mag2(x[j][k]));
+      m = pk_max_u16(m, (uint32_t)__shfl_xor((int)m, 16));
+      m = pk_max_u16(m, (uint32_t)__shfl_xor((int)m, 32));
+      const Scale slo = scale_from_amax(m & 0xFFFFu);
+      const Scale shi = scale_from_amax(m >> 16);
+      const uint32_t a0 = cvt4(pack_lo(x[0][k], x[1][k]), pack_lo(x[2][k], x[3][k]), slo);
+      const uint32_t a1 = cvt4(pack_lo(x[4][k], x[5][k]), pack_lo(x[6][k], x[7][k]), slo);
+      const uint32_t b0 = cvt4(pack_hi(x[0][k], x[1][k]), pack_hi(x[2][k], x[3][k]), shi);
+      const uint32_t b1 = cvt4(pack_hi(x[4][k], x[5][k]), pack_hi(x[6][k], x[7][k]), shi);
+      if (colok) {
+        const int64_t c0 = col + 2 * k;
+        *reinterpret_cast<uint2*>(q_c + c0 * p.ldc + r0) = make_uint2(a0, a1);
+        *reinterpret_cast<uint2*>(q_c + (c0 + 1) * p.ldc + r0) = make_uint2(b0, b1);
+        if (s == 0) {
+          s_c[c0 * ldsc + (rw0 >> 5)] = (uint8_t)slo.byte;
+          s_c[(c0 + 1) * ldsc + (rw0 >> 5)] = (uint8_t)shi.byte;
+        }
+      }
+    }
+  }
+}
+
+// 32-row-block interleave of w1/w3 into [E, 2F, D] and back (BF16, 16-byte copies).
+template <bool PACK>
+__global__ __launch_bounds__(256) void pack13_kernel(const uint16_t* a, const uint16_t* b,
+                                                     uint16_t* w13, uint16_t* w1, uint16_t* w3,
+                                                     int64_t E, int64_t F, int64_t D) {
+  const int64_t chunks_per_row = D / 8;
+  const int64_t total = E * 2 * F * chunks_per_row;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t ch = i % chunks_per_row;
+    const int64_t n = (i / chunks_per_row) % (2 * F);
+    const int64_t e = i / (chunks_per_row * 2 * F);
+    const int64_t f = (n >> 6) * 32 + (n & 31);
+    const bool up = (n & 32) != 0;
+    const int64_t src_off = (e * F + f) * D + ch * 8;
+    const int64_t dst_off = (e * 2 * F + n) * D + ch * 8;
+    if (PACK) {
+      const uint16_t* s = up ? b : a;
+      *reinterpret_cast<uint4*>(w13 + dst_off) = *reinterpret_cast<const uint4*>(s + src_off);
+    } else {
+      uint16_t* d = up ? w3 : w1;
+      *reinterpret_cast<uint4*>(d + src_off) = *reinterpret_cast<const uint4*>(a + dst_off);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ host launchers
+
+static hipError_t launch_quant(int kind, uint32_t mode, const QuantParams& p, int64_t batch,
+                               hipStream_t st) {
+  // the token-layout kind always runs (its first block writes the status word)
+  if ((p.rows == 0 || p.cols == 0 || batch == 0) && kind != QK_MASKED) return hipSuccess;
+  const int64_t rt = (p.rows + 127) / 128, ct = (p.cols + 127) / 128;
+  const dim3 grid((unsigned)(rt > 0 ? rt : 1), (unsigned)(ct > 0 ? ct : 1), (unsigned)(batch > 0 ? batch : 1));
+  const dim3 block(256);
+#define MXF_QLAUNCH(K, R, C) hipLaunchKernelGGL((quant_dual_kernel<K, R, C>), grid, block, 0, st, p)
+  if (kind == QK_PLAIN) {
+    if (mode == 3) MXF_QLAUNCH(QK_PLAIN, true, true);
+    else if (mode == 1) MXF_QLAUNCH(QK_PLAIN, true, false);
+    else MXF_QLAUNCH(QK_PLAIN, false, true);
+  } else if (kind == QK_MASKED) {
+    MXF_QLAUNCH(QK_MASKED, true, true);
+  } else {
+    MXF_QLAUNCH(QK_PACK13, true, true);
+  }
+#undef MXF_QLAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace mxf
+
+// Internal entry points used by the C ABI layer (abi.hip).
+hipError_t mxf_launch_quantize(const void* x, int64_t rows, int64_t cols, uint32_t mode, void* q_row,
+                               void* s_row, void* q_col, void* s_col, hipStream_t st) {
+  mxf::QuantParams p = {};
+  p.src = (const uint16_t*)x;
+  p.rows = rows;
+  p.cols = cols;
+  p.q_r = (uint8_t*)q_row;
+  p.s_r = (uint8_t*)s_row;
+  p.q_c = (uint8_t*)q_col;
+  p.s_c = (uint8_t*)s_col;
+  p.ldc = rows;
+  return mxf::launch_quant(mxf::QK_PLAIN, mode, p, 1, st);
+}
+
+// Dual quantization of the activation-like operand x [mcap, D] under the token layout
+// (pad rows read as zero, rows >= offs[E] skipped); writes the status word.
+hipError_t mxf_launch_quant_tokens(const void* x, int64_t mcap, int64_t D, const int32_t* offs,
+                                   const int32_t* counts, int E, int pad, void* q_r, void* s_r,
+                                   void* q_c, void* s_c, int32_t* status, hipStream_t st) {
+  mxf::QuantParams p = {};
+  p.src = (const uint16_t*)x;
+  p.rows = mcap;
+  p.cols = D;
+  p.q_r = (uint8_t*)q_r;
+  p.s_r = (uint8_t*)s_r;
+  p.q_c = (uint8_t*)q_c;
+  p.s_c = (uint8_t*)s_c;
+  p.ldc = mcap;
+  p.offs = offs;
+  p.counts = counts;
+  p.E = E;
+  p.pad = pad;
+  p.status = status;
+  return mxf::launch_quant(mxf::QK_MASKED, 3, p, 1, st);
+}
+
+// Dual quantization of a batch of E weight matrices [rows, cols]. pack13 = true reads w1/w3
+// [E, rows/2, cols] and quantizes their [E, rows, cols] 32-block interleave.
+hipError_t mxf_launch_quant_weights(const void* w, const void* w3, bool pack13, int64_t E, int64_t rows,
+                                    int64_t cols, void* q_r, void* s_r, void* q_c, void* s_c,
+                                    hipStream_t st) {
+  mxf::QuantParams p = {};
+  p.src = (const uint16_t*)w;
+  p.src2 = (const uint16_t*)w3;
+  p.rows = rows;
+  p.cols = cols;
+  p.src_bs = pack13 ? (rows / 2) * cols : rows * cols;
+  p.q_r = (uint8_t*)q_r;
+  p.s_r = (uint8_t*)s_r;
+  p.q_c = (uint8_t*)q_c;
+  p.s_c = (uint8_t*)s_c;
+  p.qr_bs = rows * cols;
+  p.sr_bs = rows * (cols / 32);
+  p.qc_bs = rows * cols;
+  p.sc_bs = cols * (rows / 32);
+  p.ldc = rows;
+  return mxf::launch_quant(pack13 ? mxf::QK_PACK13 : mxf::QK_PLAIN, 3, p, E, st);
+}
+
+hipError_t mxf_launch_pack13(const void* w1, const void* w3, void* w13, int64_t E, int64_t F,
+                             int64_t D, bool pack, hipStream_t st) {
+  const int64_t total = E * 2 * F * (D / 8);
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 65536);
+  if (pack)
+    hipLaunchKernelGGL(mxf::pack13_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       (const uint16_t*)w1, (const uint16_t*)w3, (uint16_t*)w13, nullptr, nullptr, E, F, D);
+  else
+    hipLaunchKernelGGL(mxf::pack13_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       (const uint16_t*)w13, nullptr, nullptr, (uint16_t*)w1, (uint16_t*)w3, E, F, D);
+  return hipGetLastError();
+}

@@ -1,0 +1,139 @@
+"""The C-ABI library loads, exports what include/mxfp8.h declares, and rejects bad
+arguments on the host before touching a GPU (CPU only: no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp8_mixed_precision_amd as mx
+from mxfp8_mixed_precision_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp8.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = mx.lib()
+    decl = declared_functions()
+    assert "mxfp8_quantize" in decl and "grouped_mlp_fwd" in decl and "grouped_mlp_bwd" in decl
+    assert sorted(decl) == sorted(_abi.EXPORTS)
+    for name in decl:
+        assert hasattr(L, name), name
+    assert mx.abi_version() == 1
+
+
+def test_header_enums_match_binding():
+    text = open(HEADER).read()
+    body = text[text.index("typedef enum {\n  MXF_T_STATUS"):]
+    body = body[:body.index("} mxf_tensor;")]
+    names = re.findall(r"MXF_T_([A-Z0-9_]+)", body)
+    names = [n for n in names if n != "COUNT"]
+    assert names == _abi.TENSORS
+    for code, name in _abi.STATUS_NAMES.items():
+        assert re.search(rf"{name} = {code}\b", text), name
+
+
+def _desc(E=4, D=256, F=256, pad=128, m=1280, flags=0):
+    return mx.make_desc(E, D, F, pad, m, flags)
+
+
+def test_layout_is_consistent():
+    d = _desc()
+    saved, ws = mx.mlp_saved_bytes(d), mx.mlp_workspace_bytes(d)
+    assert saved > 0 and ws > 0
+    E, D, F, M = 4, 256, 256, 1280
+    expect = {"XQ_C": D * M, "W13Q_C": E * D * 2 * F, "H13": M * 2 * F * 2, "HQ_C": F * M,
+              "XQ_R": M * D, "DHQ_R": M * 2 * F, "STATUS": 4, "H13_F32": 0}
+    spans = {0: [], 1: []}
+    for name in _abi.TENSORS:
+        region, off, nb = mx.mlp_tensor(d, name)
+        if name in expect:
+            assert nb == expect[name], name
+        assert off % 256 == 0
+        assert off + nb <= (saved if region == 1 else ws)
+        spans[region].append((off, off + nb, name))
+    # saved tensors never overlap each other
+    s = sorted(spans[1])
+    assert all(a[1] <= b[0] for a, b in zip(s, s[1:]))
+    # forward-only and backward-only workspace tensors may share space, but each group is disjoint
+    fwd = {"STATUS", "XQ_R", "XS_R", "W13Q_R", "W13S_R", "W2Q_R", "W2S_R", "HQ_R", "HS_R", "H13_F32"}
+    for group in (fwd, set(_abi.TENSORS) - fwd - {n for _, _, n in spans[1]}):
+        g = sorted(x for x in spans[0] if x[2] in group and x[1] > x[0])
+        assert all(a[1] <= b[0] for a, b in zip(g, g[1:])), g
+    # the debug flag adds the fp32 tensors
+    d2 = _desc(flags=mx.DEBUG_F32)
+    assert mx.mlp_tensor(d2, "H13_F32")[2] == M * 2 * F * 4
+    assert mx.mlp_workspace_bytes(d2) > ws
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(E=0), _abi.E_SHAPE), (dict(E=2000), _abi.E_SHAPE), (dict(D=200), _abi.E_SHAPE),
+    (dict(F=96), _abi.E_SHAPE), (dict(pad=64), _abi.E_SHAPE), (dict(m=1000), _abi.E_SHAPE),
+    (dict(m=-128), _abi.E_SHAPE), (dict(flags=8), _abi.E_ARG),
+])
+def test_descriptor_rejections(kw, code):
+    d = _desc(**kw)
+    assert mx.mlp_saved_bytes(d) == 0 and mx.mlp_workspace_bytes(d) == 0
+    with pytest.raises(mx.MxfError) as ei:
+        mx.mlp_tensor(d, "H13")
+    assert ei.value.status == code
+    with pytest.raises(mx.MxfError) as ei:
+        mx.grouped_mlp_fwd(d, 16, 16, 16, 16, 16, 16, 16, 16, 16, stream=0)
+    assert ei.value.status == code
+    assert mx.last_error()
+
+
+def test_mlp_pointer_rejections():
+    d = _desc()
+    good = 1 << 20
+    with pytest.raises(mx.MxfError) as ei:
+        mx.grouped_mlp_fwd(d, good, None, None, good, good, good, good, good, good, stream=0)
+    assert ei.value.status == _abi.E_NULL and "x" in str(ei.value)
+    with pytest.raises(mx.MxfError) as ei:
+        mx.grouped_mlp_fwd(d, good, None, good + 8, good, good, good, good, good, good, stream=0)
+    assert ei.value.status == _abi.E_ALIGN and "x" in str(ei.value)
+    with pytest.raises(mx.MxfError) as ei:
+        mx.grouped_mlp_fwd(d, None, None, good, good, good, good, good, good, good, stream=0)
+    assert ei.value.status == _abi.E_NULL and "offs" in str(ei.value)
+    with pytest.raises(mx.MxfError) as ei:
+        mx.grouped_mlp_bwd(d, good, None, good, good, good, None, good, good, good, stream=0)
+    assert ei.value.status == _abi.E_NULL and "dw1" in str(ei.value)
+
+
+@pytest.mark.parametrize("rows,cols,mode,code", [
+    (64, 48, mx.ROW, _abi.E_SHAPE), (48, 64, mx.COL, _abi.E_SHAPE), (-1, 64, mx.ROW, _abi.E_SHAPE),
+    (64, 64, 0, _abi.E_ARG), (64, 64, 4, _abi.E_ARG),
+])
+def test_quantize_rejections(rows, cols, mode, code):
+    good = 1 << 20
+    with pytest.raises(mx.MxfError) as ei:
+        mx.mxfp8_quantize(good, rows, cols, mode, good, good, good, good, stream=0)
+    assert ei.value.status == code
+
+
+def test_quantize_null_and_alignment():
+    good = 1 << 20
+    with pytest.raises(mx.MxfError) as ei:
+        mx.mxfp8_quantize(good, 64, 64, mx.ROW | mx.COL, good, good, None, good, stream=0)
+    assert ei.value.status == _abi.E_NULL
+    with pytest.raises(mx.MxfError) as ei:
+        mx.mxfp8_quantize(good + 4, 64, 64, mx.ROW, good, good, None, None, stream=0)
+    assert ei.value.status == _abi.E_ALIGN
+
+
+def test_valid_call_without_gpu_fails_cleanly():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    good = 1 << 20
+    with pytest.raises(mx.MxfError) as ei:
+        mx.mxfp8_quantize(good, 64, 64, mx.ROW, good, good, None, None, stream=0)
+    assert ei.value.status in (_abi.E_HIP, _abi.E_DEVICE)
