@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark of the MXFP8 routed-experts SwiGLU MLP on one MI355X.
+
+One step = grouped_mlp_fwd + grouped_mlp_bwd (every kernel of the path: weight dual
+quantization and packing, token dual quantization, FC1 + SwiGLU + dual quantization, FC2,
+dY quantization, FC2 dgrad + dSwiGLU + dual quantization, both wgrads, FC1 dgrad) on the
+DeepSeek-V3-16B-like expert-parallel rank: 16 local experts, D=2048, F=1408, 24576 routed
+rows (Zipf(1.1) counts with 2 zero-token experts) padded to 256 per expert. Inputs are
+synthetic (seeded), resident in HBM before timing; three input sets rotate so that the
+256 MB last-level cache cannot hold a step's operands.
+
+value = useful TFLOP/s = 18 * M_real * D * F / step time (pad rows are not counted).
+The line also reports, for the dominant kernel, its roofline fraction (per-kernel HIP
+event timing inside the library, on the launch stream), the standalone quantizer's GB/s
+on BF16 [16384, 7168] dual quantization, and the CPU oracle timed on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "grouped-MLP fwd+bwd MXFP8 TFLOP/s & quantize GB/s, % of MI355X roofline"
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense MXFP8 / FP8 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def gemm_flops(name, m_real, D, F):
+    """Useful FLOPs of one launch of each GEMM kernel (2 per multiply-add, real rows only)."""
+    per = {"fc1_swiglu": 2 * 2 * F * D, "fc2": 2 * D * F, "fc2_dgrad_dswiglu": 2 * F * D,
+           "fc2_wgrad": 2 * D * F, "fc1_dgrad": 2 * D * 2 * F, "fc1_wgrad": 2 * 2 * F * D}
+    return per[name] * m_real if name in per else None
+
+
+def quant_bytes(name, m_pad, m_real, E, D, F):
+    """Algorithmic HBM bytes of one launch of each quantization kernel: BF16 read of the real
+    rows, codes in both directions (2 B/element) and scales (2/32 B/element) written."""
+    out = 2 + 2.0 / 32
+    if name in ("quant_x", "quant_dy"):
+        return m_real * D * 2 + m_pad * D * out
+    if name == "quant_w13":
+        return E * 2 * F * D * (2 + out)
+    if name == "quant_w2":
+        return E * D * F * (2 + out)
+    return None
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match the sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        import hashlib
+        with open(path) as f:
+            t = json.load(f)
+        h = hashlib.sha256()
+        csrc = os.path.join(ROOT, "mxfp8_mixed_precision_amd", "csrc")
+        for n in sorted(os.listdir(csrc)):
+            with open(os.path.join(csrc, n), "rb") as f:
+                h.update(f.read())
+        if t.get("source_sha256") != h.hexdigest():
+            return None
+        return t.get("kernels", {}).get(workload, {}).get(kernel)
+    except Exception:
+        return None
+
+
+def cpu_baseline(prob):
+    """The oracle (as it stands) on a bounded sample of the same workload: the full fwd+bwd of
+    the three smallest non-empty experts, timed on the host cores."""
+    import numpy as np
+    import workloads
+    from oracle import mlp as om
+    from oracle.formats import bf16_bits_to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count()
+    counts = prob["counts"]
+    order = sorted([e for e in range(len(counts)) if counts[e] > 0], key=lambda e: counts[e])[:3]
+    D, F, pad = prob["D"], prob["F"], prob["pad"]
+    sub_counts = [counts[e] for e in order]
+    sub_offs = workloads.padded_offsets(sub_counts, pad)
+    offs = prob["offs"]
+    x = np.concatenate([bf16_bits_to_f64(workloads.bf16_bits(prob["x_cpu"][offs[e]:offs[e + 1]])) for e in order])
+    dy = np.concatenate([bf16_bits_to_f64(workloads.bf16_bits(prob["dy_cpu"][offs[e]:offs[e + 1]])) for e in order])
+    w1 = bf16_bits_to_f64(workloads.bf16_bits(prob["w1_cpu"][order]))
+    w3 = bf16_bits_to_f64(workloads.bf16_bits(prob["w3_cpu"][order]))
+    w2 = bf16_bits_to_f64(workloads.bf16_bits(prob["w2_cpu"][order]))
+    t0 = time.perf_counter()
+    fwd = om.mlp_forward(x, w1, w3, w2, sub_offs, sub_counts)
+    om.mlp_backward(fwd, dy)
+    dt = time.perf_counter() - t0
+    flops = 18.0 * sum(sub_counts) * D * F
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"full fwd+bwd of experts {order} ({sum(sub_counts)} routed rows, "
+                      f"{flops / 1e9:.1f} useful GFLOP) in {dt:.1f} s; numpy fp64, BLAS threads {threads}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3_rank", choices=["dsv3_rank", "dense", "large_expert", "tiny"])
+    ap.add_argument("--sets", type=int, default=3, help="rotating input sets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-quant", action="store_true", help="skip the standalone quantizer measurement")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE {world}) is not supported: "
+              "this build has no multi-GPU path (expert-parallel sharding is described in DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mxfp8_mixed_precision_amd as mx
+    import workloads
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    mx.lib()
+    cfg = workloads.MLP_CONFIGS[args.workload]
+    E, D, F, pad = cfg["E"], cfg["D"], cfg["F"], cfg["pad"]
+    counts = workloads.expert_counts(args.workload)
+    offs = workloads.padded_offsets(counts, pad)
+    m_pad, m_real = offs[-1], sum(counts)
+    mcap = m_pad
+
+    # input sets generated on the GPU (same recipe, GPU generator) and kept resident
+    sets = []
+    for s in range(args.sets):
+        p = workloads.mlp_problem(args.workload, seed=42 + s, device=dev)
+        sets.append({k: p[k] for k in ("x", "w1", "w3", "w2", "dy")})
+    offs_t = torch.tensor(offs, dtype=torch.int32, device=dev)
+    counts_t = torch.tensor(counts, dtype=torch.int32, device=dev)
+    ctx = mx.MlpContext(E, D, F, pad, mcap, flags=0, device=dev)
+    y = torch.empty((mcap, D), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty((mcap, D), dtype=torch.bfloat16, device=dev)
+    dw1 = torch.empty((E, F, D), dtype=torch.bfloat16, device=dev)
+    dw3 = torch.empty((E, F, D), dtype=torch.bfloat16, device=dev)
+    dw2 = torch.empty((E, D, F), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        s = sets[i % len(sets)]
+        ctx.fwd(offs_t, counts_t, s["x"], s["w1"], s["w3"], s["w2"], y)
+        ctx.bwd(offs_t, counts_t, s["dy"], dx, dw1, dw3, dw2)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    assert ctx.status() == mx.DEV_OK
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    gpu_ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    useful = 18.0 * m_real * D * F
+    executed = 18.0 * m_pad * D * F
+    value = useful / (ms_per_step / 1e3) / 1e12
+
+    # per-kernel timing (library-internal HIP events on the launch stream), same steps again
+    mx.profile_begin(12 * args.steps + 16)
+    t2 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    prof = mx.profile_end()
+    kernels = {}
+    for name, (n, tot) in prof.items():
+        avg = tot / n
+        k = {"launches": n, "avg_us": round(avg * 1e3, 2)}
+        fl = gemm_flops(name, m_real, D, F)
+        if fl is not None:
+            k["tflops"] = round(fl / (avg / 1e3) / 1e12, 1)
+        by = quant_bytes(name, m_pad, m_real, E, D, F)
+        if by is not None:
+            k["gbs"] = round(by / (avg / 1e3) / 1e9, 1)
+        kernels[name] = k
+    dom = max(prof.items(), key=lambda kv: kv[1][1])[0]
+    dn, dtot = prof[dom]
+    davg_s = dtot / dn / 1e3
+    fl = gemm_flops(dom, m_real, D, F)
+    if fl is not None:
+        ach = fl / davg_s / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_FP8_TFLOPS, 4),
+                "traffic": traffic_for(dom, args.workload)}
+    else:
+        by = quant_bytes(dom, m_pad, m_real, E, D, F)
+        ach = by / davg_s / 1e9
+        roof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic_for(dom, args.workload)}
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "mxfp8-e4m3/fp32-acc",
+        "data": "synthetic (seeded N(0,1) activations and gradients, N(0,0.02) weights, BF16)",
+        "config": {"workload": f"{args.workload}: one expert-parallel rank, E={E} D={D} F={F}, "
+                               f"{m_real} routed rows padded to {m_pad} (pad {pad}), fwd+bwd",
+                   "E": E, "D": D, "F": F, "m_real": m_real, "m_padded": m_pad, "pad_multiple": pad,
+                   "parallelism": "single GPU (one EP rank's share)"},
+        "gpu_ms_per_step": round(gpu_ms_per_step, 4),
+        "executed_tflops": round(executed / (ms_per_step / 1e3) / 1e12, 2),
+        "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 4),
+        "roofline": roof,
+        "kernels": kernels,
+        "profiled_ms_per_step": round((t3 - t2) * 1e3 / args.steps, 4),
+    }
+
+    if not args.no_quant:
+        out["quantize"] = bench_quantize(mx, torch, dev, args)
+
+    if not args.no_cpu_baseline:
+        cpu_prob = workloads.mlp_problem(args.workload, seed=42)
+        prob = {"x_cpu": cpu_prob["x"], "dy_cpu": cpu_prob["dy"], "w1_cpu": cpu_prob["w1"],
+                "w3_cpu": cpu_prob["w3"], "w2_cpu": cpu_prob["w2"], "counts": counts, "offs": offs,
+                "D": D, "F": F, "pad": pad}
+        out["cpu_baseline"] = cpu_baseline(prob)
+    print(json.dumps(out), flush=True)
+
+
+def bench_quantize(mx, torch, dev, args):
+    """Standalone dual quantization of BF16 [16384, 7168] (3 rotating inputs)."""
+    import workloads
+    rows, cols = workloads.QUANT_CONFIG["rows"], workloads.QUANT_CONFIG["cols"]
+    xs = [workloads.quant_matrix(rows, cols, seed=42 + s, device=dev) for s in range(3)]
+    q_r = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    s_r = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+    q_c = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
+    s_c = torch.empty((cols, rows // 32), dtype=torch.uint8, device=dev)
+    n = max(args.steps, 10)
+    for i in range(3):
+        mx.mxfp8_quantize(xs[i % 3], rows, cols, 3, q_r, s_r, q_c, s_c)
+    torch.cuda.synchronize()
+    mx.profile_begin(n)
+    for i in range(n):
+        mx.mxfp8_quantize(xs[i % 3], rows, cols, 3, q_r, s_r, q_c, s_c)
+    torch.cuda.synchronize()
+    prof = mx.profile_end()
+    cnt, tot = prof["quantize"]
+    avg_s = tot / cnt / 1e3
+    nbytes = rows * cols * (2 + 2 + 2.0 / 32)
+    gbs = nbytes / avg_s / 1e9
+    return {"workload": f"quant: BF16 [{rows}, {cols}] dual (row-wise + column-wise) MXFP8", "value": round(gbs, 1),
+            "unit": "GB/s", "avg_us": round(avg_s * 1e6, 2),
+            "roofline": {"bound": "hbm", "kernel": "quantize", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": traffic_for("quantize", "quant")}}
+
+
+if __name__ == "__main__":
+    main()

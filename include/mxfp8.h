@@ -167,6 +167,25 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc /* host */, const int32_t* o
  * used `workspace` into *device_status (MXF_DEV_OK or MXF_DEV_BAD_OFFSETS). */
 mxf_status mxf_read_status(const void* workspace, void* stream, int32_t* device_status /* host */);
 
+/* ------------------------------------------------------------------ kernel timing */
+
+/* Per-kernel timing for benchmarks. mxf_profile_begin(capacity) starts recording on the
+ * calling thread: each kernel that this thread's later library calls launch is bracketed by
+ * two HIP events recorded on the same stream (at most `capacity` launches; the events are
+ * created here, not in the timed calls). mxf_profile_end waits for the recorded events and
+ * returns, per kernel name, the number of launches and their summed duration in ms; it
+ * fills at most max_out entries and sets *n_out to the number filled, then stops recording.
+ * Kernel names: quant_w13, quant_w2, quant_x, fc1_swiglu, fc2, quant_dy, fc2_dgrad_dswiglu,
+ * fc2_wgrad, fc1_dgrad, fc1_wgrad, quantize.
+ * Errors: MXF_E_ARG (capacity < 1 or > 1<<20, or end without begin), MXF_E_NULL, MXF_E_HIP. */
+typedef struct {
+  char name[32];
+  int32_t launches;
+  double total_ms;
+} mxf_kernel_time;
+mxf_status mxf_profile_begin(int32_t capacity);
+mxf_status mxf_profile_end(mxf_kernel_time* out /* host */, int32_t max_out, int32_t* n_out /* host */);
+
 /* Test helpers for the [E, 2F, D] 32-block packing: w13[e, 64j+i] = w1[e, 32j+i] and
  * w13[e, 64j+32+i] = w3[e, 32j+i] (i < 32), BF16, and its inverse. F % 32 == 0. */
 mxf_status mxf_pack_w13(const void* w1, const void* w3, void* w13, int32_t E, int32_t F,

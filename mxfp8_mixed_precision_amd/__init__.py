@@ -8,7 +8,8 @@ documented intermediate tensors as views, for tests and inspection.
 from ._abi import (CAP_GFX950, COL, DEBUG_F32, DEV_BAD_OFFSETS, DEV_OK, EXPORTS, LIB_PATH, OUT_F32,
                    ROW, T, TENSORS, MlpDesc, MxfError, abi_version, grouped_mlp_bwd, grouped_mlp_fwd,
                    last_error, lib, make_desc, mlp_saved_bytes, mlp_tensor, mlp_workspace_bytes,
-                   mxfp8_quantize, pack_w13, quantize, query_device, read_status, unpack_w13)
+                   mxfp8_quantize, pack_w13, profile_begin, profile_end, quantize, query_device,
+                   read_status, unpack_w13)
 
 # shapes of the documented tensors, as functions of (E, D, F, m_capacity)
 _SHAPES = {

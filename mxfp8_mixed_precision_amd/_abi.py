@@ -32,13 +32,18 @@ T = {name: i for i, name in enumerate(TENSORS)}
 
 EXPORTS = ["mxf_abi_version", "mxf_query_device", "mxf_last_error", "mxfp8_quantize",
            "mxf_mlp_saved_bytes", "mxf_mlp_workspace_bytes", "mxf_mlp_tensor", "grouped_mlp_fwd",
-           "grouped_mlp_bwd", "mxf_read_status", "mxf_pack_w13", "mxf_unpack_w13"]
+           "grouped_mlp_bwd", "mxf_read_status", "mxf_profile_begin", "mxf_profile_end",
+           "mxf_pack_w13", "mxf_unpack_w13"]
 
 
 class MxfError(RuntimeError):
     def __init__(self, status, message):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
         self.status = status
+
+
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double)]
 
 
 class MlpDesc(ctypes.Structure):
@@ -72,6 +77,8 @@ def lib():
             "grouped_mlp_fwd": (ctypes.c_int, [pdesc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "grouped_mlp_bwd": (ctypes.c_int, [pdesc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "mxf_read_status": (ctypes.c_int, [vp, vp, ctypes.POINTER(i32)]),
+            "mxf_profile_begin": (ctypes.c_int, [i32]),
+            "mxf_profile_end": (ctypes.c_int, [ctypes.POINTER(KernelTime), i32, ctypes.POINTER(i32)]),
             "mxf_pack_w13": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp]),
             "mxf_unpack_w13": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp]),
         }
@@ -193,3 +200,16 @@ def pack_w13(w1, w3, w13, E, F, D, stream=None):
 
 def unpack_w13(w13, w1, w3, E, F, D, stream=None):
     _check(lib().mxf_unpack_w13(_ptr(w13), _ptr(w1), _ptr(w3), E, F, D, _stream(stream)))
+
+
+def profile_begin(capacity=4096):
+    """Start per-kernel event timing on this thread (see mxf_profile_begin)."""
+    _check(lib().mxf_profile_begin(capacity))
+
+
+def profile_end():
+    """Stop timing; returns {kernel name: (launches, total_ms)}."""
+    buf = (KernelTime * 64)()
+    n = ctypes.c_int32(0)
+    _check(lib().mxf_profile_end(buf, 64, ctypes.byref(n)))
+    return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(n.value)}

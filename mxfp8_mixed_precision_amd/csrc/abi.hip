@@ -15,6 +15,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "kernels.h"
 #include "mxfp8.h"
@@ -63,6 +64,38 @@ mxf_status check_device() {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ------------------------------------------------------------------ kernel timing
+
+struct Profile {
+  bool on = false;
+  int used = 0;
+  std::vector<hipEvent_t> ev;     // 2 per launch
+  std::vector<const char*> name;  // per launch
+  ~Profile() {
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+  }
+};
+thread_local Profile g_prof;
+
+// Brackets one kernel launch with events when profiling is on; `launch` returns hipError_t.
+template <class Fn>
+hipError_t timed(const char* name, hipStream_t st, Fn&& launch) {
+  Profile& P = g_prof;
+  const bool rec = P.on && P.used < (int)P.name.size();
+  if (rec) {
+    hipError_t e = hipEventRecord(P.ev[2 * P.used], st);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch();
+  if (e != hipSuccess) return e;
+  if (rec) {
+    e = hipEventRecord(P.ev[2 * P.used + 1], st);
+    if (e != hipSuccess) return e;
+    P.name[P.used++] = name;
+  }
+  return hipSuccess;
+}
 
 // ------------------------------------------------------------------ MLP buffer layout
 
@@ -177,8 +210,9 @@ mxf_status mxfp8_quantize(const void* x, int64_t rows, int64_t cols, uint32_t mo
   if ((mode & MXF_COL) && !aligned16(q_col)) return fail(MXF_E_ALIGN, "q_col is not 16-byte aligned");
   mxf_status s = check_device();
   if (s != MXF_OK) return s;
-  MXF_HIP(mxf_launch_quantize(x, rows, cols, mode, q_row, s_row, q_col, s_col, (hipStream_t)stream),
-          "quantize launch");
+  MXF_HIP(timed("quantize", (hipStream_t)stream, [&] {
+            return mxf_launch_quantize(x, rows, cols, mode, q_row, s_row, q_col, s_col, (hipStream_t)stream);
+          }), "quantize launch");
   return MXF_OK;
 }
 
@@ -239,13 +273,19 @@ mxf_status grouped_mlp_fwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   const int64_t M = desc->m_capacity, D = desc->D, F = desc->F, E = desc->E;
   const bool dbg = (desc->flags & MXF_DEBUG_F32) != 0;
 
-  MXF_HIP(mxf_launch_quant_weights(w1, w3, true, E, 2 * F, D, T(MXF_T_W13Q_R), T(MXF_T_W13S_R),
-                                   T(MXF_T_W13Q_C), T(MXF_T_W13S_C), st), "W13 quantize launch");
-  MXF_HIP(mxf_launch_quant_weights(w2, nullptr, false, E, D, F, T(MXF_T_W2Q_R), T(MXF_T_W2S_R),
-                                   T(MXF_T_W2Q_C), T(MXF_T_W2S_C), st), "W2 quantize launch");
-  MXF_HIP(mxf_launch_quant_tokens(x, M, D, offs, counts, (int)E, desc->pad_multiple, T(MXF_T_XQ_R),
-                                  T(MXF_T_XS_R), T(MXF_T_XQ_C), T(MXF_T_XS_C), (int32_t*)T(MXF_T_STATUS), st),
-          "X quantize launch");
+  MXF_HIP(timed("quant_w13", st, [&] {
+            return mxf_launch_quant_weights(w1, w3, true, E, 2 * F, D, T(MXF_T_W13Q_R), T(MXF_T_W13S_R),
+                                            T(MXF_T_W13Q_C), T(MXF_T_W13S_C), st);
+          }), "W13 quantize launch");
+  MXF_HIP(timed("quant_w2", st, [&] {
+            return mxf_launch_quant_weights(w2, nullptr, false, E, D, F, T(MXF_T_W2Q_R), T(MXF_T_W2S_R),
+                                            T(MXF_T_W2Q_C), T(MXF_T_W2S_C), st);
+          }), "W2 quantize launch");
+  MXF_HIP(timed("quant_x", st, [&] {
+            return mxf_launch_quant_tokens(x, M, D, offs, counts, (int)E, desc->pad_multiple, T(MXF_T_XQ_R),
+                                           T(MXF_T_XS_R), T(MXF_T_XQ_C), T(MXF_T_XS_C),
+                                           (int32_t*)T(MXF_T_STATUS), st);
+          }), "X quantize launch");
 
   mxf::GemmParams p = {};
   p.offs = offs;
@@ -262,7 +302,7 @@ mxf_status grouped_mlp_fwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   p.h13 = (uint16_t*)T(MXF_T_H13);
   p.q_r = T(MXF_T_HQ_R); p.s_r = T(MXF_T_HS_R); p.q_c = T(MXF_T_HQ_C); p.s_c = T(MXF_T_HS_C);
   p.dbg = dbg ? (float*)T(MXF_T_H13_F32) : nullptr;
-  MXF_HIP(mxf_launch_gemm_mgroup(1, p, st), "FC1 launch");
+  MXF_HIP(timed("fc1_swiglu", st, [&] { return mxf_launch_gemm_mgroup(1, p, st); }), "FC1 launch");
   // FC2
   p.A = T(MXF_T_HQ_R); p.As = T(MXF_T_HS_R); p.lda = F; p.ldas = F / 32;
   p.B = T(MXF_T_W2Q_R); p.Bs = T(MXF_T_W2S_R); p.ldb = F; p.ldbs = F / 32;
@@ -270,7 +310,7 @@ mxf_status grouped_mlp_fwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   p.N = D; p.K = F;
   p.C = y; p.ldc = D; p.out_f32 = (desc->flags & MXF_OUT_F32) ? 1 : 0;
   p.dbg = nullptr;
-  MXF_HIP(mxf_launch_gemm_mgroup(0, p, st), "FC2 launch");
+  MXF_HIP(timed("fc2", st, [&] { return mxf_launch_gemm_mgroup(0, p, st); }), "FC2 launch");
   return MXF_OK;
 }
 
@@ -296,9 +336,11 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   const bool dbg = (desc->flags & MXF_DEBUG_F32) != 0;
   const int of32 = (desc->flags & MXF_OUT_F32) ? 1 : 0;
 
-  MXF_HIP(mxf_launch_quant_tokens(dy, M, D, offs, counts, (int)E, desc->pad_multiple, T(MXF_T_DYQ_R),
-                                  T(MXF_T_DYS_R), T(MXF_T_DYQ_C), T(MXF_T_DYS_C), (int32_t*)T(MXF_T_STATUS), st),
-          "dY quantize launch");
+  MXF_HIP(timed("quant_dy", st, [&] {
+            return mxf_launch_quant_tokens(dy, M, D, offs, counts, (int)E, desc->pad_multiple, T(MXF_T_DYQ_R),
+                                           T(MXF_T_DYS_R), T(MXF_T_DYQ_C), T(MXF_T_DYS_C),
+                                           (int32_t*)T(MXF_T_STATUS), st);
+          }), "dY quantize launch");
   mxf::GemmParams p = {};
   p.offs = offs;
   p.counts = counts;
@@ -314,7 +356,7 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   p.h13 = (uint16_t*)T(MXF_T_H13);
   p.q_r = T(MXF_T_DHQ_R); p.s_r = T(MXF_T_DHS_R); p.q_c = T(MXF_T_DHQ_C); p.s_c = T(MXF_T_DHS_C);
   p.dbg = dbg ? (float*)T(MXF_T_DH_F32) : nullptr;
-  MXF_HIP(mxf_launch_gemm_mgroup(2, p, st), "FC2 dgrad launch");
+  MXF_HIP(timed("fc2_dgrad_dswiglu", st, [&] { return mxf_launch_gemm_mgroup(2, p, st); }), "FC2 dgrad launch");
   p.dbg = nullptr;
   p.out_f32 = of32;
   // FC2 wgrad: dW2[e] = dY^T h over the expert's tokens
@@ -322,7 +364,7 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   p.B = T(MXF_T_HQ_C); p.Bs = T(MXF_T_HS_C); p.ldb = M; p.ldbs = M / 32;
   p.M = D; p.N = F; p.K = M;
   p.C = dw2; p.ldc = F; p.c_es = D * F;
-  MXF_HIP(mxf_launch_gemm_kgroup(0, p, st), "FC2 wgrad launch");
+  MXF_HIP(timed("fc2_wgrad", st, [&] { return mxf_launch_gemm_kgroup(0, p, st); }), "FC2 wgrad launch");
   // FC1 dgrad: dX = dH13 W13
   p.M = M;
   p.A = T(MXF_T_DHQ_R); p.As = T(MXF_T_DHS_R); p.lda = 2 * F; p.ldas = 2 * F / 32;
@@ -330,13 +372,13 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   p.b_es = D * 2 * F; p.bs_es = D * 2 * F / 32;
   p.N = D; p.K = 2 * F;
   p.C = dx; p.ldc = D;
-  MXF_HIP(mxf_launch_gemm_mgroup(0, p, st), "FC1 dgrad launch");
+  MXF_HIP(timed("fc1_dgrad", st, [&] { return mxf_launch_gemm_mgroup(0, p, st); }), "FC1 dgrad launch");
   // FC1 wgrad: dW13[e] = dH13^T X over the expert's tokens, unpacked into dW1 / dW3
   p.A = T(MXF_T_DHQ_C); p.As = T(MXF_T_DHS_C); p.lda = M; p.ldas = M / 32;
   p.B = T(MXF_T_XQ_C); p.Bs = T(MXF_T_XS_C); p.ldb = M; p.ldbs = M / 32;
   p.M = 2 * F; p.N = D; p.K = M;
   p.C = dw1; p.C2 = dw3; p.ldc = D; p.c_es = F * D;
-  MXF_HIP(mxf_launch_gemm_kgroup(3, p, st), "FC1 wgrad launch");
+  MXF_HIP(timed("fc1_wgrad", st, [&] { return mxf_launch_gemm_kgroup(3, p, st); }), "FC1 wgrad launch");
   return MXF_OK;
 }
 
@@ -345,6 +387,48 @@ mxf_status mxf_read_status(const void* workspace, void* stream, int32_t* device_
   if (!workspace || !device_status) return fail(MXF_E_NULL, "workspace/device_status is NULL");
   MXF_HIP(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
   MXF_HIP(hipMemcpy(device_status, workspace, sizeof(int32_t), hipMemcpyDeviceToHost), "hipMemcpy");
+  return MXF_OK;
+}
+
+mxf_status mxf_profile_begin(int32_t capacity) {
+  g_err.clear();
+  if (capacity < 1 || capacity > (1 << 20)) return fail(MXF_E_ARG, "capacity = %d: must be in [1, 2^20]", capacity);
+  Profile& P = g_prof;
+  while ((int)P.ev.size() < 2 * capacity) {
+    hipEvent_t e;
+    MXF_HIP(hipEventCreate(&e), "hipEventCreate");
+    P.ev.push_back(e);
+  }
+  P.name.assign(capacity, nullptr);
+  P.used = 0;
+  P.on = true;
+  return MXF_OK;
+}
+
+mxf_status mxf_profile_end(mxf_kernel_time* out, int32_t max_out, int32_t* n_out) {
+  g_err.clear();
+  Profile& P = g_prof;
+  if (!P.on) return fail(MXF_E_ARG, "mxf_profile_end without mxf_profile_begin on this thread");
+  if (!out || !n_out) return fail(MXF_E_NULL, "out/n_out is NULL");
+  P.on = false;
+  int n = 0;
+  for (int i = 0; i < P.used; ++i) {
+    MXF_HIP(hipEventSynchronize(P.ev[2 * i + 1]), "hipEventSynchronize");
+    float ms = 0.0f;
+    MXF_HIP(hipEventElapsedTime(&ms, P.ev[2 * i], P.ev[2 * i + 1]), "hipEventElapsedTime");
+    int k = 0;
+    while (k < n && strcmp(out[k].name, P.name[i]) != 0) ++k;
+    if (k == n) {
+      if (n == max_out) continue;
+      memset(&out[k], 0, sizeof(out[k]));
+      snprintf(out[k].name, sizeof(out[k].name), "%s", P.name[i]);
+      ++n;
+    }
+    out[k].launches += 1;
+    out[k].total_ms += ms;
+  }
+  *n_out = n;
+  P.used = 0;
   return MXF_OK;
 }
 
