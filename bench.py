@@ -112,6 +112,8 @@ def main():
     ap.add_argument("--sets", type=int, default=3, help="rotating input sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quant", action="store_true", help="skip the standalone quantizer measurement")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference kernel for HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -126,6 +128,15 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        nbytes = 1 << 30
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 3}), flush=True)
+        return
     mx.lib()
     cfg = workloads.MLP_CONFIGS[args.workload]
     E, D, F, pad = cfg["E"], cfg["D"], cfg["F"], cfg["pad"]

@@ -45,80 +45,73 @@ template <int BM, int BN, int WM, int WN>
 struct Tile {
   static constexpr int BK = 128;
   static constexpr int NT = WM * WN * 64;
+  static constexpr int NW = WM * WN;
   static constexpr int TM = BM / WM;
   static constexpr int TN = BN / WN;
   static constexpr int FM = TM / 32;
   static constexpr int FN = TN / 32;
+  // one pipeline stage: A tile [BM][128 B], B tile [BN][128 B], then one 256-byte slot of
+  // scale words per wavefront for A and for B (rows beyond BM / BN land in unused slots)
   static constexpr int A_OFF = 0;
   static constexpr int B_OFF = BM * BK;
   static constexpr int SA_OFF = (BM + BN) * BK;
-  static constexpr int SB_OFF = SA_OFF + (BM > NT ? BM : NT) * 4;  // every thread stores a scale
-  static constexpr int STAGE = SB_OFF + (BN > NT ? BN : NT) * 4;   // word (extra ones are unused)
-  static constexpr int CA = BM * 8 / NT;  // 16-byte A chunks per thread per K step
-  static constexpr int CB = BN * 8 / NT;
-  // epilogue staging (per wavefront, bf16 elements): SwiGLU h tile TM x (TN/2 + 8),
-  // dSwiGLU packed tile TM x (2TN + 8)
-  static constexpr int EPI_ROWS = 64;  // epilogues stage 64 rows of a wavefront tile at a time
+  static constexpr int SB_OFF = SA_OFF + NW * 256;
+  static constexpr int STAGE = SB_OFF + NW * 256;
+  static constexpr int LDS_BYTES = 160 * 1024;
+  static constexpr int S = LDS_BYTES / STAGE >= 4 ? 4 : LDS_BYTES / STAGE;  // stages (S-1 steps in flight)
+  static constexpr int IA = BM / 8 / NW;  // 1 KB direct-to-LDS loads of the A tile, per wavefront
+  static constexpr int IB = BN / 8 / NW;
+  static constexpr int L = IA + IB + 2;   // loads per wavefront per K step (with the scale words)
+  static constexpr int EPI_ROWS = TN > 64 ? 32 : 64;  // rows of a wavefront tile staged at a time
   static constexpr int EPI_SW = EPI_ROWS * (TN / 2 + 8) * 2;
   static constexpr int EPI_DSW = EPI_ROWS * ((TN + 8) + (2 * TN + 8)) * 2;
-  static constexpr int LDS_MAIN = 2 * STAGE;
+  static constexpr int LDS_MAIN = S * STAGE;
   static constexpr int imax(int a, int b) { return a > b ? a : b; }
-  // LDS of a kernel instance: the main loop's two stages or its epilogue's staging
+  // LDS of a kernel instance: the main loop's stages or its epilogue's staging
   static constexpr int lds(int epi) {
-    return imax(LDS_MAIN, epi == 2 ? EPI_DSW * WM * WN : epi == 1 ? EPI_SW * WM * WN : 0);
+    return imax(LDS_MAIN, epi == 2 ? EPI_DSW * NW : epi == 1 ? EPI_SW * NW : 0);
   }
-  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile/thread mismatch");
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile/wavefront mismatch");
+  static_assert(BM <= 64 * NW && BN <= 64 * NW, "one scale-word load per wavefront and operand");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 fragments");
+  static_assert(S * STAGE <= LDS_BYTES && S >= 2, "pipeline does not fit in LDS");
+  static_assert(IA % 2 == 0 && IB % 2 == 0, "the swizzle alternates between load pairs");
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+// LDS tile layout: 128-byte rows, 16-byte chunk c of row r stored at chunk c ^ ((r / 2) % 8). A
+// 16-lane phase of ds_read_b128 reads 16 consecutive rows at one chunk index; with 64 banks
+// (256 bytes) the even rows then cover bank slots 0-7 and the odd rows slots 8-15 once each.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
 __device__ __forceinline__ void store_out(void* C, int64_t idx, float v, int f32) {
   if (f32) reinterpret_cast<float*>(C)[idx] = v;
   else reinterpret_cast<uint16_t*>(C)[idx] = (uint16_t)bf16_bits(v);
 }
 
-// Staging registers of one K step, held in vector registers (4 dwords per 16-byte chunk).
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt low bits
+// [3:0] and high bits [15:14]; expcnt 7 and lgkmcnt 15 mean "no wait").
 template <int N>
-struct Stage {
-  typedef unsigned int vec __attribute__((ext_vector_type(4 * N)));
-};
-
-// Global loads of one K step into the staging registers (see the kernel for the chunk map).
-template <int CA, int CB>
-__device__ __forceinline__ void gload(typename Stage<CA>::vec& ra, typename Stage<CB>::vec& rb,
-                                      uint32_t& rsa, uint32_t& rsb, const uint8_t* a_src,
-                                      const uint8_t* b_src, int64_t a_step, int64_t b_step,
-                                      const uint8_t* sa_src, const uint8_t* sb_src, int64_t k0) {
-#pragma unroll
-  for (int i = 0; i < CA; ++i) {
-    const uint4 v = *reinterpret_cast<const uint4*>(a_src + i * a_step + k0);
-    ra[4 * i] = v.x; ra[4 * i + 1] = v.y; ra[4 * i + 2] = v.z; ra[4 * i + 3] = v.w;
-  }
-#pragma unroll
-  for (int i = 0; i < CB; ++i) {
-    const uint4 v = *reinterpret_cast<const uint4*>(b_src + i * b_step + k0);
-    rb[4 * i] = v.x; rb[4 * i + 1] = v.y; rb[4 * i + 2] = v.z; rb[4 * i + 3] = v.w;
-  }
-  rsa = *reinterpret_cast<const uint32_t*>(sa_src + k0 / 32);
-  rsb = *reinterpret_cast<const uint32_t*>(sb_src + k0 / 32);
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Staging registers -> one LDS stage (A/B tiles swizzled, scale words per row).
-template <int CA, int CB, int BM, int BN, int RSTEP>
-__device__ __forceinline__ void sstore(uint8_t* a_lds, uint8_t* b_lds, uint8_t* sa_lds, uint8_t* sb_lds,
-                                       const typename Stage<CA>::vec& ra, const typename Stage<CB>::vec& rb,
-                                       uint32_t rsa, uint32_t rsb, int ab_dst, int tid) {
-#pragma unroll
-  for (int i = 0; i < CA; ++i)
-    *reinterpret_cast<uint4*>(a_lds + ab_dst + i * RSTEP * 128) =
-        make_uint4(ra[4 * i], ra[4 * i + 1], ra[4 * i + 2], ra[4 * i + 3]);
-#pragma unroll
-  for (int i = 0; i < CB; ++i)
-    *reinterpret_cast<uint4*>(b_lds + ab_dst + i * RSTEP * 128) =
-        make_uint4(rb[4 * i], rb[4 * i + 1], rb[4 * i + 2], rb[4 * i + 3]);
-  *reinterpret_cast<uint32_t*>(sa_lds + tid * 4) = rsa;  // branch-free: rows >= BM / BN land
-  *reinterpret_cast<uint32_t*>(sb_lds + tid * 4) = rsb;  // in unused padding
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Direct global -> LDS loads (gfx950 global_load_lds_dword{,x4}): lane l's bytes land at LDS
+// address m0 + size * l. Written as inline asm so that the compiler's wait insertion does not
+// treat every LDS read as aliasing the in-flight fills (it would drain the pipeline with
+// vmcnt(0) before each read); the kernel waits on vmcnt itself. M0 is set in the same asm
+// block and clobbered; the instruction has no destination VGPRs.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_ptr)p;
+}
+// Address = wavefront-uniform 64-bit base (SGPRs) + per-lane 32-bit offset (one VGPR).
+__device__ __forceinline__ void g2lds16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+__device__ __forceinline__ void g2lds4(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
 }
 
 template <int BM, int BN, int WM, int WN, int SCHED, int EPI>
@@ -215,39 +208,55 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  // global -> register staging of the next K step, then register -> LDS with the XOR swizzle.
-  // Chunk q = tid + i * NT of a tile is row q / 8, bytes 16 * (q % 8); since NT / 8 is a
-  // multiple of 8, row % 8 and q % 8 depend on tid only, so every chunk of a thread is its
-  // first chunk plus i rows-of-NT/8.
-  constexpr int RSTEP = T::NT / 8;  // rows between a thread's chunks
-  static_assert(RSTEP % 8 == 0, "swizzle assumes NT / 8 is a multiple of 8");
-  typename Stage<T::CA>::vec ra;
-  typename Stage<T::CB>::vec rb;
-  uint32_t rsa = 0, rsb = 0;
-  const uint8_t* a_src = Ag + (int64_t)(tid >> 3) * p.lda + ((tid & 7) << 4);
-  const uint8_t* b_src = Bg + (int64_t)(tid >> 3) * p.ldb + ((tid & 7) << 4);
-  const int64_t a_step = (int64_t)RSTEP * p.lda;
-  const int64_t b_step = (int64_t)RSTEP * p.ldb;
-  const int ab_dst = swz(tid >> 3, tid & 7);  // A and B share the in-tile layout
-  const uint8_t* sa_src = Asg + (int64_t)(tid % BM) * p.ldas;  // threads past BM/BN re-read a
-  const uint8_t* sb_src = Bsg + (int64_t)(tid % BN) * p.ldbs;  // valid row (stored to padding)
-
-#define MXF_GLOAD(kt_) gload<T::CA, T::CB>(ra, rb, rsa, rsb, a_src, b_src, a_step, b_step, sa_src, sb_src, (int64_t)(kt_) * T::BK)
-#define MXF_SSTORE(stage_) sstore<T::CA, T::CB, BM, BN, RSTEP>(smem + (stage_) * T::STAGE + T::A_OFF, smem + (stage_) * T::STAGE + T::B_OFF, smem + (stage_) * T::STAGE + T::SA_OFF, smem + (stage_) * T::STAGE + T::SB_OFF, ra, rb, rsa, rsb, ab_dst, tid)
-
+  // Pipeline: S LDS stages in a ring, filled by direct global->LDS loads (no register
+  // staging), S-1 K steps in flight. A wavefront's 1 KB load writes LDS bytes
+  // [base, base + 1024) in lane order (16 bytes per lane), so the swizzle of the tile layout
+  // is applied on the global side: the lane that lands on LDS chunk (row, c) fetches global
+  // chunk (row, c ^ ((row / 2) % 8)). A load covers 8 consecutive tile rows starting at a
+  // multiple of 8, lane l at row offset l / 8; so (row / 2) % 8 = 4 * (load index % 2) + l / 16
+  // and the source chunk only alternates between even and odd loads.
   const int r32 = lane & 31;
   const int g = lane >> 5;
+  const int64_t lrow = lane >> 3;  // row within a 1 KB load
+  const uint32_t lcol0 = (uint32_t)(((lane & 7) ^ (lane >> 4)) << 4);        // even loads
+  const uint32_t lcol1 = (uint32_t)(((lane & 7) ^ (4 | (lane >> 4))) << 4);  // odd loads
+  const int wid_u = __builtin_amdgcn_readfirstlane(wid);  // wavefront-uniform (SGPR) copy
+  const uint8_t* a_s = Ag + (int64_t)wid_u * T::IA * 8 * p.lda;  // this wavefront's first rows
+  const uint8_t* b_s = Bg + (int64_t)wid_u * T::IB * 8 * p.ldb;
+  const uint32_t a_v0 = (uint32_t)(lrow * p.lda) + lcol0, a_v1 = (uint32_t)(lrow * p.lda) + lcol1;
+  const uint32_t b_v0 = (uint32_t)(lrow * p.ldb) + lcol0, b_v1 = (uint32_t)(lrow * p.ldb) + lcol1;
+  const uint32_t sa_v = (uint32_t)(((wid * 64 + lane) % BM) * p.ldas);
+  const uint32_t sb_v = (uint32_t)(((wid * 64 + lane) % BN) * p.ldbs);
+  const int64_t a8 = 8 * p.lda, b8 = 8 * p.ldb;
+  const uint32_t lds0 = lds_addr(smem);
+  auto issue = [&](int kt, int stage) {
+    const int64_t k0 = (int64_t)kt * T::BK;
+    const uint32_t st = lds0 + stage * T::STAGE;
+#pragma unroll
+    for (int i = 0; i < T::IA; ++i)
+      g2lds16(a_s + i * a8 + k0, (i & 1) ? a_v1 : a_v0, st + T::A_OFF + (wid_u * T::IA + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < T::IB; ++i)
+      g2lds16(b_s + i * b8 + k0, (i & 1) ? b_v1 : b_v0, st + T::B_OFF + (wid_u * T::IB + i) * 1024);
+    g2lds4(Asg + k0 / 32, sa_v, st + T::SA_OFF + wid_u * 256);
+    g2lds4(Bsg + k0 / 32, sb_v, st + T::SB_OFF + wid_u * 256);
+  };
+
   if (KT > 0) {
-    MXF_GLOAD(0);
-    MXF_SSTORE(0);
-    __syncthreads();
+    // prologue: steps 0 .. S-2 (clamped to the last step; a surplus load fills a stage that
+    // is never read, which keeps every wavefront's load count per step fixed)
+#pragma unroll
+    for (int st = 0; st < T::S - 1; ++st) issue(st < KT ? st : KT - 1, st);
   }
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    // prefetch the next K step (the last iteration re-reads its own step; nothing is stored)
-    MXF_GLOAD(kt + 1 < KT ? kt + 1 : kt);
-    __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before this step's LDS reads / MFMAs
-    const uint8_t* base = smem + cur * T::STAGE;
+    // this wavefront's loads of step kt are done once at most (S-2) steps' loads remain
+    wait_vmcnt<(T::S - 2) * T::L>();
+    __syncthreads();  // every wavefront's step-kt data is in LDS; step kt-1 fully consumed
+    {
+      const int nxt = kt + T::S - 1;
+      issue(nxt < KT ? nxt : KT - 1, nxt % T::S);  // refill the stage consumed at step kt-1
+    }
+    const uint8_t* base = smem + (kt % T::S) * T::STAGE;
     uint32_t sa[T::FM], sb[T::FN];
 #pragma unroll
     for (int i = 0; i < T::FM; ++i)
@@ -284,16 +293,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
                                                                         (int)sa[i], 2, (int)sb[j]);
         }
     }
-    // keep the MFMAs ahead of the LDS stores of the prefetched step, so the global-load
-    // latency overlaps the matrix work instead of stalling before it
-    __builtin_amdgcn_sched_barrier(0);
-    // unconditional, so the K step stays one basic block: on the last step this rewrites the
-    // idle buffer (last read one step earlier, before the previous barrier) and nobody reads it
-    MXF_SSTORE(cur ^ 1);
-    __syncthreads();
   }
-#undef MXF_GLOAD
-#undef MXF_SSTORE
+  if (KT > 0) {
+    wait_vmcnt<0>();  // surplus loads must land before the epilogue reuses LDS
+  }
 
   // ------------------------------------------------------------------ epilogues
   const int64_t wrow0 = m0 + wm * T::TM;  // first output row of this wavefront
@@ -329,7 +332,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
     static_assert(T::FN % 2 == 0, "SwiGLU epilogue needs whole gate/up column pairs");
     constexpr int HC = T::TN / 2;                 // h columns per wavefront
     constexpr int HP = HC + 8;                    // LDS pitch (bf16 elements)
-    constexpr int RC = T::TM < 64 ? T::TM : 64;   // rows per chunk
+    constexpr int RC = T::TM < T::EPI_ROWS ? T::TM : T::EPI_ROWS;  // rows per chunk
     constexpr int FC = RC / 32;                   // fragments per chunk
     const int64_t ldn = p.N;                      // 2F
     const int64_t F = p.N / 2;
@@ -406,7 +409,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
     constexpr int DP = T::TN + 8;   // dh tile pitch (bf16 elements)
     constexpr int PC = 2 * T::TN;   // packed columns per wavefront
     constexpr int HP = PC + 8;
-    constexpr int RC = T::TM < 64 ? T::TM : 64;
+    constexpr int RC = T::TM < T::EPI_ROWS ? T::TM : T::EPI_ROWS;
     constexpr int FC = RC / 32;
     const int64_t F = p.N;
     const int64_t ld13 = 2 * F;
@@ -496,8 +499,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
 
 // ------------------------------------------------------------------ host launchers
 
-// Tile configurations: 256x128 (wavefront tile 128x64) where the dimensions allow it, else
-// 128x128 (wavefront tile 64x64). M-grouped tiles must divide pad_multiple.
+// Tile configurations (4 wavefronts): 256x128 (wavefront tile 128x64) where the dimensions
+// allow, else 128x128 (64x64). M-grouped row tiles divide pad_multiple. (256x256 with a
+// 128x128 wavefront tile measured slower: only two LDS stages fit and its epilogues spill.)
 template <int BM, int BN, int SCHED, int EPI>
 static hipError_t launch_cfg(const GemmParams& p, hipStream_t st) {
   // 1-D grids: the kernel maps block ids to tiles (see the schedulers)
