@@ -72,7 +72,8 @@ def traffic_for(kernel, workload):
 
 def cpu_baseline(prob):
     """The oracle (as it stands) on a bounded sample of the same workload: the full fwd+bwd of
-    the three smallest non-empty experts, timed on the host cores."""
+    the smallest non-empty experts holding at least 2500 routed rows together, timed on the
+    host cores."""
     import numpy as np
     import workloads
     from oracle import mlp as om
@@ -83,7 +84,11 @@ def cpu_baseline(prob):
     except Exception:
         threads = os.cpu_count()
     counts = prob["counts"]
-    order = sorted([e for e in range(len(counts)) if counts[e] > 0], key=lambda e: counts[e])[:3]
+    order = []
+    for e in sorted([e for e in range(len(counts)) if counts[e] > 0], key=lambda e: counts[e]):
+        order.append(e)
+        if sum(counts[i] for i in order) >= 2500:
+            break
     D, F, pad = prob["D"], prob["F"], prob["pad"]
     sub_counts = [counts[e] for e in order]
     sub_offs = workloads.padded_offsets(sub_counts, pad)
@@ -114,6 +119,8 @@ def main():
     ap.add_argument("--no-quant", action="store_true", help="skip the standalone quantizer measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference kernel for HBM byte counters)")
+    ap.add_argument("--quant-only", action="store_true",
+                    help="only measure the standalone quantizer (for a profiler run of that kernel alone)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -136,6 +143,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 3}), flush=True)
+        return
+    if args.quant_only:
+        mx.lib()
+        print(json.dumps({"quantize": bench_quantize(mx, torch, dev, args)}), flush=True)
         return
     mx.lib()
     cfg = workloads.MLP_CONFIGS[args.workload]
