@@ -229,34 +229,38 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
   const uint32_t sb_v = (uint32_t)(((wid * 64 + lane) % BN) * p.ldbs);
   const int64_t a8 = 8 * p.lda, b8 = 8 * p.ldb;
   const uint32_t lds0 = lds_addr(smem);
-  auto issue = [&](int kt, int stage) {
-    const int64_t k0 = (int64_t)kt * T::BK;
-    const uint32_t st = lds0 + stage * T::STAGE;
-#pragma unroll
-    for (int i = 0; i < T::IA; ++i)
-      g2lds16(a_s + i * a8 + k0, (i & 1) ? a_v1 : a_v0, st + T::A_OFF + (wid_u * T::IA + i) * 1024);
-#pragma unroll
-    for (int i = 0; i < T::IB; ++i)
+  // One of the L direct-to-LDS loads of a K step: q < IA are A-tile loads, then IB B-tile
+  // loads, then the A and B scale words. q is a compile-time constant at every call.
+  auto issue_one = [&](int q, int64_t k0, uint32_t st) {
+    if (q < T::IA) {
+      g2lds16(a_s + q * a8 + k0, (q & 1) ? a_v1 : a_v0, st + T::A_OFF + (wid_u * T::IA + q) * 1024);
+    } else if (q < T::IA + T::IB) {
+      const int i = q - T::IA;
       g2lds16(b_s + i * b8 + k0, (i & 1) ? b_v1 : b_v0, st + T::B_OFF + (wid_u * T::IB + i) * 1024);
-    g2lds4(Asg + k0 / 32, sa_v, st + T::SA_OFF + wid_u * 256);
-    g2lds4(Bsg + k0 / 32, sb_v, st + T::SB_OFF + wid_u * 256);
+    } else if (q == T::IA + T::IB) {
+      g2lds4(Asg + k0 / 32, sa_v, st + T::SA_OFF + wid_u * 256);
+    } else {
+      g2lds4(Bsg + k0 / 32, sb_v, st + T::SB_OFF + wid_u * 256);
+    }
   };
 
   if (KT > 0) {
     // prologue: steps 0 .. S-2 (clamped to the last step; a surplus load fills a stage that
     // is never read, which keeps every wavefront's load count per step fixed)
 #pragma unroll
-    for (int st = 0; st < T::S - 1; ++st) issue(st < KT ? st : KT - 1, st);
+    for (int st = 0; st < T::S - 1; ++st) {
+      const int64_t k0 = (int64_t)(st < KT ? st : KT - 1) * T::BK;
+#pragma unroll
+      for (int q = 0; q < T::L; ++q) issue_one(q, k0, lds0 + st * T::STAGE);
+    }
   }
+  constexpr int NMF = 2 * T::FM * T::FN;  // MFMAs per K step
   for (int kt = 0; kt < KT; ++kt) {
     // this wavefront's loads of step kt are done once at most (S-2) steps' loads remain
     wait_vmcnt<(T::S - 2) * T::L>();
     __syncthreads();  // every wavefront's step-kt data is in LDS; step kt-1 fully consumed
-    {
-      const int nxt = kt + T::S - 1;
-      issue(nxt < KT ? nxt : KT - 1, nxt % T::S);  // refill the stage consumed at step kt-1
-    }
     const uint8_t* base = smem + (kt % T::S) * T::STAGE;
+    // all fragments and scales of the step are read up front (LDS latency overlaps the MFMAs)
     uint32_t sa[T::FM], sb[T::FN];
 #pragma unroll
     for (int i = 0; i < T::FM; ++i)
@@ -264,35 +268,43 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < T::FN; ++j)
       sb[j] = *reinterpret_cast<const uint32_t*>(base + T::SB_OFF + (wn * T::TN + j * 32 + r32) * 4) >> (8 * g);
+    v8i af[2][T::FM], bf[2][T::FN];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      v8i af[T::FM], bf[T::FN];
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
       for (int i = 0; i < T::FM; ++i) {
         const int row = wm * T::TM + i * 32 + r32;
-        const uint4 lo = *reinterpret_cast<const uint4*>(base + T::A_OFF + swz(row, 4 * s + g));
-        const uint4 hi = *reinterpret_cast<const uint4*>(base + T::A_OFF + swz(row, 4 * s + 2 + g));
-        af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        const uint4 lo = *reinterpret_cast<const uint4*>(base + T::A_OFF + swz(row, 4 * h + g));
+        const uint4 hi = *reinterpret_cast<const uint4*>(base + T::A_OFF + swz(row, 4 * h + 2 + g));
+        af[h][i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
 #pragma unroll
       for (int j = 0; j < T::FN; ++j) {
         const int row = wn * T::TN + j * 32 + r32;
-        const uint4 lo = *reinterpret_cast<const uint4*>(base + T::B_OFF + swz(row, 4 * s + g));
-        const uint4 hi = *reinterpret_cast<const uint4*>(base + T::B_OFF + swz(row, 4 * s + 2 + g));
-        bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        const uint4 lo = *reinterpret_cast<const uint4*>(base + T::B_OFF + swz(row, 4 * h + g));
+        const uint4 hi = *reinterpret_cast<const uint4*>(base + T::B_OFF + swz(row, 4 * h + 2 + g));
+        bf[h][j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
-#pragma unroll
-      for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < T::FN; ++j) {
-          if (s == 0)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0,
-                                                                        (int)sa[i], 0, (int)sb[j]);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 2,
-                                                                        (int)sa[i], 2, (int)sb[j]);
-        }
     }
+    // MFMAs with the refill of the stage consumed at step kt-1 interleaved one load after each
+    // MFMA, so that a full load queue never holds the wavefront before its matrix work
+    const int nxt = kt + T::S - 1;
+    const int64_t nk0 = (int64_t)(nxt < KT ? nxt : KT - 1) * T::BK;
+    const uint32_t nst = lds0 + (nxt % T::S) * T::STAGE;
+#pragma unroll
+    for (int m = 0; m < NMF; ++m) {
+      const int h = m / (T::FM * T::FN), i = (m / T::FN) % T::FM, j = m % T::FN;
+      if (h == 0)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[0][i], bf[0][j], acc[i][j], 0, 0, 0,
+                                                                    (int)sa[i], 0, (int)sb[j]);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[1][i], bf[1][j], acc[i][j], 0, 0, 2,
+                                                                    (int)sa[i], 2, (int)sb[j]);
+      if (m < T::L) issue_one(m, nk0, nst);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int q = NMF; q < T::L; ++q) issue_one(q, nk0, nst);  // loads beyond the MFMA count
   }
   if (KT > 0) {
     wait_vmcnt<0>();  // surplus loads must land before the epilogue reuses LDS
