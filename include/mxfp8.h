@@ -111,7 +111,14 @@ typedef struct {
 } mxf_mlp_desc;
 
 /* Tensors held in the caller's buffers (for tests and inspection). Region: 0 = workspace,
- * 1 = saved (forward -> backward context). Codes u8, scales u8 (E8M0), h13 BF16. */
+ * 1 = saved (forward -> backward context). Codes u8, scales u8 (E8M0), h13 BF16.
+ *
+ * MXF_T_H13 (the BF16-rounded FC1 output g | u, kept for the backward pass) is stored
+ * fragment-tiled, in the order the matrix-core accumulators produce and consume it: records
+ * of 2048 BF16 values, record R * (F/32) + J holding rows 32R .. 32R+31 and h columns
+ * 32J .. 32J+31; inside a record, index ((s * 64) + c + 32 b) * 16 + 4 k + j (s = 0 gate,
+ * 1 up; b < 2, c < 32, k < 4, j < 4) holds row 32R + 8k + 4b + j, column 32J + c of the
+ * gate (s = 0) or up (s = 1) projection. Same size as [Mcap, 2F]. */
 typedef enum {
   MXF_T_STATUS = 0,                                       /* int32 status word (workspace) */
   MXF_T_XQ_R, MXF_T_XS_R,                                 /* [Mcap, D], [Mcap, D/32]       (ws)    */
@@ -120,7 +127,7 @@ typedef enum {
   MXF_T_W13Q_C, MXF_T_W13S_C,                             /* [E, D, 2F], [E, D, 2F/32]     (saved) */
   MXF_T_W2Q_R, MXF_T_W2S_R,                               /* [E, D, F], [E, D, F/32]       (ws)    */
   MXF_T_W2Q_C, MXF_T_W2S_C,                               /* [E, F, D], [E, F, D/32]       (saved) */
-  MXF_T_H13,                                              /* [Mcap, 2F] BF16, packed order (saved) */
+  MXF_T_H13,                                              /* Mcap*2F BF16, fragment-tiled (saved) */
   MXF_T_HQ_R, MXF_T_HS_R,                                 /* [Mcap, F], [Mcap, F/32]       (ws)    */
   MXF_T_HQ_C, MXF_T_HS_C,                                 /* [F, Mcap], [F, Mcap/32]       (saved) */
   MXF_T_DYQ_R, MXF_T_DYS_R, MXF_T_DYQ_C, MXF_T_DYS_C,     /* like X                        (ws)    */

@@ -31,6 +31,19 @@ _SHAPES = {
 }
 
 
+def h13_rowmajor(tiled, F):
+    """Row-major [M, 2F] copy of the fragment-tiled saved h13 (BF16, flat or any shape).
+
+    Stored order: 4096-byte records, record (R, J) = rows 32R..32R+31 x h columns
+    32J..32J+31, at record index R * (F/32) + J; inside a record, element
+    (s, b, c, k, j) -- s = 0 gate / 1 up, lane c + 32b, slot 4k + j -- is row
+    32R + 8k + 4b + j, packed column 64J + 32s + c.
+    """
+    t = tiled.reshape(-1, F // 32, 2, 2, 32, 4, 4)     # R, J, s, b, c, k, j
+    M = t.shape[0] * 32
+    return t.permute(0, 5, 3, 6, 1, 2, 4).reshape(M, 2 * F)  # R, k, b, j | J, s, c
+
+
 class MlpContext:
     """Descriptor plus caller-owned device buffers for one MLP configuration."""
 
@@ -45,15 +58,21 @@ class MlpContext:
         self.saved = torch.empty(nsaved, dtype=torch.uint8, device=device)
         self.workspace = torch.empty(nws, dtype=torch.uint8, device=device)
 
-    def view(self, name):
-        """A typed view of documented tensor `name` inside saved / workspace."""
-        import torch
+    def view_raw(self, name):
+        """The bytes of documented tensor `name` inside saved / workspace (uint8, flat)."""
         region, off, nbytes = mlp_tensor(self.desc, name)
         buf = self.saved if region == 1 else self.workspace
-        raw = buf[off:off + nbytes]
+        return buf[off:off + nbytes]
+
+    def view(self, name):
+        """A typed view of documented tensor `name` inside saved / workspace. H13, which the
+        library stores fragment-tiled (include/mxfp8.h), is returned as a row-major
+        [m_capacity, 2F] BF16 copy."""
+        import torch
+        raw = self.view_raw(name)
         shape = _SHAPES[name](self.E, self.D, self.F, self.m_capacity)
         if name == "H13":
-            return raw.view(torch.bfloat16).view(shape)
+            return h13_rowmajor(raw.view(torch.bfloat16), self.F)
         if name in ("H13_F32", "DH_F32"):
             return raw.view(torch.float32).view(shape)
         if name == "STATUS":

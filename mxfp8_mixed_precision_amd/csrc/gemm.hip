@@ -28,6 +28,8 @@
 //   K-grouped (both wgrads): blockIdx.z = expert; K runs over the expert's token segment
 //     (the real rows rounded up to 128; pad rows are zero codes). A zero-token expert runs
 //     no K step and stores zeros.
+#include <type_traits>
+
 #include "kernels.h"
 #include "mx_device.h"
 
@@ -43,45 +45,49 @@ enum GemmEpi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2, EPI_UNPACK13 = 3 
 
 template <int BM, int BN, int WM, int WN>
 struct Tile {
-  static constexpr int BK = 128;
+  static constexpr int BK = 64;   // K per pipeline stage (one MFMA K step)
+  static constexpr int S = 4;     // stages in the LDS ring
   static constexpr int NT = WM * WN * 64;
   static constexpr int NW = WM * WN;
   static constexpr int TM = BM / WM;
   static constexpr int TN = BN / WN;
   static constexpr int FM = TM / 32;
   static constexpr int FN = TN / 32;
-  // one pipeline stage: A tile [BM][128 B], B tile [BN][128 B], then one 256-byte slot of
-  // scale words per wavefront for A and for B (rows beyond BM / BN land in unused slots)
+  // one stage: A tile [BM][64 B], B tile [BN][64 B], then one 256-byte slot of scale words per
+  // wavefront for A and for B (rows beyond BM / BN land in unused slots). A scale word holds
+  // the four E8M0 bytes of 128 k, so both stages of a 128-k block load the same words.
   static constexpr int A_OFF = 0;
   static constexpr int B_OFF = BM * BK;
   static constexpr int SA_OFF = (BM + BN) * BK;
   static constexpr int SB_OFF = SA_OFF + NW * 256;
   static constexpr int STAGE = SB_OFF + NW * 256;
   static constexpr int LDS_BYTES = 160 * 1024;
-  static constexpr int S = LDS_BYTES / STAGE >= 4 ? 4 : LDS_BYTES / STAGE;  // stages (S-1 steps in flight)
-  static constexpr int IA = BM / 8 / NW;  // 1 KB direct-to-LDS loads of the A tile, per wavefront
-  static constexpr int IB = BN / 8 / NW;
-  static constexpr int L = IA + IB + 2;   // loads per wavefront per K step (with the scale words)
-  static constexpr int EPI_ROWS = TN > 64 ? 32 : 64;  // rows of a wavefront tile staged at a time
-  static constexpr int EPI_SW = EPI_ROWS * (TN / 2 + 8) * 2;
-  static constexpr int EPI_DSW = EPI_ROWS * ((TN + 8) + (2 * TN + 8)) * 2;
+  static constexpr int IA = BM / 16 / NW;  // 1 KB direct-to-LDS loads (16 rows) of A, per wavefront
+  static constexpr int IB = BN / 16 / NW;
+  static constexpr int L = IA + IB + 2;    // loads per wavefront per stage (with the scale words)
+  // epilogue staging: BF16 output tile; SwiGLU: row-major h tile + transposed codes + scales;
+  // dSwiGLU (one wavefront row at a time): packed dG/dU tile + transposed codes + scales
+  static constexpr int EPI_ST = BM * (BN + 8) * 2;
+  static constexpr int EPI_SW = BM * (BN / 2 + 8) * 2 + (BN / 2) * (BM + 8) + (BN / 2) * (BM / 32);
+  static constexpr int EPI_DSW = TM * (2 * BN + 8) * 2 + 2 * BN * (TM + 8) + 2 * BN * (TM / 32);
   static constexpr int LDS_MAIN = S * STAGE;
   static constexpr int imax(int a, int b) { return a > b ? a : b; }
   // LDS of a kernel instance: the main loop's stages or its epilogue's staging
   static constexpr int lds(int epi) {
-    return imax(LDS_MAIN, epi == 2 ? EPI_DSW * NW : epi == 1 ? EPI_SW * NW : 0);
+    return imax(LDS_MAIN, epi == 2 ? EPI_DSW : epi == 1 ? EPI_SW : EPI_ST);
   }
-  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile/wavefront mismatch");
+  static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "tile/wavefront mismatch");
   static_assert(BM <= 64 * NW && BN <= 64 * NW, "one scale-word load per wavefront and operand");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 fragments");
-  static_assert(S * STAGE <= LDS_BYTES && S >= 2, "pipeline does not fit in LDS");
-  static_assert(IA % 2 == 0 && IB % 2 == 0, "the swizzle alternates between load pairs");
+  static_assert(S * STAGE <= LDS_BYTES, "pipeline does not fit in LDS");
+  static_assert(S * L <= 63, "loads in flight exceed the vmcnt range");
 };
 
-// LDS tile layout: 128-byte rows, 16-byte chunk c of row r stored at chunk c ^ ((r / 2) % 8). A
-// 16-lane phase of ds_read_b128 reads 16 consecutive rows at one chunk index; with 64 banks
-// (256 bytes) the even rows then cover bank slots 0-7 and the odd rows slots 8-15 once each.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+// LDS tile layout: 64-byte rows, 16-byte chunk c of row r stored at chunk c ^ ((r / 4) % 4). A
+// 16-lane phase of ds_read_b128 reads 16 consecutive rows at one chunk index; four rows share
+// a 256-byte bank window and the XOR spreads the four windows' chunks, so the 16 reads hit
+// 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
 __device__ __forceinline__ void store_out(void* C, int64_t idx, float v, int f32) {
   if (f32) reinterpret_cast<float*>(C)[idx] = v;
@@ -198,7 +204,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
     Bg = p.B + n0 * p.ldb + kbeg;
     Bsg = p.Bs + n0 * p.ldbs + kbeg / 32;
   }
-  const int KT = (int)((kend - kbeg) / T::BK);
+  const int tr0 = wm * T::TM;  // first row / column of this wavefront within the block tile
+  const int tc0 = wn * T::TN;
+  const int KT = (int)((kend - kbeg) / T::BK);  // stages (even: K is a multiple of 128)
 
   v16f acc[T::FM][T::FN];
 #pragma unroll
@@ -208,302 +216,431 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  // Pipeline: S LDS stages in a ring, filled by direct global->LDS loads (no register
-  // staging), S-1 K steps in flight. A wavefront's 1 KB load writes LDS bytes
-  // [base, base + 1024) in lane order (16 bytes per lane), so the swizzle of the tile layout
-  // is applied on the global side: the lane that lands on LDS chunk (row, c) fetches global
-  // chunk (row, c ^ ((row / 2) % 8)). A load covers 8 consecutive tile rows starting at a
-  // multiple of 8, lane l at row offset l / 8; so (row / 2) % 8 = 4 * (load index % 2) + l / 16
-  // and the source chunk only alternates between even and odd loads.
+  // Direct global->LDS loads: a wavefront's 1 KB load covers 16 consecutive tile rows (starting
+  // at a multiple of 16) and writes LDS bytes [base, base + 1024) in lane order, 16 bytes per
+  // lane: lane l lands on row l / 4, LDS chunk l % 4. The swizzle is applied on the global
+  // side: that lane fetches chunk (l % 4) ^ ((row / 4) % 4) = (l % 4) ^ (l / 16), the same for
+  // every load, so one per-lane offset serves them all.
   const int r32 = lane & 31;
   const int g = lane >> 5;
-  const int64_t lrow = lane >> 3;  // row within a 1 KB load
-  const uint32_t lcol0 = (uint32_t)(((lane & 7) ^ (lane >> 4)) << 4);        // even loads
-  const uint32_t lcol1 = (uint32_t)(((lane & 7) ^ (4 | (lane >> 4))) << 4);  // odd loads
+  const int64_t lrow = lane >> 2;
+  const uint32_t lcol = (uint32_t)(((lane & 3) ^ (lane >> 4)) << 4);
   const int wid_u = __builtin_amdgcn_readfirstlane(wid);  // wavefront-uniform (SGPR) copy
-  const uint8_t* a_s = Ag + (int64_t)wid_u * T::IA * 8 * p.lda;  // this wavefront's first rows
-  const uint8_t* b_s = Bg + (int64_t)wid_u * T::IB * 8 * p.ldb;
-  const uint32_t a_v0 = (uint32_t)(lrow * p.lda) + lcol0, a_v1 = (uint32_t)(lrow * p.lda) + lcol1;
-  const uint32_t b_v0 = (uint32_t)(lrow * p.ldb) + lcol0, b_v1 = (uint32_t)(lrow * p.ldb) + lcol1;
+  const uint8_t* a_s = Ag + (int64_t)wid_u * T::IA * 16 * p.lda;  // this wavefront's first rows
+  const uint8_t* b_s = Bg + (int64_t)wid_u * T::IB * 16 * p.ldb;
+  const uint32_t a_v = (uint32_t)(lrow * p.lda) + lcol;
+  const uint32_t b_v = (uint32_t)(lrow * p.ldb) + lcol;
   const uint32_t sa_v = (uint32_t)(((wid * 64 + lane) % BM) * p.ldas);
   const uint32_t sb_v = (uint32_t)(((wid * 64 + lane) % BN) * p.ldbs);
-  const int64_t a8 = 8 * p.lda, b8 = 8 * p.ldb;
+  const int64_t a16 = 16 * p.lda, b16 = 16 * p.ldb;
   const uint32_t lds0 = lds_addr(smem);
-  // One of the L direct-to-LDS loads of a K step: q < IA are A-tile loads, then IB B-tile
-  // loads, then the A and B scale words. q is a compile-time constant at every call.
-  auto issue_one = [&](int q, int64_t k0, uint32_t st) {
+  // One of the L direct-to-LDS loads of stage ks into the LDS slot of stage kt (ks == kt, or
+  // a surplus load of the last stage into a free slot, which keeps every step's load count
+  // and waits the same): q < IA are A-tile loads, then IB B-tile loads, then the A and B
+  // scale words (of the 128-k block holding the stage). q is a compile-time constant.
+  auto issue_one = [&](int q, int ks, int kt) {
+    const int64_t k0 = (int64_t)ks * T::BK;
+    const uint32_t st = lds0 + (kt % T::S) * T::STAGE;
     if (q < T::IA) {
-      g2lds16(a_s + q * a8 + k0, (q & 1) ? a_v1 : a_v0, st + T::A_OFF + (wid_u * T::IA + q) * 1024);
+      g2lds16(a_s + q * a16 + k0, a_v, st + T::A_OFF + (wid_u * T::IA + q) * 1024);
     } else if (q < T::IA + T::IB) {
       const int i = q - T::IA;
-      g2lds16(b_s + i * b8 + k0, (i & 1) ? b_v1 : b_v0, st + T::B_OFF + (wid_u * T::IB + i) * 1024);
+      g2lds16(b_s + i * b16 + k0, b_v, st + T::B_OFF + (wid_u * T::IB + i) * 1024);
     } else if (q == T::IA + T::IB) {
-      g2lds4(Asg + k0 / 32, sa_v, st + T::SA_OFF + wid_u * 256);
+      g2lds4(Asg + (k0 >> 7) * 4, sa_v, st + T::SA_OFF + wid_u * 256);
     } else {
-      g2lds4(Bsg + k0 / 32, sb_v, st + T::SB_OFF + wid_u * 256);
+      g2lds4(Bsg + (k0 >> 7) * 4, sb_v, st + T::SB_OFF + wid_u * 256);
     }
   };
 
-  if (KT > 0) {
-    // prologue: steps 0 .. S-2 (clamped to the last step; a surplus load fills a stage that
-    // is never read, which keeps every wavefront's load count per step fixed)
-#pragma unroll
-    for (int st = 0; st < T::S - 1; ++st) {
-      const int64_t k0 = (int64_t)(st < KT ? st : KT - 1) * T::BK;
-#pragma unroll
-      for (int q = 0; q < T::L; ++q) issue_one(q, k0, lds0 + st * T::STAGE);
-    }
-  }
-  constexpr int NMF = 2 * T::FM * T::FN;  // MFMAs per K step
-  for (int kt = 0; kt < KT; ++kt) {
-    // this wavefront's loads of step kt are done once at most (S-2) steps' loads remain
-    wait_vmcnt<(T::S - 2) * T::L>();
-    __syncthreads();  // every wavefront's step-kt data is in LDS; step kt-1 fully consumed
+  // Fragments of one stage in registers: A/B operands and this lane's two E8M0 scale bytes
+  // (its 32-k group of the stage: byte 2 * (kt % 2) + g of the row's scale word, read alone so
+  // that the matrix instruction takes it with op_sel 0).
+  v8i fa[2][T::FM], fb[2][T::FN];
+  uint32_t sa[2][T::FM], sb[2][T::FN];
+  // LDS reads of stage kt into register set kt % 2, as a list of NR reads so that they can be
+  // interleaved with the matrix instructions of the previous stage. Read r < 2 FM: A fragment
+  // r / 2, half r % 2 (k bytes [16g, 16g+16) or [32+16g, 32+16g+16)); then 2 FN B reads; then
+  // FM + FN scale bytes.
+  constexpr int NR = 2 * (T::FM + T::FN) + T::FM + T::FN;
+  auto read_one = [&](int r, int kt, auto par) {
+    constexpr int B = decltype(par)::value;  // kt % 2
     const uint8_t* base = smem + (kt % T::S) * T::STAGE;
-    // all fragments and scales of the step are read up front (LDS latency overlaps the MFMAs)
-    uint32_t sa[T::FM], sb[T::FN];
-#pragma unroll
-    for (int i = 0; i < T::FM; ++i)
-      sa[i] = *reinterpret_cast<const uint32_t*>(base + T::SA_OFF + (wm * T::TM + i * 32 + r32) * 4) >> (8 * g);
-#pragma unroll
-    for (int j = 0; j < T::FN; ++j)
-      sb[j] = *reinterpret_cast<const uint32_t*>(base + T::SB_OFF + (wn * T::TN + j * 32 + r32) * 4) >> (8 * g);
-    v8i af[2][T::FM], bf[2][T::FN];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int i = 0; i < T::FM; ++i) {
-        const int row = wm * T::TM + i * 32 + r32;
-        const uint4 lo = *reinterpret_cast<const uint4*>(base + T::A_OFF + swz(row, 4 * h + g));
-        const uint4 hi = *reinterpret_cast<const uint4*>(base + T::A_OFF + swz(row, 4 * h + 2 + g));
-        af[h][i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
-#pragma unroll
-      for (int j = 0; j < T::FN; ++j) {
-        const int row = wn * T::TN + j * 32 + r32;
-        const uint4 lo = *reinterpret_cast<const uint4*>(base + T::B_OFF + swz(row, 4 * h + g));
-        const uint4 hi = *reinterpret_cast<const uint4*>(base + T::B_OFF + swz(row, 4 * h + 2 + g));
-        bf[h][j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
+    if (r < 2 * T::FM) {
+      const int i = r >> 1, hi = r & 1;
+      const uint4 v = *reinterpret_cast<const uint4*>(base + T::A_OFF + swz(tr0 + i * 32 + r32, 2 * hi + g));
+      fa[B][i][4 * hi] = (int)v.x; fa[B][i][4 * hi + 1] = (int)v.y;
+      fa[B][i][4 * hi + 2] = (int)v.z; fa[B][i][4 * hi + 3] = (int)v.w;
+    } else if (r < 2 * (T::FM + T::FN)) {
+      const int j = (r - 2 * T::FM) >> 1, hi = r & 1;
+      const uint4 v = *reinterpret_cast<const uint4*>(base + T::B_OFF + swz(tc0 + j * 32 + r32, 2 * hi + g));
+      fb[B][j][4 * hi] = (int)v.x; fb[B][j][4 * hi + 1] = (int)v.y;
+      fb[B][j][4 * hi + 2] = (int)v.z; fb[B][j][4 * hi + 3] = (int)v.w;
+    } else if (r < 2 * (T::FM + T::FN) + T::FM) {
+      const int i = r - 2 * (T::FM + T::FN);
+      sa[B][i] = base[T::SA_OFF + (tr0 + i * 32 + r32) * 4 + 2 * B + g];
+    } else {
+      const int j = r - 2 * (T::FM + T::FN) - T::FM;
+      sb[B][j] = base[T::SB_OFF + (tc0 + j * 32 + r32) * 4 + 2 * B + g];
     }
-    // MFMAs with the refill of the stage consumed at step kt-1 interleaved one load after each
-    // MFMA, so that a full load queue never holds the wavefront before its matrix work
-    const int nxt = kt + T::S - 1;
-    const int64_t nk0 = (int64_t)(nxt < KT ? nxt : KT - 1) * T::BK;
-    const uint32_t nst = lds0 + (nxt % T::S) * T::STAGE;
+  };
+
+  // Pipeline (S = 4 stages in an LDS ring, register double buffering): at step kt the
+  // wavefront waits until stage kt+1 has landed (the loads of stages kt+2 and kt+3 may remain
+  // in flight) and passes the block barrier, after which stage kt+1 is visible to all and
+  // every wavefront holds stage kt in registers (its LDS reads completed before the barrier),
+  // so stage kt's slot takes the loads of stage kt+4. The MFMAs on stage kt are interleaved
+  // with the LDS reads of stage kt+1 and those loads. Every step but the last two loads a
+  // stage (past the end: a surplus copy of the last stage), so the waits are the same
+  // everywhere; steps are instantiated with compile-time flags so that each interleaved
+  // sequence is one basic block.
+  constexpr int NMF = T::FM * T::FN;  // MFMAs per stage
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  if (KT > 0) {
+#pragma unroll
+    for (int st = 0; st < T::S; ++st) {
+#pragma unroll
+      for (int q = 0; q < T::L; ++q) issue_one(q, st < KT ? st : KT - 1, st);
+    }
+    wait_vmcnt<3 * T::L>();
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < NR; ++r) read_one(r, 0, I0());
+  }
+  // step kt (P = kt % 2); MORE: stage kt+1 exists; LOAD: load stage kt+4 (clamped)
+  auto step = [&](int kt, auto par, auto more, auto load) {
+    constexpr int P = decltype(par)::value;
+    constexpr bool MORE = decltype(more)::value, LOAD = decltype(load)::value;
+    if (MORE) wait_vmcnt<2 * T::L>();
+    __syncthreads();
+    const int ks = kt + 4 < KT ? kt + 4 : KT - 1;
 #pragma unroll
     for (int m = 0; m < NMF; ++m) {
-      const int h = m / (T::FM * T::FN), i = (m / T::FN) % T::FM, j = m % T::FN;
-      if (h == 0)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[0][i], bf[0][j], acc[i][j], 0, 0, 0,
-                                                                    (int)sa[i], 0, (int)sb[j]);
-      else
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[1][i], bf[1][j], acc[i][j], 0, 0, 2,
-                                                                    (int)sa[i], 2, (int)sb[j]);
-      if (m < T::L) issue_one(m, nk0, nst);
+      const int i = m / T::FN, j = m % T::FN;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[P][i], fb[P][j], acc[i][j], 0, 0, 0,
+                                                                  (int)sa[P][i], 0, (int)sb[P][j]);
+      if (MORE) {
+#pragma unroll
+        for (int r = m * NR / NMF; r < (m + 1) * NR / NMF; ++r)
+          read_one(r, kt + 1, std::integral_constant<int, 1 - P>());
+      }
+      if (LOAD && m < T::L) issue_one(m, ks, kt + 4);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (LOAD) {
 #pragma unroll
-    for (int q = NMF; q < T::L; ++q) issue_one(q, nk0, nst);  // loads beyond the MFMA count
+      for (int q = NMF; q < T::L; ++q) issue_one(q, ks, kt + 4);
+    }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  int kt = 0;
+  for (; kt + 2 < KT; kt += 2) {
+    step(kt, I0(), T_(), T_());
+    step(kt + 1, I1(), T_(), T_());
+  }
+  if (KT > 0) {  // the last two stages (KT is even)
+    step(kt, I0(), T_(), F_());
+    step(kt + 1, I1(), F_(), F_());
   }
   if (KT > 0) {
-    wait_vmcnt<0>();  // surplus loads must land before the epilogue reuses LDS
+    wait_vmcnt<0>();  // no load may still target LDS when the epilogue reuses it
   }
 
   // ------------------------------------------------------------------ epilogues
+  // The pipeline LDS is idle after the main loop; every epilogue stages through it so that
+  // global stores are 16-byte, row-contiguous runs (a wavefront store covers whole lines).
   const int64_t wrow0 = m0 + wm * T::TM;  // first output row of this wavefront
   const int64_t wcol0 = n0 + wn * T::TN;  // first output column of this wavefront
+  __syncthreads();  // every wavefront has finished reading the last stage
 
   if (EPI == EPI_STORE || EPI == EPI_UNPACK13) {
+    const int64_t ebase = (SCHED == SCHED_KGROUP) ? (int64_t)e * p.c_es : 0;
+    if (p.out_f32) {
+      // fp32 output (a test/debug option): direct stores from the accumulator layout
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i) {
+        // fragment rows are 32-aligned: a packed W13 row n goes to dW1 (n % 64 < 32) or dW3,
+        // row 32 * (n / 64) + n % 32 of expert e
+        const int64_t fr = wrow0 + i * 32;
+        float* base = (EPI == EPI_STORE)
+                          ? reinterpret_cast<float*>(p.C) + ebase + fr * p.ldc
+                          : reinterpret_cast<float*>((fr & 32) ? p.C2 : p.C) + ebase + (fr >> 6) * 32 * p.ldc;
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 16; ++q)
+            base[(8 * (q >> 2) + 4 * g + (q & 3)) * p.ldc + wcol0 + j * 32 + r32] = acc[i][j][q];
+      }
+      return;
+    }
+    // BF16 tile [BM][BN] in LDS, then 16-byte row-contiguous copies
+    constexpr int CP = BN + 8;
+    uint16_t* cs = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
     for (int i = 0; i < T::FM; ++i)
 #pragma unroll
       for (int j = 0; j < T::FN; ++j)
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int64_t row = wrow0 + i * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
-          const int64_t col = wcol0 + j * 32 + r32;
-          if (EPI == EPI_STORE) {
-            const int64_t base = (SCHED == SCHED_KGROUP) ? (int64_t)e * p.c_es : 0;
-            store_out(p.C, base + row * p.ldc + col, acc[i][j][q], p.out_f32);
-          } else {
-            // row = packed W13 row n -> dW1 / dW3 row 32*(n/64) + n%32 of expert e
-            void* dst = (row & 32) ? p.C2 : p.C;
-            const int64_t frow = (row >> 6) * 32 + (row & 31);
-            store_out(dst, (int64_t)e * p.c_es + frow * p.ldc + col, acc[i][j][q], p.out_f32);
-          }
-        }
+        for (int q = 0; q < 16; ++q)
+          cs[(tr0 + i * 32 + 8 * (q >> 2) + 4 * g + (q & 3)) * CP + tc0 + j * 32 + r32] =
+              (uint16_t)bf16_bits(acc[i][j][q]);
+    __syncthreads();
+    constexpr int CPR = BN / 8;  // 16-byte chunks per row
+    static_assert((BM * CPR) % T::NT == 0, "whole copy rounds");
+#pragma unroll 2
+    for (int it = 0; it < BM * CPR / T::NT; ++it) {
+      const int t = it * T::NT + tid;
+      const int r = t / CPR, c = t % CPR;
+      const uint4 v = *reinterpret_cast<const uint4*>(cs + r * CP + c * 8);
+      const int64_t row = m0 + r, col = n0 + c * 8;
+      uint16_t* dst;
+      if (EPI == EPI_STORE) {
+        dst = reinterpret_cast<uint16_t*>(p.C) + ebase + row * p.ldc + col;
+      } else {
+        dst = reinterpret_cast<uint16_t*>((row & 32) ? p.C2 : p.C) + ebase +
+              ((row >> 6) * 32 + (row & 31)) * p.ldc + col;
+      }
+      *reinterpret_cast<uint4*>(dst) = v;
+    }
     return;
   }
 
   if (EPI == EPI_SWIGLU) {
-    // N = 2F (packed gate/up columns): fragment pair (2c, 2c+1) of a wavefront holds gate and
-    // up columns of the same 32 h columns. g, u are rounded to BF16 (saved for backward),
-    // h = BF16(silu(g) * u) is staged in LDS (64 rows at a time) and quantized along rows
-    // (32-column groups) and along columns (32-row groups).
+    // N = 2F (packed gate/up columns): fragment pair (2c, 2c+1) of a wavefront holds the gate
+    // and up columns of the same 32 h columns, in the same accumulator slots. Per pair:
+    //  * g, u are rounded to BF16 and saved (for the backward pass) as one 4 KB record in
+    //    accumulator order: two 2 KB coalesced stores, no staging;
+    //  * h = BF16(silu(g) * u); its column-wise groups (32 rows of one column: this lane's 16
+    //    slots plus lane l^32's) are quantized in registers and the codes staged, transposed,
+    //    in LDS; h itself is staged row-major for the row-wise groups.
+    // Then the whole block quantizes the row-wise groups and copies the column codes out.
     static_assert(T::FN % 2 == 0, "SwiGLU epilogue needs whole gate/up column pairs");
-    constexpr int HC = T::TN / 2;                 // h columns per wavefront
-    constexpr int HP = HC + 8;                    // LDS pitch (bf16 elements)
-    constexpr int RC = T::TM < T::EPI_ROWS ? T::TM : T::EPI_ROWS;  // rows per chunk
-    constexpr int FC = RC / 32;                   // fragments per chunk
-    const int64_t ldn = p.N;                      // 2F
+    constexpr int HCB = BN / 2;   // h columns of the block
+    constexpr int HP = HCB + 8;   // row-major h tile pitch (bf16)
+    constexpr int QP = BM + 8;    // transposed code tile pitch (bytes)
+    constexpr int SG = BM / 32;   // column-wise groups per column in the block
     const int64_t F = p.N / 2;
-    const int64_t hcol0 = wcol0 / 2;
-    uint16_t* hs = reinterpret_cast<uint16_t*>(smem) + wid * (RC * HP);
+    const int64_t hc0 = n0 / 2;
+    uint16_t* hR = reinterpret_cast<uint16_t*>(smem);
+    uint8_t* qT = smem + BM * HP * 2;
+    uint8_t* sT = qT + HCB * QP;
+    if (p.dbg) {
 #pragma unroll
-    for (int ic = 0; ic < T::FM; ic += FC) {
-      __syncthreads();  // LDS free (main loop or previous chunk)
+      for (int i = 0; i < T::FM; ++i)
 #pragma unroll
-      for (int ii = 0; ii < FC; ++ii)
+        for (int j = 0; j < T::FN; ++j)
 #pragma unroll
-        for (int jp = 0; jp < T::FN / 2; ++jp)
+          for (int q = 0; q < 16; ++q)
+            p.dbg[(wrow0 + i * 32 + 8 * (q >> 2) + 4 * g + (q & 3)) * p.N + wcol0 + j * 32 + r32] = acc[i][j][q];
+    }
 #pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int i = ic + ii;
-            const int rl = ii * 32 + 8 * (q >> 2) + 4 * g + (q & 3);  // row within the chunk
-            const int64_t row = wrow0 + i * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
-            const int64_t cg = wcol0 + (2 * jp) * 32 + r32;  // gate column (packed)
-            const float gv = acc[i][2 * jp][q];
-            const float uv = acc[i][2 * jp + 1][q];
-            const uint32_t gb = bf16_bits(gv), ub = bf16_bits(uv);
-            p.h13[row * ldn + cg] = (uint16_t)gb;
-            p.h13[row * ldn + cg + 32] = (uint16_t)ub;
-            if (p.dbg) {
-              p.dbg[row * ldn + cg] = gv;
-              p.dbg[row * ldn + cg + 32] = uv;
-            }
-            const float gf = bf16_to_f32(gb), uf = bf16_to_f32(ub);
-            const float h = gf * sigmoid_f(gf) * uf;
-            hs[rl * HP + jp * 32 + r32] = (uint16_t)bf16_bits(h);
+    for (int i = 0; i < T::FM; ++i) {
+#pragma unroll
+      for (int jp = 0; jp < T::FN / 2; ++jp) {
+        const int hcl = tc0 / 2 + jp * 32 + r32;  // h column within the block
+        uint32_t gw[8], uw[8], hw[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          uint32_t gb[2], ub[2], hb[2];
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const int q = 2 * t + s;
+            const float gv = acc[i][2 * jp][q], uv = acc[i][2 * jp + 1][q];
+            gb[s] = bf16_bits(gv);
+            ub[s] = bf16_bits(uv);
+            const float gf = bf16_to_f32(gb[s]), uf = bf16_to_f32(ub[s]);
+            hb[s] = bf16_bits(gf * sigmoid_f(gf) * uf);
           }
-      __syncthreads();
-      const int64_t crow0 = wrow0 + ic * 32;  // first output row of the chunk
-      for (int q = lane; q < RC * (HC / 32); q += 64) {
-        const int rl = q / (HC / 32), gi = q % (HC / 32);
-        uint32_t v[16], cd[8];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint4 x = *reinterpret_cast<const uint4*>(hs + rl * HP + gi * 32 + t * 8);
-          v[4 * t] = x.x; v[4 * t + 1] = x.y; v[4 * t + 2] = x.z; v[4 * t + 3] = x.w;
+          gw[t] = gb[0] | (gb[1] << 16);
+          uw[t] = ub[0] | (ub[1] << 16);
+          hw[t] = hb[0] | (hb[1] << 16);
         }
-        const uint32_t byte = quant32(v, cd);
-        const int64_t row = crow0 + rl;
-        uint8_t* dst = p.q_r + row * F + hcol0 + gi * 32;
-        *reinterpret_cast<uint4*>(dst) = make_uint4(cd[0], cd[1], cd[2], cd[3]);
-        *reinterpret_cast<uint4*>(dst + 16) = make_uint4(cd[4], cd[5], cd[6], cd[7]);
-        p.s_r[row * (F / 32) + (hcol0 >> 5) + gi] = (uint8_t)byte;
-      }
-      for (int q = lane; q < HC * FC; q += 64) {
-        const int cl = q % HC, rg = q / HC;
-        uint32_t v[16], cd[8];
+        const int64_t rec = ((wrow0 + i * 32) >> 5) * (F >> 5) + ((hc0 + tc0 / 2 + jp * 32) >> 5);
+        uint4* dg = reinterpret_cast<uint4*>(p.h13 + rec * 2048) + 2 * lane;
+        dg[0] = make_uint4(gw[0], gw[1], gw[2], gw[3]);
+        dg[1] = make_uint4(gw[4], gw[5], gw[6], gw[7]);
+        dg[128] = make_uint4(uw[0], uw[1], uw[2], uw[3]);
+        dg[129] = make_uint4(uw[4], uw[5], uw[6], uw[7]);
+        uint32_t am = amax16(hw);
+        am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+        const Scale s = scale_from_amax(am);
+        const int rl = tr0 + i * 32 + 4 * g;
 #pragma unroll
-        for (int t = 0; t < 16; ++t)
-          v[t] = (uint32_t)hs[(rg * 32 + 2 * t) * HP + cl] | ((uint32_t)hs[(rg * 32 + 2 * t + 1) * HP + cl] << 16);
-        const uint32_t byte = quant32(v, cd);
-        const int64_t hc = hcol0 + cl;
-        uint8_t* dst = p.q_c + hc * p.mcap + crow0 + rg * 32;
-        *reinterpret_cast<uint4*>(dst) = make_uint4(cd[0], cd[1], cd[2], cd[3]);
-        *reinterpret_cast<uint4*>(dst + 16) = make_uint4(cd[4], cd[5], cd[6], cd[7]);
-        p.s_c[hc * (p.mcap / 32) + (crow0 >> 5) + rg] = (uint8_t)byte;
+        for (int k = 0; k < 4; ++k)
+          *reinterpret_cast<uint32_t*>(qT + hcl * QP + rl + 8 * k) = cvt4(hw[2 * k], hw[2 * k + 1], s);
+        if (g == 0) sT[hcl * SG + (tr0 >> 5) + i] = (uint8_t)s.byte;
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          hR[(rl + 8 * (q >> 2) + (q & 3)) * HP + hcl] = (uint16_t)(hw[q >> 1] >> (16 * (q & 1)));
       }
+    }
+    __syncthreads();
+    // row-wise groups: one task = 16 columns of a row; lanes 2c and 2c+1 hold one group
+    constexpr int CPR = HCB / 16;
+    static_assert((BM * CPR) % T::NT == 0 && CPR % 2 == 0, "whole row-pass rounds");
+#pragma unroll 2
+    for (int it = 0; it < BM * CPR / T::NT; ++it) {
+      const int t = it * T::NT + tid;
+      const int r = t / CPR, c = t % CPR;
+      const uint4 a = *reinterpret_cast<const uint4*>(hR + r * HP + c * 16);
+      const uint4 b = *reinterpret_cast<const uint4*>(hR + r * HP + c * 16 + 8);
+      const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      uint32_t am = amax16(v);
+      am = max(am, dpp_xor1(am));
+      const Scale s = scale_from_amax(am);
+      const int64_t row = m0 + r;
+      *reinterpret_cast<uint4*>(p.q_r + row * F + hc0 + c * 16) =
+          make_uint4(cvt4(v[0], v[1], s), cvt4(v[2], v[3], s), cvt4(v[4], v[5], s), cvt4(v[6], v[7], s));
+      if (!(c & 1)) p.s_r[row * (F >> 5) + ((hc0 + c * 16) >> 5)] = (uint8_t)s.byte;
+    }
+    // column-wise codes: a column's BM codes are contiguous in hq_c
+    constexpr int CPC = BM / 16;
+    static_assert((HCB * CPC) % T::NT == 0, "whole column-copy rounds");
+#pragma unroll 2
+    for (int it = 0; it < HCB * CPC / T::NT; ++it) {
+      const int t = it * T::NT + tid;
+      const int hc = t / CPC, c = t % CPC;
+      const uint2 a = *reinterpret_cast<const uint2*>(qT + hc * QP + c * 16);
+      const uint2 b = *reinterpret_cast<const uint2*>(qT + hc * QP + c * 16 + 8);
+      *reinterpret_cast<uint4*>(p.q_c + (hc0 + hc) * p.mcap + m0 + c * 16) = make_uint4(a.x, a.y, b.x, b.y);
+    }
+    for (int t = tid; t < HCB; t += T::NT) {
+      uint8_t* dst = p.s_c + (hc0 + t) * (p.mcap >> 5) + (m0 >> 5);
+      if (SG == 8) *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(sT + t * SG);
+      else *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(sT + t * SG);
     }
     return;
   }
 
   if (EPI == EPI_DSWIGLU) {
-    // N = F: acc = dh. Per 64-row chunk of the wavefront tile:
-    //  1. dh -> BF16 into an LDS tile [64, TN];
-    //  2. row pass, one (row, 32-column group) per lane task: 16-byte loads of the saved BF16
-    //     g and u (contiguous in the packed h13), dG = dh u s (1 + g (1 - s)), dU = dh g s with
-    //     s = sigmoid(g), each -> BF16; both row-wise groups quantized and stored; dG, dU
-    //     written into a packed LDS tile [64, 2TN] (gate group then up group per 32 columns);
-    //  3. column pass over the packed tile: column-wise groups quantized and stored.
-    constexpr int DP = T::TN + 8;   // dh tile pitch (bf16 elements)
-    constexpr int PC = 2 * T::TN;   // packed columns per wavefront
-    constexpr int HP = PC + 8;
-    constexpr int RC = T::TM < T::EPI_ROWS ? T::TM : T::EPI_ROWS;
-    constexpr int FC = RC / 32;
+    // N = F: acc = dh. The saved g, u of every fragment are loaded first (4 KB records in
+    // accumulator order, so each lane's slots arrive in its own registers). Then, one wavefront
+    // row (TM rows) at a time: dG = dh u s (1 + g (1 - s)), dU = dh g s with s = sigmoid(g),
+    // each rounded to BF16; their column-wise groups are quantized in registers (codes staged
+    // transposed in LDS), the BF16 values staged row-major in the packed order (gate group,
+    // then up group, per 32 columns); the block then quantizes the row-wise groups and copies
+    // the column codes out.
+    constexpr int PCB = 2 * BN;       // packed columns of the block
+    constexpr int DP = PCB + 8;       // row-major tile pitch (bf16)
+    constexpr int QP = T::TM + 8;     // transposed code tile pitch (bytes)
+    constexpr int SG = T::TM / 32;
     const int64_t F = p.N;
     const int64_t ld13 = 2 * F;
-    const int64_t pcol0 = 2 * wcol0;
-    uint16_t* dhs = reinterpret_cast<uint16_t*>(smem) + wid * (RC * (DP + HP));
-    uint16_t* hs = dhs + RC * DP;
+    const int64_t pc0 = 2 * n0;
+    uint16_t* dR = reinterpret_cast<uint16_t*>(smem);
+    uint8_t* qT = smem + T::TM * DP * 2;
+    uint8_t* sT = qT + PCB * QP;
+    // g, u of one fragment row (FN fragments) in flight while the previous one is processed
+    uint4 gs[2][T::FN][2], us[2][T::FN][2];
+    auto load_gu = [&](int i, int buf) {
 #pragma unroll
-    for (int ic = 0; ic < T::FM; ic += FC) {
-      __syncthreads();
+      for (int j = 0; j < T::FN; ++j) {
+        const int64_t rec = ((wrow0 + i * 32) >> 5) * (F >> 5) + ((wcol0 + j * 32) >> 5);
+        const uint4* src = reinterpret_cast<const uint4*>(p.h13 + rec * 2048) + 2 * lane;
+        gs[buf][j][0] = src[0];
+        gs[buf][j][1] = src[1];
+        us[buf][j][0] = src[128];
+        us[buf][j][1] = src[129];
+      }
+    };
+    load_gu(0, 0);
+    if (p.dbg) {
 #pragma unroll
-      for (int ii = 0; ii < FC; ++ii)
+      for (int i = 0; i < T::FM; ++i)
 #pragma unroll
         for (int j = 0; j < T::FN; ++j)
 #pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int i = ic + ii;
-            const int rl = ii * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
-            const float dv = acc[i][j][q];
-            if (p.dbg) p.dbg[(wrow0 + ic * 32 + rl) * F + wcol0 + j * 32 + r32] = dv;
-            dhs[rl * DP + j * 32 + r32] = (uint16_t)bf16_bits(dv);
+          for (int q = 0; q < 16; ++q)
+            p.dbg[(wrow0 + i * 32 + 8 * (q >> 2) + 4 * g + (q & 3)) * F + wcol0 + j * 32 + r32] = acc[i][j][q];
+    }
+#pragma unroll 1
+    for (int hh = 0; hh < WM; ++hh) {
+      if (wm == hh) {
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i) {
+          if (i + 1 < T::FM) load_gu(i + 1, (i + 1) & 1);
+#pragma unroll
+          for (int j = 0; j < T::FN; ++j) {
+            const int b = i & 1;
+            const uint32_t gw[8] = {gs[b][j][0].x, gs[b][j][0].y, gs[b][j][0].z, gs[b][j][0].w,
+                                    gs[b][j][1].x, gs[b][j][1].y, gs[b][j][1].z, gs[b][j][1].w};
+            const uint32_t uw[8] = {us[b][j][0].x, us[b][j][0].y, us[b][j][0].z, us[b][j][0].w,
+                                    us[b][j][1].x, us[b][j][1].y, us[b][j][1].z, us[b][j][1].w};
+            uint32_t dgw[8], duw[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+              uint32_t og = 0, ou = 0;
+#pragma unroll
+              for (int s = 0; s < 2; ++s) {
+                const int q = 2 * t + s;
+                const float dv = acc[i][j][q];
+                const float dh = bf16_to_f32(bf16_bits(dv));
+                const float gf = bf16_to_f32((gw[t] >> (16 * s)) & 0xFFFFu);
+                const float uf = bf16_to_f32((uw[t] >> (16 * s)) & 0xFFFFu);
+                const float sg = sigmoid_f(gf);
+                og |= bf16_bits(dh * uf * sg * (1.0f + gf * (1.0f - sg))) << (16 * s);
+                ou |= bf16_bits(dh * gf * sg) << (16 * s);
+              }
+              dgw[t] = og;
+              duw[t] = ou;
+            }
+            const int pcg = 2 * (tc0 + j * 32) + r32;  // packed column of dG (dU: + 32)
+            const int rl = i * 32 + 4 * g;
+#pragma unroll
+            for (int part = 0; part < 2; ++part) {
+              const uint32_t* w = part ? duw : dgw;
+              const int pcl = pcg + 32 * part;
+              uint32_t am = amax16(w);
+              am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+              const Scale s = scale_from_amax(am);
+#pragma unroll
+              for (int k = 0; k < 4; ++k)
+                *reinterpret_cast<uint32_t*>(qT + pcl * QP + rl + 8 * k) = cvt4(w[2 * k], w[2 * k + 1], s);
+              if (g == 0) sT[pcl * SG + i] = (uint8_t)s.byte;
+#pragma unroll
+              for (int q = 0; q < 16; ++q)
+                dR[(rl + 8 * (q >> 2) + (q & 3)) * DP + pcl] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
+            }
           }
-      __syncthreads();
-      const int64_t crow0 = wrow0 + ic * 32;
-      for (int q = lane; q < RC * (T::TN / 32); q += 64) {
-        const int rl = q / (T::TN / 32), gi = q % (T::TN / 32);
-        const int64_t row = crow0 + rl;
-        const uint16_t* gsrc = p.h13 + row * ld13 + pcol0 + gi * 64;  // g group, then u group
-        uint32_t gv[16], uv[16], dgv[16], duv[16], cd[8];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint4 a = *reinterpret_cast<const uint4*>(gsrc + t * 8);
-          const uint4 b = *reinterpret_cast<const uint4*>(gsrc + 32 + t * 8);
-          gv[4 * t] = a.x; gv[4 * t + 1] = a.y; gv[4 * t + 2] = a.z; gv[4 * t + 3] = a.w;
-          uv[4 * t] = b.x; uv[4 * t + 1] = b.y; uv[4 * t + 2] = b.z; uv[4 * t + 3] = b.w;
-        }
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const uint32_t d2 = *reinterpret_cast<const uint32_t*>(dhs + rl * DP + gi * 32 + 2 * t);
-          uint32_t og = 0, ou = 0;
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const float dh = bf16_to_f32((d2 >> (16 * h)) & 0xFFFFu);
-            const float gf = bf16_to_f32((gv[t] >> (16 * h)) & 0xFFFFu);
-            const float uf = bf16_to_f32((uv[t] >> (16 * h)) & 0xFFFFu);
-            const float sg = sigmoid_f(gf);
-            og |= bf16_bits(dh * uf * sg * (1.0f + gf * (1.0f - sg))) << (16 * h);
-            ou |= bf16_bits(dh * gf * sg) << (16 * h);
-          }
-          dgv[t] = og;
-          duv[t] = ou;
-        }
-        uint8_t* dst = p.q_r + row * ld13 + pcol0 + gi * 64;
-        uint32_t byte = quant32(dgv, cd);
-        *reinterpret_cast<uint4*>(dst) = make_uint4(cd[0], cd[1], cd[2], cd[3]);
-        *reinterpret_cast<uint4*>(dst + 16) = make_uint4(cd[4], cd[5], cd[6], cd[7]);
-        p.s_r[row * (ld13 / 32) + (pcol0 >> 5) + 2 * gi] = (uint8_t)byte;
-        byte = quant32(duv, cd);
-        *reinterpret_cast<uint4*>(dst + 32) = make_uint4(cd[0], cd[1], cd[2], cd[3]);
-        *reinterpret_cast<uint4*>(dst + 48) = make_uint4(cd[4], cd[5], cd[6], cd[7]);
-        p.s_r[row * (ld13 / 32) + (pcol0 >> 5) + 2 * gi + 1] = (uint8_t)byte;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          *reinterpret_cast<uint4*>(hs + rl * HP + gi * 64 + t * 8) =
-              make_uint4(dgv[4 * t], dgv[4 * t + 1], dgv[4 * t + 2], dgv[4 * t + 3]);
-          *reinterpret_cast<uint4*>(hs + rl * HP + gi * 64 + 32 + t * 8) =
-              make_uint4(duv[4 * t], duv[4 * t + 1], duv[4 * t + 2], duv[4 * t + 3]);
         }
       }
       __syncthreads();
-      for (int q = lane; q < PC * FC; q += 64) {
-        const int cl = q % PC, rg = q / PC;
-        uint32_t v[16], cd[8];
-#pragma unroll
-        for (int t = 0; t < 16; ++t)
-          v[t] = (uint32_t)hs[(rg * 32 + 2 * t) * HP + cl] | ((uint32_t)hs[(rg * 32 + 2 * t + 1) * HP + cl] << 16);
-        const uint32_t byte = quant32(v, cd);
-        const int64_t pcg = pcol0 + cl;
-        uint8_t* dst = p.q_c + pcg * p.mcap + crow0 + rg * 32;
-        *reinterpret_cast<uint4*>(dst) = make_uint4(cd[0], cd[1], cd[2], cd[3]);
-        *reinterpret_cast<uint4*>(dst + 16) = make_uint4(cd[4], cd[5], cd[6], cd[7]);
-        p.s_c[pcg * (p.mcap / 32) + (crow0 >> 5) + rg] = (uint8_t)byte;
+      const int64_t rbase = m0 + hh * T::TM;
+      constexpr int CPR = PCB / 16;
+      static_assert((T::TM * CPR) % T::NT == 0 && CPR % 2 == 0, "whole row-pass rounds");
+#pragma unroll 2
+      for (int it = 0; it < T::TM * CPR / T::NT; ++it) {
+        const int t = it * T::NT + tid;
+        const int r = t / CPR, c = t % CPR;
+        const uint4 a = *reinterpret_cast<const uint4*>(dR + r * DP + c * 16);
+        const uint4 b = *reinterpret_cast<const uint4*>(dR + r * DP + c * 16 + 8);
+        const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        uint32_t am = amax16(v);
+        am = max(am, dpp_xor1(am));
+        const Scale s = scale_from_amax(am);
+        const int64_t row = rbase + r;
+        *reinterpret_cast<uint4*>(p.q_r + row * ld13 + pc0 + c * 16) =
+            make_uint4(cvt4(v[0], v[1], s), cvt4(v[2], v[3], s), cvt4(v[4], v[5], s), cvt4(v[6], v[7], s));
+        if (!(c & 1)) p.s_r[row * (ld13 >> 5) + ((pc0 + c * 16) >> 5)] = (uint8_t)s.byte;
       }
+      constexpr int CPC = T::TM / 16;
+      static_assert((PCB * CPC) % T::NT == 0, "whole column-copy rounds");
+#pragma unroll 2
+      for (int it = 0; it < PCB * CPC / T::NT; ++it) {
+        const int t = it * T::NT + tid;
+        const int pc = t / CPC, c = t % CPC;
+        const uint2 a = *reinterpret_cast<const uint2*>(qT + pc * QP + c * 16);
+        const uint2 b = *reinterpret_cast<const uint2*>(qT + pc * QP + c * 16 + 8);
+        *reinterpret_cast<uint4*>(p.q_c + (pc0 + pc) * p.mcap + rbase + c * 16) = make_uint4(a.x, a.y, b.x, b.y);
+      }
+      for (int t = tid; t < PCB; t += T::NT) {
+        uint8_t* dst = p.s_c + (pc0 + t) * (p.mcap >> 5) + (rbase >> 5);
+        if (SG == 4) *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(sT + t * SG);
+        else *reinterpret_cast<uint16_t*>(dst) = *reinterpret_cast<const uint16_t*>(sT + t * SG);
+      }
+      __syncthreads();  // the staging tiles are rewritten for the next wavefront row
     }
     return;
   }
@@ -531,6 +668,8 @@ static hipError_t launch_cfg(const GemmParams& p, hipStream_t st) {
 
 template <int SCHED, int EPI>
 static hipError_t launch(const GemmParams& p, bool big_m, hipStream_t st) {
+  if constexpr (EPI != EPI_DSWIGLU)
+    if (big_m && p.N % 256 == 0) return launch_cfg<256, 256, SCHED, EPI>(p, st);
   if (big_m) return launch_cfg<256, 128, SCHED, EPI>(p, st);
   return launch_cfg<128, 128, SCHED, EPI>(p, st);
 }
@@ -541,7 +680,7 @@ static hipError_t launch(const GemmParams& p, bool big_m, hipStream_t st) {
 // epi: 0 store (C, ldc, out_f32), 1 SwiGLU + dual quant, 2 dSwiGLU + dual quant.
 hipError_t mxf_launch_gemm_mgroup(int epi, const mxf::GemmParams& p, hipStream_t st) {
   using namespace mxf;
-  if (p.mcap % 128 || p.N % 128 || p.K % 128) return hipErrorInvalidValue;
+  if (p.mcap % 128 || p.N % 128 || p.K % 128 || p.ldc % 8) return hipErrorInvalidValue;
   const bool big = (p.pad % 256 == 0) && (p.mcap % 256 == 0);
   switch (epi) {
     case EPI_STORE: return launch<SCHED_MGROUP, EPI_STORE>(p, big, st);
@@ -555,7 +694,7 @@ hipError_t mxf_launch_gemm_mgroup(int epi, const mxf::GemmParams& p, hipStream_t
 // epi: 0 store into C + e * c_es, 3 store with the W13 row unpack into C (dW1) / C2 (dW3).
 hipError_t mxf_launch_gemm_kgroup(int epi, const mxf::GemmParams& p, hipStream_t st) {
   using namespace mxf;
-  if (p.M % 128 || p.N % 128) return hipErrorInvalidValue;
+  if (p.M % 128 || p.N % 128 || p.ldc % 8) return hipErrorInvalidValue;
   const bool big = (p.M % 256 == 0);
   switch (epi) {
     case EPI_STORE: return launch<SCHED_KGROUP, EPI_STORE>(p, big, st);

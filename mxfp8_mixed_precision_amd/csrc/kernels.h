@@ -22,7 +22,7 @@ struct GemmParams {
   void* C2;          // UNPACK13: dW3
   int64_t ldc, c_es;
   int out_f32;
-  uint16_t* h13;     // SWIGLU: written [mcap, 2F]; DSWIGLU: read [mcap, 2F]
+  uint16_t* h13;     // SWIGLU: written, DSWIGLU: read; fragment-tiled (4 KB per 32x32 h block)
   uint8_t* q_r;      // SWIGLU: hq_r [mcap, F];  DSWIGLU: dhq_r [mcap, 2F]
   uint8_t* s_r;
   uint8_t* q_c;      // SWIGLU: hq_c [F, mcap];  DSWIGLU: dhq_c [2F, mcap]

@@ -101,6 +101,22 @@ __device__ __forceinline__ uint32_t quant32(const uint32_t* v, uint32_t* codes) 
   return s.byte;
 }
 
+// Value held by lane l ^ 1 (DPP quad permute [1,0,3,2]) and by lane l ^ 2 ([2,3,0,1]).
+__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+}
+
+// Amax magnitude bits of 16 BF16 values held in 8 packed words.
+__device__ __forceinline__ uint32_t amax16(const uint32_t* v) {
+  uint32_t m = mag2(v[0]);
+#pragma unroll
+  for (int i = 1; i < 8; ++i) m = pk_max_u16(m, mag2(v[i]));
+  return max(m & 0xFFFFu, m >> 16);
+}
+
 // Pack the low (or high) BF16 halves of two words: (a.lo, b.lo) or (a.hi, b.hi).
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x05040100u);
@@ -115,10 +131,12 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
 }
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// sigmoid(g) without overflow for either sign.
+// sigmoid(g) without overflow for either sign: with e = exp(-|g|), 1 / (1 + e) for g >= 0 and
+// e / (1 + e) otherwise. Built from the hardware base-2 exponential and reciprocal (each
+// within about 1 ulp): the result is rounded to BF16 by every caller.
 __device__ __forceinline__ float sigmoid_f(float g) {
-  const float e = expf(-fabsf(g));
-  const float r = 1.0f / (1.0f + e);
+  const float e = __builtin_amdgcn_exp2f(-fabsf(g) * 1.44269504088896340736f);
+  const float r = __builtin_amdgcn_rcpf(1.0f + e);
   return g >= 0.0f ? r : e * r;
 }
 

@@ -41,12 +41,6 @@ struct QuantParams {
   int32_t* status;                      // QK_MASKED: device status word (block 0 writes it)
 };
 
-__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
-}
-__device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
-}
 
 template <int KIND, bool ROW, bool COL>
 __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {

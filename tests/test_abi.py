@@ -137,3 +137,26 @@ def test_valid_call_without_gpu_fails_cleanly():
     with pytest.raises(mx.MxfError) as ei:
         mx.mxfp8_quantize(good, 64, 64, mx.ROW, good, good, None, None, stream=0)
     assert ei.value.status in (_abi.E_HIP, _abi.E_DEVICE)
+
+
+def test_h13_untile_matches_documented_order():
+    """The binding's row-major copy of the tiled h13 follows the element formula stated for
+    MXF_T_H13 in include/mxfp8.h (checked index by index on a small case)."""
+    import torch
+    import mxfp8_mixed_precision_amd as mx
+    M, F = 64, 96
+    tiled = torch.empty(M * 2 * F, dtype=torch.int64)
+    for R in range(M // 32):
+        for J in range(F // 32):
+            base = (R * (F // 32) + J) * 2048
+            for s in range(2):
+                for b in range(2):
+                    for c in range(32):
+                        for k in range(4):
+                            for j in range(4):
+                                row = 32 * R + 8 * k + 4 * b + j
+                                col = 64 * J + 32 * s + c
+                                tiled[base + (s * 64 + c + 32 * b) * 16 + 4 * k + j] = row * 100000 + col
+    rm = mx.h13_rowmajor(tiled, F)
+    want = torch.arange(M)[:, None] * 100000 + torch.arange(2 * F)[None, :]
+    assert torch.equal(rm, want)
