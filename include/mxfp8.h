@@ -118,7 +118,13 @@ typedef struct {
  * of 2048 BF16 values, record R * (F/32) + J holding rows 32R .. 32R+31 and h columns
  * 32J .. 32J+31; inside a record, index ((s * 64) + c + 32 b) * 16 + 4 k + j (s = 0 gate,
  * 1 up; b < 2, c < 32, k < 4, j < 4) holds row 32R + 8k + 4b + j, column 32J + c of the
- * gate (s = 0) or up (s = 1) projection. Same size as [Mcap, 2F]. */
+ * gate (s = 0) or up (s = 1) projection. Same size as [Mcap, 2F].
+ *
+ * Every scale tensor below (…S_R, …S_C) holds the E8M0 bytes of a code tensor with R rows
+ * and K columns (the shapes listed are [R, K/32], per expert for the weights) in 128-k
+ * planes, the order the GEMM loads them in: the byte of (row r, 32-group g) is at
+ * (g / 4) * 4R + 4r + g % 4, so the four scale bytes of a row for one 128-wide block of K
+ * are a word and the words of consecutive rows are adjacent. Same size as [R, K/32]. */
 typedef enum {
   MXF_T_STATUS = 0,                                       /* int32 status word (workspace) */
   MXF_T_XQ_R, MXF_T_XS_R,                                 /* [Mcap, D], [Mcap, D/32]       (ws)    */

@@ -31,6 +31,19 @@ _SHAPES = {
 }
 
 
+_PLANE_SCALES = ("XS_R", "XS_C", "W13S_R", "W13S_C", "W2S_R", "W2S_C", "HS_R", "HS_C", "DYS_R", "DYS_C",
+                 "DHS_R", "DHS_C")
+
+
+def scales_rowmajor(planes, shape):
+    """Row-major copy [..., R, G] of a scale tensor stored in 128-k planes [..., G/4, R, 4]
+    (byte of row r, group g at (g / 4) * 4R + 4r + g % 4; leading dims are experts)."""
+    *lead, R, G = shape
+    t = planes.reshape(*lead, G // 4, R, 4)
+    n = len(lead)
+    return t.permute(*range(n), n + 1, n, n + 2).reshape(*lead, R, G)
+
+
 def h13_rowmajor(tiled, F):
     """Row-major [M, 2F] copy of the fragment-tiled saved h13 (BF16, flat or any shape).
 
@@ -65,14 +78,16 @@ class MlpContext:
         return buf[off:off + nbytes]
 
     def view(self, name):
-        """A typed view of documented tensor `name` inside saved / workspace. H13, which the
-        library stores fragment-tiled (include/mxfp8.h), is returned as a row-major
-        [m_capacity, 2F] BF16 copy."""
+        """A typed view of documented tensor `name` inside saved / workspace. H13 (stored
+        fragment-tiled) and the scale tensors (stored in 128-k planes; include/mxfp8.h) are
+        returned as row-major copies: [m_capacity, 2F] BF16 and [..., R, K/32] bytes."""
         import torch
         raw = self.view_raw(name)
         shape = _SHAPES[name](self.E, self.D, self.F, self.m_capacity)
         if name == "H13":
             return h13_rowmajor(raw.view(torch.bfloat16), self.F)
+        if name in _PLANE_SCALES:
+            return scales_rowmajor(raw, shape)
         if name in ("H13_F32", "DH_F32"):
             return raw.view(torch.float32).view(shape)
         if name == "STATUS":

@@ -295,17 +295,19 @@ mxf_status grouped_mlp_fwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   p.mcap = M;
   p.M = M;
   // FC1 + SwiGLU + dual quantization of h
-  p.A = T(MXF_T_XQ_R); p.As = T(MXF_T_XS_R); p.lda = D; p.ldas = D / 32;
-  p.B = T(MXF_T_W13Q_R); p.Bs = T(MXF_T_W13S_R); p.ldb = D; p.ldbs = D / 32;
+  // every scale tensor is in 128-k planes: row stride 4, plane stride 4 x rows
+  p.A = T(MXF_T_XQ_R); p.As = T(MXF_T_XS_R); p.lda = D; p.ldas = 4; p.kbsa = 4 * M;
+  p.B = T(MXF_T_W13Q_R); p.Bs = T(MXF_T_W13S_R); p.ldb = D; p.ldbs = 4; p.kbsb = 4 * 2 * F;
   p.b_es = 2 * F * D; p.bs_es = 2 * F * D / 32;
   p.N = 2 * F; p.K = D;
   p.h13 = (uint16_t*)T(MXF_T_H13);
   p.q_r = T(MXF_T_HQ_R); p.s_r = T(MXF_T_HS_R); p.q_c = T(MXF_T_HQ_C); p.s_c = T(MXF_T_HS_C);
+  p.sr_rs = 4; p.sr_kbs = 4 * M; p.sc_rs = 4; p.sc_kbs = 4 * F;
   p.dbg = dbg ? (float*)T(MXF_T_H13_F32) : nullptr;
   MXF_HIP(timed("fc1_swiglu", st, [&] { return mxf_launch_gemm_mgroup(1, p, st); }), "FC1 launch");
   // FC2
-  p.A = T(MXF_T_HQ_R); p.As = T(MXF_T_HS_R); p.lda = F; p.ldas = F / 32;
-  p.B = T(MXF_T_W2Q_R); p.Bs = T(MXF_T_W2S_R); p.ldb = F; p.ldbs = F / 32;
+  p.A = T(MXF_T_HQ_R); p.As = T(MXF_T_HS_R); p.lda = F; p.ldas = 4; p.kbsa = 4 * M;
+  p.B = T(MXF_T_W2Q_R); p.Bs = T(MXF_T_W2S_R); p.ldb = F; p.ldbs = 4; p.kbsb = 4 * D;
   p.b_es = D * F; p.bs_es = D * F / 32;
   p.N = D; p.K = F;
   p.C = y; p.ldc = D; p.out_f32 = (desc->flags & MXF_OUT_F32) ? 1 : 0;
@@ -349,33 +351,35 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   p.mcap = M;
   // FC2 dgrad + dSwiGLU + dual quantization of dH13
   p.M = M;
-  p.A = T(MXF_T_DYQ_R); p.As = T(MXF_T_DYS_R); p.lda = D; p.ldas = D / 32;
-  p.B = T(MXF_T_W2Q_C); p.Bs = T(MXF_T_W2S_C); p.ldb = D; p.ldbs = D / 32;
+  // every scale tensor is in 128-k planes: row stride 4, plane stride 4 x rows
+  p.A = T(MXF_T_DYQ_R); p.As = T(MXF_T_DYS_R); p.lda = D; p.ldas = 4; p.kbsa = 4 * M;
+  p.B = T(MXF_T_W2Q_C); p.Bs = T(MXF_T_W2S_C); p.ldb = D; p.ldbs = 4; p.kbsb = 4 * F;
   p.b_es = F * D; p.bs_es = F * D / 32;
   p.N = F; p.K = D;
   p.h13 = (uint16_t*)T(MXF_T_H13);
   p.q_r = T(MXF_T_DHQ_R); p.s_r = T(MXF_T_DHS_R); p.q_c = T(MXF_T_DHQ_C); p.s_c = T(MXF_T_DHS_C);
+  p.sr_rs = 4; p.sr_kbs = 4 * M; p.sc_rs = 4; p.sc_kbs = 4 * 2 * F;
   p.dbg = dbg ? (float*)T(MXF_T_DH_F32) : nullptr;
   MXF_HIP(timed("fc2_dgrad_dswiglu", st, [&] { return mxf_launch_gemm_mgroup(2, p, st); }), "FC2 dgrad launch");
   p.dbg = nullptr;
   p.out_f32 = of32;
   // FC2 wgrad: dW2[e] = dY^T h over the expert's tokens
-  p.A = T(MXF_T_DYQ_C); p.As = T(MXF_T_DYS_C); p.lda = M; p.ldas = M / 32;
-  p.B = T(MXF_T_HQ_C); p.Bs = T(MXF_T_HS_C); p.ldb = M; p.ldbs = M / 32;
+  p.A = T(MXF_T_DYQ_C); p.As = T(MXF_T_DYS_C); p.lda = M; p.ldas = 4; p.kbsa = 4 * D;
+  p.B = T(MXF_T_HQ_C); p.Bs = T(MXF_T_HS_C); p.ldb = M; p.ldbs = 4; p.kbsb = 4 * F;
   p.M = D; p.N = F; p.K = M;
   p.C = dw2; p.ldc = F; p.c_es = D * F;
   MXF_HIP(timed("fc2_wgrad", st, [&] { return mxf_launch_gemm_kgroup(0, p, st); }), "FC2 wgrad launch");
   // FC1 dgrad: dX = dH13 W13
   p.M = M;
-  p.A = T(MXF_T_DHQ_R); p.As = T(MXF_T_DHS_R); p.lda = 2 * F; p.ldas = 2 * F / 32;
-  p.B = T(MXF_T_W13Q_C); p.Bs = T(MXF_T_W13S_C); p.ldb = 2 * F; p.ldbs = 2 * F / 32;
+  p.A = T(MXF_T_DHQ_R); p.As = T(MXF_T_DHS_R); p.lda = 2 * F; p.ldas = 4; p.kbsa = 4 * M;
+  p.B = T(MXF_T_W13Q_C); p.Bs = T(MXF_T_W13S_C); p.ldb = 2 * F; p.ldbs = 4; p.kbsb = 4 * D;
   p.b_es = D * 2 * F; p.bs_es = D * 2 * F / 32;
   p.N = D; p.K = 2 * F;
   p.C = dx; p.ldc = D;
   MXF_HIP(timed("fc1_dgrad", st, [&] { return mxf_launch_gemm_mgroup(0, p, st); }), "FC1 dgrad launch");
   // FC1 wgrad: dW13[e] = dH13^T X over the expert's tokens, unpacked into dW1 / dW3
-  p.A = T(MXF_T_DHQ_C); p.As = T(MXF_T_DHS_C); p.lda = M; p.ldas = M / 32;
-  p.B = T(MXF_T_XQ_C); p.Bs = T(MXF_T_XS_C); p.ldb = M; p.ldbs = M / 32;
+  p.A = T(MXF_T_DHQ_C); p.As = T(MXF_T_DHS_C); p.lda = M; p.ldas = 4; p.kbsa = 4 * 2 * F;
+  p.B = T(MXF_T_XQ_C); p.Bs = T(MXF_T_XS_C); p.ldb = M; p.ldbs = 4; p.kbsb = 4 * D;
   p.M = 2 * F; p.N = D; p.K = M;
   p.C = dw1; p.C2 = dw3; p.ldc = D; p.c_es = F * D;
   MXF_HIP(timed("fc1_wgrad", st, [&] { return mxf_launch_gemm_kgroup(3, p, st); }), "FC1 wgrad launch");

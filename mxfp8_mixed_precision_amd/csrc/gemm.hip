@@ -200,9 +200,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
     kend = kbeg + ksp[e];
     __syncthreads();  // the LDS scratch is reused by the main loop
     Ag = p.A + m0 * p.lda + kbeg;
-    Asg = p.As + m0 * p.ldas + kbeg / 32;
+    Asg = p.As + m0 * p.ldas + (kbeg >> 7) * p.kbsa;
     Bg = p.B + n0 * p.ldb + kbeg;
-    Bsg = p.Bs + n0 * p.ldbs + kbeg / 32;
+    Bsg = p.Bs + n0 * p.ldbs + (kbeg >> 7) * p.kbsb;
   }
   const int tr0 = wm * T::TM;  // first row / column of this wavefront within the block tile
   const int tc0 = wn * T::TN;
@@ -247,9 +247,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
       const int i = q - T::IA;
       g2lds16(b_s + i * b16 + k0, b_v, st + T::B_OFF + (wid_u * T::IB + i) * 1024);
     } else if (q == T::IA + T::IB) {
-      g2lds4(Asg + (k0 >> 7) * 4, sa_v, st + T::SA_OFF + wid_u * 256);
+      g2lds4(Asg + (k0 >> 7) * p.kbsa, sa_v, st + T::SA_OFF + wid_u * 256);
     } else {
-      g2lds4(Bsg + (k0 >> 7) * 4, sb_v, st + T::SB_OFF + wid_u * 256);
+      g2lds4(Bsg + (k0 >> 7) * p.kbsb, sb_v, st + T::SB_OFF + wid_u * 256);
     }
   };
 
@@ -493,7 +493,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
       const int64_t row = m0 + r;
       *reinterpret_cast<uint4*>(p.q_r + row * F + hc0 + c * 16) =
           make_uint4(cvt4(v[0], v[1], s), cvt4(v[2], v[3], s), cvt4(v[4], v[5], s), cvt4(v[6], v[7], s));
-      if (!(c & 1)) p.s_r[row * (F >> 5) + ((hc0 + c * 16) >> 5)] = (uint8_t)s.byte;
+      const int64_t grp = (hc0 + c * 16) >> 5;
+      if (!(c & 1)) p.s_r[row * p.sr_rs + (grp >> 2) * p.sr_kbs + (grp & 3)] = (uint8_t)s.byte;
     }
     // column-wise codes: a column's BM codes are contiguous in hq_c
     constexpr int CPC = BM / 16;
@@ -506,10 +507,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
       const uint2 b = *reinterpret_cast<const uint2*>(qT + hc * QP + c * 16 + 8);
       *reinterpret_cast<uint4*>(p.q_c + (hc0 + hc) * p.mcap + m0 + c * 16) = make_uint4(a.x, a.y, b.x, b.y);
     }
-    for (int t = tid; t < HCB; t += T::NT) {
-      uint8_t* dst = p.s_c + (hc0 + t) * (p.mcap >> 5) + (m0 >> 5);
-      if (SG == 8) *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(sT + t * SG);
-      else *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(sT + t * SG);
+    // column scales: SG groups per column (whole 128-row planes: m0 is a multiple of 128)
+    for (int t = tid; t < HCB * (SG / 4); t += T::NT) {
+      const int hc = t / (SG / 4), w4 = t % (SG / 4);
+      *reinterpret_cast<uint32_t*>(p.s_c + (hc0 + hc) * p.sc_rs + ((m0 >> 7) + w4) * p.sc_kbs) =
+          *reinterpret_cast<const uint32_t*>(sT + hc * SG + 4 * w4);
     }
     return;
   }
@@ -623,7 +625,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
         const int64_t row = rbase + r;
         *reinterpret_cast<uint4*>(p.q_r + row * ld13 + pc0 + c * 16) =
             make_uint4(cvt4(v[0], v[1], s), cvt4(v[2], v[3], s), cvt4(v[4], v[5], s), cvt4(v[6], v[7], s));
-        if (!(c & 1)) p.s_r[row * (ld13 >> 5) + ((pc0 + c * 16) >> 5)] = (uint8_t)s.byte;
+        const int64_t grp = (pc0 + c * 16) >> 5;
+        if (!(c & 1)) p.s_r[row * p.sr_rs + (grp >> 2) * p.sr_kbs + (grp & 3)] = (uint8_t)s.byte;
       }
       constexpr int CPC = T::TM / 16;
       static_assert((PCB * CPC) % T::NT == 0, "whole column-copy rounds");
@@ -636,7 +639,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
         *reinterpret_cast<uint4*>(p.q_c + (pc0 + pc) * p.mcap + rbase + c * 16) = make_uint4(a.x, a.y, b.x, b.y);
       }
       for (int t = tid; t < PCB; t += T::NT) {
-        uint8_t* dst = p.s_c + (pc0 + t) * (p.mcap >> 5) + (rbase >> 5);
+        // SG = TM / 32 groups per column: one 128-row plane word (TM = 128) or half of one
+        const int64_t rg = rbase >> 5;
+        uint8_t* dst = p.s_c + (pc0 + t) * p.sc_rs + (rg >> 2) * p.sc_kbs + (rg & 3);
         if (SG == 4) *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(sT + t * SG);
         else *reinterpret_cast<uint16_t*>(dst) = *reinterpret_cast<const uint16_t*>(sT + t * SG);
       }

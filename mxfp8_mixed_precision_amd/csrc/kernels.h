@@ -5,12 +5,17 @@
 
 namespace mxf {
 
+// Scale addressing (every E8M0 tensor): the byte of (row r, 32-group g) is at
+// r * rs + (g / 4) * kbs + g % 4. Row-major [R][G]: rs = G, kbs = 4. The MLP's operands use
+// 128-k planes [G/4][R][4] (rs = 4, kbs = 4R): the scale words of consecutive rows for one
+// 128-k block are contiguous, so a tile's scales for a K step are one contiguous run.
 struct GemmParams {
   const uint8_t* A;   // codes, rows of K bytes with pitch lda
-  const uint8_t* As;  // scales, pitch ldas
+  const uint8_t* As;  // scales: row stride ldas, 128-k plane stride kbsa
   const uint8_t* B;
   const uint8_t* Bs;
   int64_t lda, ldas, ldb, ldbs;
+  int64_t kbsa, kbsb;
   int64_t b_es, bs_es;  // M-grouped: bytes between experts in B / Bs
   int64_t M, N, K;      // M-grouped: M = m_capacity. K-grouped: output [M, N] per expert
   const int32_t* offs;
@@ -24,9 +29,10 @@ struct GemmParams {
   int out_f32;
   uint16_t* h13;     // SWIGLU: written, DSWIGLU: read; fragment-tiled (4 KB per 32x32 h block)
   uint8_t* q_r;      // SWIGLU: hq_r [mcap, F];  DSWIGLU: dhq_r [mcap, 2F]
-  uint8_t* s_r;
+  uint8_t* s_r;      // their scales: row stride sr_rs, plane stride sr_kbs
   uint8_t* q_c;      // SWIGLU: hq_c [F, mcap];  DSWIGLU: dhq_c [2F, mcap]
-  uint8_t* s_c;
+  uint8_t* s_c;      // row stride sc_rs, plane stride sc_kbs
+  int64_t sr_rs, sr_kbs, sc_rs, sc_kbs;
   float* dbg;        // optional fp32 copy of the accumulator ([mcap, N])
 };
 

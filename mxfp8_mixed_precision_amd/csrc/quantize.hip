@@ -30,9 +30,10 @@ struct QuantParams {
   int64_t rows, cols;    // logical matrix per batch entry (QK_PACK13: rows = 2F, cols = D)
   int64_t src_bs;        // elements between batch entries of src / src2
   uint8_t* q_r;
-  uint8_t* s_r;
+  uint8_t* s_r;          // scale byte (r, g) at r * sr_rs + (g / 4) * sr_kbs + g % 4
   uint8_t* q_c;
-  uint8_t* s_c;
+  uint8_t* s_c;          // scale byte (column c, row group g) at c * sc_rs + (g / 4) * sc_kbs + g % 4
+  int64_t sr_rs, sr_kbs, sc_rs, sc_kbs;
   int64_t qr_bs, sr_bs, qc_bs, sc_bs;  // bytes between batch entries of each output
   int64_t ldc;                          // row pitch (bytes) of q_c; multiple of 32
   const int32_t* offs;                  // QK_MASKED: token offsets [E+1]
@@ -88,7 +89,8 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
   if (ROW) {
     uint8_t* q_r = p.q_r + e * p.qr_bs;
     uint8_t* s_r = p.s_r + e * p.sr_bs;
-    const int64_t ng = p.cols >> 5;
+    const int64_t grp = col >> 5;
+    uint8_t* s_rg = s_r + (grp >> 2) * p.sr_kbs + (grp & 3);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       uint32_t m = pk_max_u16(pk_max_u16(mag2(x[j][0]), mag2(x[j][1])),
@@ -102,7 +104,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
       const int64_t r = r0 + j;
       if (colok && r < p.rows) {
         *reinterpret_cast<uint2*>(q_r + r * p.cols + col) = make_uint2(lo, hi);
-        if ((c & 3) == 0) s_r[r * ng + (col >> 5)] = (uint8_t)sc.byte;
+        if ((c & 3) == 0) s_rg[r * p.sr_rs] = (uint8_t)sc.byte;
       }
     }
   }
@@ -110,7 +112,8 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
   if (COL) {
     uint8_t* q_c = p.q_c + e * p.qc_bs;
     uint8_t* s_c = p.s_c + e * p.sc_bs;
-    const int64_t ldsc = p.ldc >> 5;
+    const int64_t rgrp = rw0 >> 5;
+    uint8_t* s_cg = s_c + (rgrp >> 2) * p.sc_kbs + (rgrp & 3);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       uint32_t m = mag2(x[0][k]);
@@ -129,8 +132,8 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
         *reinterpret_cast<uint2*>(q_c + c0 * p.ldc + r0) = make_uint2(a0, a1);
         *reinterpret_cast<uint2*>(q_c + (c0 + 1) * p.ldc + r0) = make_uint2(b0, b1);
         if (s == 0) {
-          s_c[c0 * ldsc + (rw0 >> 5)] = (uint8_t)slo.byte;
-          s_c[(c0 + 1) * ldsc + (rw0 >> 5)] = (uint8_t)shi.byte;
+          s_cg[c0 * p.sc_rs] = (uint8_t)slo.byte;
+          s_cg[(c0 + 1) * p.sc_rs] = (uint8_t)shi.byte;
         }
       }
     }
@@ -200,11 +203,14 @@ hipError_t mxf_launch_quantize(const void* x, int64_t rows, int64_t cols, uint32
   p.q_c = (uint8_t*)q_col;
   p.s_c = (uint8_t*)s_col;
   p.ldc = rows;
+  p.sr_rs = cols / 32; p.sr_kbs = 4;  // row-major scales
+  p.sc_rs = rows / 32; p.sc_kbs = 4;
   return mxf::launch_quant(mxf::QK_PLAIN, mode, p, 1, st);
 }
 
 // Dual quantization of the activation-like operand x [mcap, D] under the token layout
-// (pad rows read as zero, rows >= offs[E] skipped); writes the status word.
+// (pad rows read as zero, rows >= offs[E] skipped); writes the status word. Scales in 128-k
+// planes (row-wise [D/128][mcap][4], column-wise [mcap/128][D][4]).
 hipError_t mxf_launch_quant_tokens(const void* x, int64_t mcap, int64_t D, const int32_t* offs,
                                    const int32_t* counts, int E, int pad, void* q_r, void* s_r,
                                    void* q_c, void* s_c, int32_t* status, hipStream_t st) {
@@ -217,6 +223,8 @@ hipError_t mxf_launch_quant_tokens(const void* x, int64_t mcap, int64_t D, const
   p.q_c = (uint8_t*)q_c;
   p.s_c = (uint8_t*)s_c;
   p.ldc = mcap;
+  p.sr_rs = 4; p.sr_kbs = 4 * mcap;  // 128-k planes
+  p.sc_rs = 4; p.sc_kbs = 4 * D;
   p.offs = offs;
   p.counts = counts;
   p.E = E;
@@ -225,7 +233,8 @@ hipError_t mxf_launch_quant_tokens(const void* x, int64_t mcap, int64_t D, const
   return mxf::launch_quant(mxf::QK_MASKED, 3, p, 1, st);
 }
 
-// Dual quantization of a batch of E weight matrices [rows, cols]. pack13 = true reads w1/w3
+// Dual quantization of a batch of E weight matrices [rows, cols], scales in 128-k planes per
+// matrix ([cols/128][rows][4] and [rows/128][cols][4]). pack13 = true reads w1/w3
 // [E, rows/2, cols] and quantizes their [E, rows, cols] 32-block interleave.
 hipError_t mxf_launch_quant_weights(const void* w, const void* w3, bool pack13, int64_t E, int64_t rows,
                                     int64_t cols, void* q_r, void* s_r, void* q_c, void* s_c,
@@ -245,6 +254,8 @@ hipError_t mxf_launch_quant_weights(const void* w, const void* w3, bool pack13, 
   p.qc_bs = rows * cols;
   p.sc_bs = cols * (rows / 32);
   p.ldc = rows;
+  p.sr_rs = 4; p.sr_kbs = 4 * rows;  // 128-k planes per matrix
+  p.sc_rs = 4; p.sc_kbs = 4 * cols;
   return mxf::launch_quant(pack13 ? mxf::QK_PACK13 : mxf::QK_PLAIN, 3, p, E, st);
 }
 

@@ -160,3 +160,24 @@ def test_h13_untile_matches_documented_order():
     rm = mx.h13_rowmajor(tiled, F)
     want = torch.arange(M)[:, None] * 100000 + torch.arange(2 * F)[None, :]
     assert torch.equal(rm, want)
+
+
+def test_scale_planes_match_documented_order():
+    """The binding's row-major copy of a plane-ordered scale tensor follows the byte formula
+    stated in include/mxfp8.h, with and without a leading expert dimension."""
+    import torch
+    import mxfp8_mixed_precision_amd as mx
+    for lead in ((), (3,)):
+        R, G = 40, 12
+        n = 1
+        for d in lead:
+            n *= d
+        planes = torch.empty(n * R * G, dtype=torch.int64)
+        for e in range(n):
+            for r in range(R):
+                for g in range(G):
+                    planes[e * R * G + (g // 4) * 4 * R + 4 * r + g % 4] = (e * 1000 + r) * 100 + g
+        rm = mx.scales_rowmajor(planes, (*lead, R, G))
+        want = ((torch.arange(n)[:, None, None] * 1000 + torch.arange(R)[None, :, None]) * 100
+                + torch.arange(G)[None, None, :]).reshape(*lead, R, G)
+        assert torch.equal(rm, want)
