@@ -131,7 +131,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
   const int wm = wid / WN;
   const int wn = wid % WN;
 
-  if (!offsets_valid(p.offs, p.counts, p.E, p.pad, p.mcap)) return;
+  const Offsets ofs = read_offsets(p.offs, p.counts, p.E, p.pad, p.mcap);
+  if (!ofs.ok) return;
 
   int e;
   int64_t m0, n0, kbeg, kend;
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
     // groups of GM row tiles x all column tiles: the ~32 blocks an XCD runs at once share a
     // few A row panels and B column panels in that XCD's L2.
     constexpr int GM = 4;
-    const int64_t mtu = p.offs[p.E] / BM;
+    const int64_t mtu = ofs.mend / BM;
     const int64_t ntiles = mtu * ntn;
     const int64_t b = blockIdx.x;
     if (b >= ntiles) return;
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
     const int64_t within = t - grp * GM * ntn;
     m0 = (first + within % gsz) * BM;
     n0 = (within / gsz) * BN;
-    e = expert_of_row(p.offs, p.E, m0);
+    e = ofs.expert(m0);
     kbeg = 0;
     kend = p.K;
     Ag = p.A + m0 * p.lda;

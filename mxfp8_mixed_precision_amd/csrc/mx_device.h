@@ -162,6 +162,22 @@ __device__ __forceinline__ bool offsets_valid(const int32_t* offs, const int32_t
   return !__any(bad);
 }
 
+// The token offsets read once by a whole wavefront (E < 64: lane i holds offs[i] and
+// counts[i-1]): validity as in offsets_valid, offs[E], and -- with expert() -- the expert that
+// owns a row, from a ballot instead of a chain of dependent loads. Every lane sees the same
+// answers. For E >= 64 the members fall back to the looping helpers.
+struct Offsets {
+  const int32_t* offs;
+  int E;
+  int32_t o;     // offs[lane] (lanes 0..E)
+  bool ok;
+  int64_t mend;  // offs[E]
+  __device__ __forceinline__ int expert(int64_t m) const;
+};
+
+__device__ __forceinline__ bool offsets_valid(const int32_t* offs, const int32_t* counts, int E,
+                                              int pad, int64_t mcap);
+
 // Expert that owns row m (offs[e] <= m < offs[e+1]); requires m < offs[E].
 __device__ __forceinline__ int expert_of_row(const int32_t* offs, int E, int64_t m) {
   int lo = 0, hi = E;  // invariant: offs[lo] <= m < offs[hi]
@@ -170,6 +186,48 @@ __device__ __forceinline__ int expert_of_row(const int32_t* offs, int E, int64_t
     if ((int64_t)offs[mid] <= m) lo = mid; else hi = mid;
   }
   return lo;
+}
+
+}  // namespace mxf
+
+namespace mxf {
+
+__device__ __forceinline__ Offsets read_offsets(const int32_t* offs, const int32_t* counts, int E, int pad,
+                                                int64_t mcap) {
+  Offsets r;
+  r.offs = offs;
+  r.E = E;
+  r.o = 0;
+  if (E >= 64) {
+    r.ok = offsets_valid(offs, counts, E, pad, mcap);
+    r.mend = r.ok ? offs[E] : 0;
+    return r;
+  }
+  const int lane = threadIdx.x & 63;
+  const bool in = lane <= E;
+  const int32_t o = in ? offs[lane] : 0;
+  const int32_t c = (counts && lane >= 1 && in) ? counts[lane - 1] : 0;
+  const int32_t prev = __shfl_up(o, 1);
+  bool bad = false;
+  if (in) {
+    if (o % pad != 0 || o < 0 || (int64_t)o > mcap) bad = true;
+    if (lane == 0 && o != 0) bad = true;
+    if (lane > 0) {
+      if (o < prev) bad = true;
+      if (counts && (c < 0 || c > o - prev)) bad = true;
+    }
+  }
+  r.o = o;
+  r.ok = !__any(bad);
+  r.mend = __builtin_amdgcn_readlane(o, E);  // uniform (SGPR) copy
+  return r;
+}
+
+__device__ __forceinline__ int Offsets::expert(int64_t m) const {
+  if (E >= 64) return expert_of_row(offs, E, m);
+  const int lane = threadIdx.x & 63;
+  // e = #{i in [1, E-1] : offs[i] <= m} (offs is non-decreasing and offs[0] = 0 <= m)
+  return __popcll(__ballot(lane >= 1 && lane < E && (int64_t)o <= m));
 }
 
 }  // namespace mxf

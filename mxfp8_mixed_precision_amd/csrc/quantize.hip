@@ -58,12 +58,11 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
   const uint16_t* src = p.src + e * p.src_bs;
   int64_t src_row0 = rw0;      // source row of the wavefront's first row
   if (KIND == QK_MASKED) {
-    const bool ok = offsets_valid(p.offs, p.counts, p.E, p.pad, p.rows);
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *p.status = ok ? 0 : 1;
-    if (!ok) return;
-    const int64_t mend = p.offs[p.E];
-    if (rw0 >= mend) return;  // tail rows: never read or written
-    const int ex = expert_of_row(p.offs, p.E, rw0);
+    const Offsets ofs = read_offsets(p.offs, p.counts, p.E, p.pad, p.rows);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *p.status = ofs.ok ? 0 : 1;
+    if (!ofs.ok) return;
+    if (rw0 >= ofs.mend) return;  // tail rows: never read or written
+    const int ex = ofs.expert(rw0);
     valid_end = p.offs[ex] + (p.counts ? p.counts[ex] : p.offs[ex + 1] - p.offs[ex]);
   } else if (KIND == QK_PACK13) {
     // packed row n of [2F, D]: groups of 32 rows alternate between w1 and w3
