@@ -518,24 +518,30 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
   }
 
   if (EPI == EPI_DSWIGLU) {
-    // N = F: acc = dh. The saved g, u of every fragment are loaded first (4 KB records in
-    // accumulator order, so each lane's slots arrive in its own registers). Then, one wavefront
-    // row (TM rows) at a time: dG = dh u s (1 + g (1 - s)), dU = dh g s with s = sigmoid(g),
-    // each rounded to BF16; their column-wise groups are quantized in registers (codes staged
-    // transposed in LDS), the BF16 values staged row-major in the packed order (gate group,
-    // then up group, per 32 columns); the block then quantizes the row-wise groups and copies
-    // the column codes out.
+    // N = F: acc = dh. Two rounds; in round hh every wavefront takes its fragment rows
+    // [hh FM/2, (hh+1) FM/2) (all SIMDs busy): dG = dh u s (1 + g (1 - s)), dU = dh g s with
+    // s = sigmoid(g), from the saved g, u (4 KB records in accumulator order, so each lane's
+    // slots arrive in its own registers), each rounded to BF16. Their column-wise groups are
+    // quantized in registers (codes staged transposed in LDS) and the BF16 values staged
+    // row-major in the packed order (gate group, then up group, per 32 columns); then the block
+    // quantizes the staged rows' row-wise groups and copies the column codes out.
+    static_assert(T::FM % 2 == 0, "two rounds of whole fragment rows");
+    constexpr int FH = T::FM / 2;     // fragment rows per wavefront per round
+    constexpr int RH = T::TM / 2;     // rows per wavefront per round
     constexpr int PCB = 2 * BN;       // packed columns of the block
     constexpr int DP = PCB + 8;       // row-major tile pitch (bf16)
     constexpr int QP = T::TM + 8;     // transposed code tile pitch (bytes)
-    constexpr int SG = T::TM / 32;
+    constexpr int SG = T::TM / 32;    // column groups staged per round
     const int64_t F = p.N;
     const int64_t ld13 = 2 * F;
     const int64_t pc0 = 2 * n0;
     uint16_t* dR = reinterpret_cast<uint16_t*>(smem);
     uint8_t* qT = smem + T::TM * DP * 2;
     uint8_t* sT = qT + PCB * QP;
-    // g, u of one fragment row (FN fragments) in flight while the previous one is processed
+    // staged row lr of round hh is block row (lr / RH) * TM + hh * RH + lr % RH
+    auto brow = [&](int hh, int lr) { return (lr / RH) * T::TM + hh * RH + lr % RH; };
+    // g, u of two fragment rows (FN fragments each) in flight: row i + 2 is requested as soon
+    // as row i has been consumed
     uint4 gs[2][T::FN][2], us[2][T::FN][2];
     auto load_gu = [&](int i, int buf) {
 #pragma unroll
@@ -549,6 +555,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
       }
     };
     load_gu(0, 0);
+    load_gu(1, 1);
     if (p.dbg) {
 #pragma unroll
       for (int i = 0; i < T::FM; ++i)
@@ -558,59 +565,57 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
           for (int q = 0; q < 16; ++q)
             p.dbg[(wrow0 + i * 32 + 8 * (q >> 2) + 4 * g + (q & 3)) * F + wcol0 + j * 32 + r32] = acc[i][j][q];
     }
-#pragma unroll 1
-    for (int hh = 0; hh < WM; ++hh) {
-      if (wm == hh) {
 #pragma unroll
-        for (int i = 0; i < T::FM; ++i) {
-          if (i + 1 < T::FM) load_gu(i + 1, (i + 1) & 1);
+    for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-          for (int j = 0; j < T::FN; ++j) {
-            const int b = i & 1;
-            const uint32_t gw[8] = {gs[b][j][0].x, gs[b][j][0].y, gs[b][j][0].z, gs[b][j][0].w,
-                                    gs[b][j][1].x, gs[b][j][1].y, gs[b][j][1].z, gs[b][j][1].w};
-            const uint32_t uw[8] = {us[b][j][0].x, us[b][j][0].y, us[b][j][0].z, us[b][j][0].w,
-                                    us[b][j][1].x, us[b][j][1].y, us[b][j][1].z, us[b][j][1].w};
-            uint32_t dgw[8], duw[8];
+      for (int ii = 0; ii < FH; ++ii) {
+        const int i = hh * FH + ii;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-              uint32_t og = 0, ou = 0;
+        for (int j = 0; j < T::FN; ++j) {
+          const int b = i & 1;
+          const uint32_t gw[8] = {gs[b][j][0].x, gs[b][j][0].y, gs[b][j][0].z, gs[b][j][0].w,
+                                  gs[b][j][1].x, gs[b][j][1].y, gs[b][j][1].z, gs[b][j][1].w};
+          const uint32_t uw[8] = {us[b][j][0].x, us[b][j][0].y, us[b][j][0].z, us[b][j][0].w,
+                                  us[b][j][1].x, us[b][j][1].y, us[b][j][1].z, us[b][j][1].w};
+          uint32_t dgw[8], duw[8];
 #pragma unroll
-              for (int s = 0; s < 2; ++s) {
-                const int q = 2 * t + s;
-                const float dv = acc[i][j][q];
-                const float dh = bf16_to_f32(bf16_bits(dv));
-                const float gf = bf16_to_f32((gw[t] >> (16 * s)) & 0xFFFFu);
-                const float uf = bf16_to_f32((uw[t] >> (16 * s)) & 0xFFFFu);
-                const float sg = sigmoid_f(gf);
-                og |= bf16_bits(dh * uf * sg * (1.0f + gf * (1.0f - sg))) << (16 * s);
-                ou |= bf16_bits(dh * gf * sg) << (16 * s);
-              }
-              dgw[t] = og;
-              duw[t] = ou;
+          for (int t = 0; t < 8; ++t) {
+            uint32_t og = 0, ou = 0;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+              const int q = 2 * t + s;
+              const float dv = acc[i][j][q];
+              const float dh = bf16_to_f32(bf16_bits(dv));
+              const float gf = bf16_to_f32((gw[t] >> (16 * s)) & 0xFFFFu);
+              const float uf = bf16_to_f32((uw[t] >> (16 * s)) & 0xFFFFu);
+              const float sg = sigmoid_f(gf);
+              og |= bf16_bits(dh * uf * sg * (1.0f + gf * (1.0f - sg))) << (16 * s);
+              ou |= bf16_bits(dh * gf * sg) << (16 * s);
             }
-            const int pcg = 2 * (tc0 + j * 32) + r32;  // packed column of dG (dU: + 32)
-            const int rl = i * 32 + 4 * g;
+            dgw[t] = og;
+            duw[t] = ou;
+          }
+          const int pcg = 2 * (tc0 + j * 32) + r32;  // packed column of dG (dU: + 32)
+          const int rl = wm * RH + ii * 32 + 4 * g;  // staged row of slot 0
 #pragma unroll
-            for (int part = 0; part < 2; ++part) {
-              const uint32_t* w = part ? duw : dgw;
-              const int pcl = pcg + 32 * part;
-              uint32_t am = amax16(w);
-              am = max(am, (uint32_t)__shfl_xor((int)am, 32));
-              const Scale s = scale_from_amax(am);
+          for (int part = 0; part < 2; ++part) {
+            const uint32_t* w = part ? duw : dgw;
+            const int pcl = pcg + 32 * part;
+            uint32_t am = amax16(w);
+            am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+            const Scale s = scale_from_amax(am);
 #pragma unroll
-              for (int k = 0; k < 4; ++k)
-                *reinterpret_cast<uint32_t*>(qT + pcl * QP + rl + 8 * k) = cvt4(w[2 * k], w[2 * k + 1], s);
-              if (g == 0) sT[pcl * SG + i] = (uint8_t)s.byte;
+            for (int k = 0; k < 4; ++k)
+              *reinterpret_cast<uint32_t*>(qT + pcl * QP + rl + 8 * k) = cvt4(w[2 * k], w[2 * k + 1], s);
+            if (g == 0) sT[pcl * SG + wm * FH + ii] = (uint8_t)s.byte;
 #pragma unroll
-              for (int q = 0; q < 16; ++q)
-                dR[(rl + 8 * (q >> 2) + (q & 3)) * DP + pcl] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
-            }
+            for (int q = 0; q < 16; ++q)
+              dR[(rl + 8 * (q >> 2) + (q & 3)) * DP + pcl] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
           }
         }
+        if (i + 2 < T::FM) load_gu(i + 2, i & 1);
       }
       __syncthreads();
-      const int64_t rbase = m0 + hh * T::TM;
       constexpr int CPR = PCB / 16;
       static_assert((T::TM * CPR) % T::NT == 0 && CPR % 2 == 0, "whole row-pass rounds");
 #pragma unroll 2
@@ -623,30 +628,29 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
         uint32_t am = amax16(v);
         am = max(am, dpp_xor1(am));
         const Scale s = scale_from_amax(am);
-        const int64_t row = rbase + r;
+        const int64_t row = m0 + brow(hh, r);
         *reinterpret_cast<uint4*>(p.q_r + row * ld13 + pc0 + c * 16) =
             make_uint4(cvt4(v[0], v[1], s), cvt4(v[2], v[3], s), cvt4(v[4], v[5], s), cvt4(v[6], v[7], s));
         const int64_t grp = (pc0 + c * 16) >> 5;
         if (!(c & 1)) p.s_r[row * p.sr_rs + (grp >> 2) * p.sr_kbs + (grp & 3)] = (uint8_t)s.byte;
       }
       constexpr int CPC = T::TM / 16;
-      static_assert((PCB * CPC) % T::NT == 0, "whole column-copy rounds");
+      static_assert((PCB * CPC) % T::NT == 0 && RH % 16 == 0, "whole column-copy rounds");
 #pragma unroll 2
       for (int it = 0; it < PCB * CPC / T::NT; ++it) {
         const int t = it * T::NT + tid;
         const int pc = t / CPC, c = t % CPC;
         const uint2 a = *reinterpret_cast<const uint2*>(qT + pc * QP + c * 16);
         const uint2 b = *reinterpret_cast<const uint2*>(qT + pc * QP + c * 16 + 8);
-        *reinterpret_cast<uint4*>(p.q_c + (pc0 + pc) * p.mcap + rbase + c * 16) = make_uint4(a.x, a.y, b.x, b.y);
+        *reinterpret_cast<uint4*>(p.q_c + (pc0 + pc) * p.mcap + m0 + brow(hh, c * 16)) =
+            make_uint4(a.x, a.y, b.x, b.y);
       }
-      for (int t = tid; t < PCB; t += T::NT) {
-        // SG = TM / 32 groups per column: one 128-row plane word (TM = 128) or half of one
-        const int64_t rg = rbase >> 5;
-        uint8_t* dst = p.s_c + (pc0 + t) * p.sc_rs + (rg >> 2) * p.sc_kbs + (rg & 3);
-        if (SG == 4) *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(sT + t * SG);
-        else *reinterpret_cast<uint16_t*>(dst) = *reinterpret_cast<const uint16_t*>(sT + t * SG);
+      for (int t = tid; t < PCB * SG; t += T::NT) {
+        const int pc = t / SG, gi = t % SG;
+        const int64_t rg = (m0 + brow(hh, gi * 32)) >> 5;
+        p.s_c[(pc0 + pc) * p.sc_rs + (rg >> 2) * p.sc_kbs + (rg & 3)] = sT[pc * SG + gi];
       }
-      __syncthreads();  // the staging tiles are rewritten for the next wavefront row
+      __syncthreads();  // the staging tiles are rewritten in the next round
     }
     return;
   }
