@@ -45,23 +45,36 @@ struct QuantParams {
 
 template <int KIND, bool ROW, bool COL>
 __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  // Column codes of the block, transposed [128 columns][QTP bytes], and the block's scale
+  // words (4 groups of a row / of a column), staged in LDS so that every global store is a
+  // 16-byte (codes) or 4-byte (scales) piece of a contiguous run.
+  constexpr int QTP = 128 + 8;
+  __shared__ __attribute__((aligned(16))) uint8_t qT[COL ? 128 * QTP : 16];
+  __shared__ uint32_t srow[128];
+  __shared__ uint32_t scol[128];
+  uint8_t* srow_b = reinterpret_cast<uint8_t*>(srow);
+  uint8_t* scol_b = reinterpret_cast<uint8_t*>(scol);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
   const int s = lane >> 4;
   const int c = lane & 15;
   const int64_t e = blockIdx.z;
-  const int64_t col = (int64_t)blockIdx.y * 128 + c * 8;
-  const int64_t rw0 = (int64_t)blockIdx.x * 128 + w * 32;  // first row of this wavefront
-  const int64_t r0 = rw0 + 8 * s;                           // first row of this lane
+  const int64_t row0 = (int64_t)blockIdx.x * 128, col0 = (int64_t)blockIdx.y * 128;
+  const int64_t col = col0 + c * 8;
+  const int64_t rw0 = row0 + w * 32;  // first row of this wavefront
+  const int64_t r0 = rw0 + 8 * s;     // first row of this lane
 
   int64_t valid_end = p.rows;  // rows at or past this read as zero
   const uint16_t* src = p.src + e * p.src_bs;
   int64_t src_row0 = rw0;      // source row of the wavefront's first row
   if (KIND == QK_MASKED) {
+    // every wavefront reads the offsets (same answers everywhere); mend and the block's rows
+    // are multiples of 128, so a block is either wholly before offs[E] or wholly past it
     const Offsets ofs = read_offsets(p.offs, p.counts, p.E, p.pad, p.rows);
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *p.status = ofs.ok ? 0 : 1;
     if (!ofs.ok) return;
-    if (rw0 >= ofs.mend) return;  // tail rows: never read or written
+    if (row0 >= ofs.mend) return;  // tail rows: never read or written
     const int ex = ofs.expert(rw0);
     valid_end = p.offs[ex] + (p.counts ? p.counts[ex] : p.offs[ex + 1] - p.offs[ex]);
   } else if (KIND == QK_PACK13) {
@@ -70,14 +83,14 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
     src = ((grp & 1) ? p.src2 : p.src) + e * p.src_bs;
     src_row0 = (grp >> 1) * 32;
   }
-  if (rw0 >= p.rows) return;
   const bool colok = col < p.cols;
+  const int64_t rend = valid_end < p.rows ? valid_end : p.rows;
 
   uint32_t x[8][4];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int64_t r = r0 + j;
-    if (colok && r < valid_end) {
+    if (colok && r < rend) {
       const uint4 v = *reinterpret_cast<const uint4*>(src + (src_row0 + 8 * s + j) * p.cols + col);
       x[j][0] = v.x; x[j][1] = v.y; x[j][2] = v.z; x[j][3] = v.w;
     } else {
@@ -87,9 +100,6 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
 
   if (ROW) {
     uint8_t* q_r = p.q_r + e * p.qr_bs;
-    uint8_t* s_r = p.s_r + e * p.sr_bs;
-    const int64_t grp = col >> 5;
-    uint8_t* s_rg = s_r + (grp >> 2) * p.sr_kbs + (grp & 3);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       uint32_t m = pk_max_u16(pk_max_u16(mag2(x[j][0]), mag2(x[j][1])),
@@ -101,18 +111,12 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
       const uint32_t lo = cvt4(x[j][0], x[j][1], sc);
       const uint32_t hi = cvt4(x[j][2], x[j][3], sc);
       const int64_t r = r0 + j;
-      if (colok && r < p.rows) {
-        *reinterpret_cast<uint2*>(q_r + r * p.cols + col) = make_uint2(lo, hi);
-        if ((c & 3) == 0) s_rg[r * p.sr_rs] = (uint8_t)sc.byte;
-      }
+      if (colok && r < p.rows) *reinterpret_cast<uint2*>(q_r + r * p.cols + col) = make_uint2(lo, hi);
+      if ((c & 3) == 0) srow_b[(r - row0) * 4 + (c >> 2)] = (uint8_t)sc.byte;
     }
   }
 
   if (COL) {
-    uint8_t* q_c = p.q_c + e * p.qc_bs;
-    uint8_t* s_c = p.s_c + e * p.sc_bs;
-    const int64_t rgrp = rw0 >> 5;
-    uint8_t* s_cg = s_c + (rgrp >> 2) * p.sc_kbs + (rgrp & 3);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       uint32_t m = mag2(x[0][k]);
@@ -126,14 +130,53 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
       const uint32_t a1 = cvt4(pack_lo(x[4][k], x[5][k]), pack_lo(x[6][k], x[7][k]), slo);
       const uint32_t b0 = cvt4(pack_hi(x[0][k], x[1][k]), pack_hi(x[2][k], x[3][k]), shi);
       const uint32_t b1 = cvt4(pack_hi(x[4][k], x[5][k]), pack_hi(x[6][k], x[7][k]), shi);
-      if (colok) {
-        const int64_t c0 = col + 2 * k;
-        *reinterpret_cast<uint2*>(q_c + c0 * p.ldc + r0) = make_uint2(a0, a1);
-        *reinterpret_cast<uint2*>(q_c + (c0 + 1) * p.ldc + r0) = make_uint2(b0, b1);
-        if (s == 0) {
-          s_cg[c0 * p.sc_rs] = (uint8_t)slo.byte;
-          s_cg[(c0 + 1) * p.sc_rs] = (uint8_t)shi.byte;
-        }
+      const int cl = c * 8 + 2 * k;  // block-local column
+      const int rl = w * 32 + 8 * s;  // block-local row
+      *reinterpret_cast<uint2*>(qT + cl * QTP + rl) = make_uint2(a0, a1);
+      *reinterpret_cast<uint2*>(qT + (cl + 1) * QTP + rl) = make_uint2(b0, b1);
+      if (s == 0) {
+        scol_b[cl * 4 + w] = (uint8_t)slo.byte;
+        scol_b[(cl + 1) * 4 + w] = (uint8_t)shi.byte;
+      }
+    }
+  }
+  __syncthreads();
+
+  if (ROW && tid < 128) {
+    // the block's 4 row groups of row r are one word in the 128-k plane layout
+    const int64_t r = row0 + tid;
+    const int64_t g0 = col0 >> 5;
+    const int64_t ng = (p.cols - col0) >> 5;  // valid groups in the block (>= 1)
+    uint8_t* dst = p.s_r + e * p.sr_bs + r * p.sr_rs + (g0 >> 2) * p.sr_kbs;
+    if (r < p.rows) {
+      if (ng >= 4 && (p.sr_rs & 3) == 0 && (p.sr_kbs & 3) == 0) {
+        *reinterpret_cast<uint32_t*>(dst) = srow[tid];
+      } else {
+        for (int g = 0; g < 4 && g < ng; ++g) dst[g] = srow_b[tid * 4 + g];
+      }
+    }
+  }
+  if (COL) {
+    uint8_t* q_c = p.q_c + e * p.qc_bs;
+    // a column's codes for the block's rows are contiguous in q_c: 16 bytes per task
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int t = it * 256 + tid;
+      const int cl = t >> 3, ch = t & 7;
+      if (col0 + cl < p.cols && row0 + ch * 16 < p.rows) {
+        const uint2 a = *reinterpret_cast<const uint2*>(qT + cl * QTP + ch * 16);
+        const uint2 b = *reinterpret_cast<const uint2*>(qT + cl * QTP + ch * 16 + 8);
+        *reinterpret_cast<uint4*>(q_c + (col0 + cl) * p.ldc + row0 + ch * 16) = make_uint4(a.x, a.y, b.x, b.y);
+      }
+    }
+    if (tid < 128 && col0 + tid < p.cols) {
+      const int64_t g0 = row0 >> 5;
+      const int64_t ng = (p.rows - row0) >> 5;
+      uint8_t* dst = p.s_c + e * p.sc_bs + (col0 + tid) * p.sc_rs + (g0 >> 2) * p.sc_kbs;
+      if (ng >= 4 && (p.sc_rs & 3) == 0 && (p.sc_kbs & 3) == 0) {
+        *reinterpret_cast<uint32_t*>(dst) = scol[tid];
+      } else {
+        for (int g = 0; g < 4 && g < ng; ++g) dst[g] = scol_b[tid * 4 + g];
       }
     }
   }
