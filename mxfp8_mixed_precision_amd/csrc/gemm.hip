@@ -165,9 +165,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
     Bg = p.B + e * p.b_es + n0 * p.ldb;
     Bsg = p.Bs + e * p.bs_es + n0 * p.ldbs;
   } else {
-    // Experts are taken longest-K first (their tiles start earliest, which shortens the tail);
-    // within an expert, tiles go 8 row tiles fastest, so consecutive blocks -- one per XCD --
-    // each keep one A row panel in their L2 while sweeping the column tiles.
+    // Experts are taken longest-K first (their tiles start earliest, which shortens the tail).
+    // Within an expert every tile streams the whole K range, so what matters is how many A
+    // row panels and B column panels each XCD's L2 must hold: block l of the expert runs on
+    // XCD l % 8, each XCD takes a contiguous run of positions, and positions walk the tile
+    // grid in strips 4 tiles wide across the smaller dimension, so a run covers a compact
+    // patch (for 11 x 8 tiles: 60 panel streams in all instead of 96 for whole rows).
     int* ksp = reinterpret_cast<int*>(smem);  // per-expert K span, then the order (LDS scratch)
     int* order = ksp + p.E;
     for (int i = tid; i < p.E; i += T::NT) {
@@ -190,13 +193,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
     const int64_t per = (int64_t)mtn * ntn;
     const int64_t t = blockIdx.x;
     e = order[t / per];
-    const int64_t w = t % per;
-    constexpr int GMK = 8;
-    const int64_t first = (w / (GMK * ntn)) * GMK;
-    const int64_t gsz = min((int64_t)GMK, mtn - first);
-    const int64_t within = w - first * ntn;
-    m0 = (first + within % gsz) * BM;
-    n0 = (within / gsz) * BN;
+    const int64_t l = t % per;
+    const int64_t q8 = per / 8, r8 = per % 8, x8 = l % 8, s8 = l / 8;
+    const int64_t pos = (x8 < r8 ? x8 * (q8 + 1) : r8 * (q8 + 1) + (x8 - r8) * q8) + s8;
+    // strips of width W across the smaller grid dimension; the longer one runs inside a strip
+    const bool mlong = mtn >= ntn;
+    const int64_t nlong = mlong ? mtn : ntn, nshort = mlong ? ntn : mtn;
+    constexpr int W = 4;
+    const int64_t nstrip = (nshort + W - 1) / W;
+    const int64_t strip = min(pos / (W * nlong), nstrip - 1);
+    const int64_t sw = min((int64_t)W, nshort - strip * W);  // width of this strip
+    const int64_t within = pos - strip * W * nlong;
+    const int64_t il = within / sw, is = strip * W + within % sw;
+    m0 = (mlong ? il : is) * BM;
+    n0 = (mlong ? is : il) * BN;
     kbeg = p.offs[e];
     kend = kbeg + ksp[e];
     __syncthreads();  // the LDS scratch is reused by the main loop
