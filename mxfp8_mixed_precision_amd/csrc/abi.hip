@@ -97,6 +97,36 @@ hipError_t timed(const char* name, hipStream_t st, Fn&& launch) {
   return hipSuccess;
 }
 
+// ------------------------------------------------------------------ helper streams
+
+// Launches of one MLP call that do not depend on each other run on two helper streams, forked
+// from and joined back into the caller's stream with events (no host synchronisation, and the
+// fork/join pattern is legal under stream capture). Each host thread owns its own helpers per
+// device, created on first use at the default priority and kept until the process ends.
+struct Helpers {
+  bool ready = false;
+  hipStream_t s[2];
+  hipEvent_t fork;
+  hipEvent_t join[2];
+};
+thread_local Helpers g_helpers[kMaxDevices];
+
+mxf_status get_helpers(Helpers** out) {
+  int dev = 0;
+  MXF_HIP(hipGetDevice(&dev), "hipGetDevice");
+  Helpers& h = g_helpers[dev];
+  if (!h.ready) {
+    for (int i = 0; i < 2; ++i) {
+      MXF_HIP(hipStreamCreateWithFlags(&h.s[i], hipStreamNonBlocking), "hipStreamCreateWithFlags");
+      MXF_HIP(hipEventCreateWithFlags(&h.join[i], hipEventDisableTiming), "hipEventCreateWithFlags");
+    }
+    MXF_HIP(hipEventCreateWithFlags(&h.fork, hipEventDisableTiming), "hipEventCreateWithFlags");
+    h.ready = true;
+  }
+  *out = &h;
+  return MXF_OK;
+}
+
 // ------------------------------------------------------------------ MLP buffer layout
 
 struct Layout {
@@ -277,15 +307,23 @@ mxf_status grouped_mlp_fwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
             return mxf_launch_quant_weights(w1, w3, true, E, 2 * F, D, T(MXF_T_W13Q_R), T(MXF_T_W13S_R),
                                             T(MXF_T_W13Q_C), T(MXF_T_W13S_C), st);
           }), "W13 quantize launch");
-  MXF_HIP(timed("quant_w2", st, [&] {
-            return mxf_launch_quant_weights(w2, nullptr, false, E, D, F, T(MXF_T_W2Q_R), T(MXF_T_W2S_R),
-                                            T(MXF_T_W2Q_C), T(MXF_T_W2S_C), st);
-          }), "W2 quantize launch");
   MXF_HIP(timed("quant_x", st, [&] {
             return mxf_launch_quant_tokens(x, M, D, offs, counts, (int)E, desc->pad_multiple, T(MXF_T_XQ_R),
                                            T(MXF_T_XS_R), T(MXF_T_XQ_C), T(MXF_T_XS_C),
                                            (int32_t*)T(MXF_T_STATUS), st);
           }), "X quantize launch");
+
+  // W2 is needed only by FC2: its (HBM-bound) quantization runs on a helper stream beside FC1,
+  // whose main loop is bound by L2 -> LDS traffic and leaves HBM bandwidth spare
+  Helpers* H = nullptr;
+  if ((s = get_helpers(&H)) != MXF_OK) return s;
+  MXF_HIP(hipEventRecord(H->fork, st), "hipEventRecord");
+  MXF_HIP(hipStreamWaitEvent(H->s[0], H->fork, 0), "hipStreamWaitEvent");
+  MXF_HIP(timed("quant_w2", H->s[0], [&] {
+            return mxf_launch_quant_weights(w2, nullptr, false, E, D, F, T(MXF_T_W2Q_R), T(MXF_T_W2S_R),
+                                            T(MXF_T_W2Q_C), T(MXF_T_W2S_C), H->s[0]);
+          }), "W2 quantize launch");
+  MXF_HIP(hipEventRecord(H->join[0], H->s[0]), "hipEventRecord");
 
   mxf::GemmParams p = {};
   p.offs = offs;
@@ -312,6 +350,7 @@ mxf_status grouped_mlp_fwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   p.N = D; p.K = F;
   p.C = y; p.ldc = D; p.out_f32 = (desc->flags & MXF_OUT_F32) ? 1 : 0;
   p.dbg = nullptr;
+  MXF_HIP(hipStreamWaitEvent(st, H->join[0], 0), "hipStreamWaitEvent");
   MXF_HIP(timed("fc2", st, [&] { return mxf_launch_gemm_mgroup(0, p, st); }), "FC2 launch");
   return MXF_OK;
 }
@@ -363,12 +402,21 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   MXF_HIP(timed("fc2_dgrad_dswiglu", st, [&] { return mxf_launch_gemm_mgroup(2, p, st); }), "FC2 dgrad launch");
   p.dbg = nullptr;
   p.out_f32 = of32;
+  // FC2 wgrad, FC1 dgrad and FC1 wgrad only read what the launches above wrote and write
+  // disjoint outputs: the two wgrads run on helper streams beside FC1 dgrad, so each kernel's
+  // last partial round of tiles overlaps the others' work
+  Helpers* H = nullptr;
+  if ((s = get_helpers(&H)) != MXF_OK) return s;
+  MXF_HIP(hipEventRecord(H->fork, st), "hipEventRecord");
+  MXF_HIP(hipStreamWaitEvent(H->s[0], H->fork, 0), "hipStreamWaitEvent");
+  MXF_HIP(hipStreamWaitEvent(H->s[1], H->fork, 0), "hipStreamWaitEvent");
   // FC2 wgrad: dW2[e] = dY^T h over the expert's tokens
   p.A = T(MXF_T_DYQ_C); p.As = T(MXF_T_DYS_C); p.lda = M; p.ldas = 4; p.kbsa = 4 * D;
   p.B = T(MXF_T_HQ_C); p.Bs = T(MXF_T_HS_C); p.ldb = M; p.ldbs = 4; p.kbsb = 4 * F;
   p.M = D; p.N = F; p.K = M;
   p.C = dw2; p.ldc = F; p.c_es = D * F;
-  MXF_HIP(timed("fc2_wgrad", st, [&] { return mxf_launch_gemm_kgroup(0, p, st); }), "FC2 wgrad launch");
+  MXF_HIP(timed("fc2_wgrad", H->s[0], [&] { return mxf_launch_gemm_kgroup(0, p, H->s[0]); }), "FC2 wgrad launch");
+  MXF_HIP(hipEventRecord(H->join[0], H->s[0]), "hipEventRecord");
   // FC1 dgrad: dX = dH13 W13
   p.M = M;
   p.A = T(MXF_T_DHQ_R); p.As = T(MXF_T_DHS_R); p.lda = 2 * F; p.ldas = 4; p.kbsa = 4 * M;
@@ -376,13 +424,17 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   p.b_es = D * 2 * F; p.bs_es = D * 2 * F / 32;
   p.N = D; p.K = 2 * F;
   p.C = dx; p.ldc = D;
-  MXF_HIP(timed("fc1_dgrad", st, [&] { return mxf_launch_gemm_mgroup(0, p, st); }), "FC1 dgrad launch");
+  const mxf::GemmParams p_dgrad1 = p;
   // FC1 wgrad: dW13[e] = dH13^T X over the expert's tokens, unpacked into dW1 / dW3
   p.A = T(MXF_T_DHQ_C); p.As = T(MXF_T_DHS_C); p.lda = M; p.ldas = 4; p.kbsa = 4 * 2 * F;
   p.B = T(MXF_T_XQ_C); p.Bs = T(MXF_T_XS_C); p.ldb = M; p.ldbs = 4; p.kbsb = 4 * D;
   p.M = 2 * F; p.N = D; p.K = M;
   p.C = dw1; p.C2 = dw3; p.ldc = D; p.c_es = F * D;
-  MXF_HIP(timed("fc1_wgrad", st, [&] { return mxf_launch_gemm_kgroup(3, p, st); }), "FC1 wgrad launch");
+  MXF_HIP(timed("fc1_wgrad", H->s[1], [&] { return mxf_launch_gemm_kgroup(3, p, H->s[1]); }), "FC1 wgrad launch");
+  MXF_HIP(hipEventRecord(H->join[1], H->s[1]), "hipEventRecord");
+  MXF_HIP(timed("fc1_dgrad", st, [&] { return mxf_launch_gemm_mgroup(0, p_dgrad1, st); }), "FC1 dgrad launch");
+  MXF_HIP(hipStreamWaitEvent(st, H->join[0], 0), "hipStreamWaitEvent");
+  MXF_HIP(hipStreamWaitEvent(st, H->join[1], 0), "hipStreamWaitEvent");
   return MXF_OK;
 }
 
