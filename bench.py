@@ -119,6 +119,8 @@ def main():
     ap.add_argument("--no-quant", action="store_true", help="skip the standalone quantizer measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference kernel for HBM byte counters)")
+    ap.add_argument("--serial", action="store_true",
+                    help="time with MXF_SERIAL too (every kernel alone; for profiler runs)")
     ap.add_argument("--quant-only", action="store_true",
                     help="only measure the standalone quantizer (for a profiler run of that kernel alone)")
     args = ap.parse_args()
@@ -163,7 +165,7 @@ def main():
         sets.append({k: p[k] for k in ("x", "w1", "w3", "w2", "dy")})
     offs_t = torch.tensor(offs, dtype=torch.int32, device=dev)
     counts_t = torch.tensor(counts, dtype=torch.int32, device=dev)
-    ctx = mx.MlpContext(E, D, F, pad, mcap, flags=0, device=dev)
+    ctx = mx.MlpContext(E, D, F, pad, mcap, flags=mx.SERIAL if args.serial else 0, device=dev)
     y = torch.empty((mcap, D), dtype=torch.bfloat16, device=dev)
     dx = torch.empty((mcap, D), dtype=torch.bfloat16, device=dev)
     dw1 = torch.empty((E, F, D), dtype=torch.bfloat16, device=dev)
@@ -194,14 +196,28 @@ def main():
     executed = 18.0 * m_pad * D * F
     value = useful / (ms_per_step / 1e3) / 1e12
 
-    # per-kernel timing (library-internal HIP events on the launch stream), same steps again
+    # Per-kernel timing: library-internal HIP events on each launch's stream, over the same
+    # steps again with MXF_SERIAL, so that every kernel runs alone on the GPU (in the timed
+    # steps above some launches of a call overlap on helper streams, which would stretch each
+    # one's own duration).
+    sctx = mx.MlpContext(E, D, F, pad, mcap, flags=mx.SERIAL, device=dev)
+
+    def sstep(i):
+        s = sets[i % len(sets)]
+        sctx.fwd(offs_t, counts_t, s["x"], s["w1"], s["w3"], s["w2"], y)
+        sctx.bwd(offs_t, counts_t, s["dy"], dx, dw1, dw3, dw2)
+
+    for i in range(2):
+        sstep(i)
+    torch.cuda.synchronize()
     mx.profile_begin(12 * args.steps + 16)
     t2 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        sstep(i)
     torch.cuda.synchronize()
     t3 = time.perf_counter()
     prof = mx.profile_end()
+    del sctx
     kernels = {}
     for name, (n, tot) in prof.items():
         avg = tot / n
@@ -242,7 +258,9 @@ def main():
         "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 4),
         "roofline": roof,
         "kernels": kernels,
-        "profiled_ms_per_step": round((t3 - t2) * 1e3 / args.steps, 4),
+        "launches": "serial (MXF_SERIAL)" if args.serial else "concurrent where independent (helper streams)",
+        "kernels_timing": "a second pass of the same steps with MXF_SERIAL (each kernel alone on the GPU)",
+        "serial_ms_per_step": round((t3 - t2) * 1e3 / args.steps, 4),
     }
 
     if not args.no_quant:

@@ -100,6 +100,10 @@ mxf_status mxfp8_quantize(const void* x, int64_t rows, int64_t cols, uint32_t mo
 #define MXF_OUT_F32 1u     /* y, dx, dw1, dw3, dw2 are FP32 instead of BF16 */
 #define MXF_DEBUG_F32 2u   /* also store the FP32 FC1 output and FP32 dh (FC2 dgrad) in the
                               workspace (tensors MXF_T_H13_F32, MXF_T_DH_F32) */
+#define MXF_SERIAL 4u      /* launch every kernel on the caller's stream, one after another
+                              (by default independent launches run concurrently on two helper
+                              streams forked from and joined into the caller's stream); for
+                              timing each kernel alone */
 
 typedef struct {
   int32_t E;             /* local experts, 1 .. 1024 */
@@ -107,7 +111,7 @@ typedef struct {
   int32_t F;             /* expert hidden dim, multiple of 128 */
   int32_t pad_multiple;  /* 128 or 256: every expert segment is a multiple of this */
   int64_t m_capacity;    /* rows allocated in x/y/dy/dx; multiple of pad_multiple */
-  uint32_t flags;        /* MXF_OUT_F32 | MXF_DEBUG_F32 */
+  uint32_t flags;        /* MXF_OUT_F32 | MXF_DEBUG_F32 | MXF_SERIAL */
 } mxf_mlp_desc;
 
 /* Tensors held in the caller's buffers (for tests and inspection). Region: 0 = workspace,
@@ -154,7 +158,12 @@ size_t mxf_mlp_workspace_bytes(const mxf_mlp_desc* desc /* host */);
 mxf_status mxf_mlp_tensor(const mxf_mlp_desc* desc /* host */, int which, int* region /* host */,
                           size_t* offset /* host */, size_t* bytes /* host */);
 
-/* Forward. offs: int32 [E+1] (offs[0] = 0, non-decreasing, multiples of pad_multiple,
+/* Streams: fwd and bwd enqueue their kernels asynchronously. Unless MXF_SERIAL is set, some of
+ * them run on two helper streams owned by the calling host thread (one pair per device); the
+ * helpers start after everything previously enqueued on `stream` and `stream` waits for them
+ * before the call returns, so the call behaves as one ordered unit of work on `stream`.
+ *
+ * Forward. offs: int32 [E+1] (offs[0] = 0, non-decreasing, multiples of pad_multiple,
  * offs[E] <= m_capacity); expert e owns rows [offs[e], offs[e+1]). counts: int32 [E] real
  * rows per expert (counts[e] <= offs[e+1]-offs[e]) or NULL (every row real). Rows in
  * [offs[e]+counts[e], offs[e+1]) are pad: read as zero, written as zero. Rows at or after

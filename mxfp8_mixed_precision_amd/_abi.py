@@ -21,7 +21,7 @@ STATUS_NAMES = {OK: "MXF_OK", E_NULL: "MXF_E_NULL", E_SHAPE: "MXF_E_SHAPE", E_AL
 DEV_OK, DEV_BAD_OFFSETS = 0, 1
 CAP_GFX950 = 1
 ROW, COL = 1, 2
-OUT_F32, DEBUG_F32 = 1, 2
+OUT_F32, DEBUG_F32, SERIAL = 1, 2, 4
 
 # tensor ids (mxf_tensor)
 TENSORS = ["STATUS", "XQ_R", "XS_R", "XQ_C", "XS_C", "W13Q_R", "W13S_R", "W13Q_C", "W13S_C",

@@ -111,7 +111,15 @@ struct Helpers {
 };
 thread_local Helpers g_helpers[kMaxDevices];
 
-mxf_status get_helpers(Helpers** out) {
+// With MXF_SERIAL the "helpers" are the caller's stream itself (no fork, no join).
+mxf_status get_helpers(Helpers** out, uint32_t flags, hipStream_t st) {
+  if (flags & MXF_SERIAL) {
+    thread_local Helpers serial;
+    serial.ready = true;
+    serial.s[0] = serial.s[1] = st;
+    *out = &serial;
+    return MXF_OK;
+  }
   int dev = 0;
   MXF_HIP(hipGetDevice(&dev), "hipGetDevice");
   Helpers& h = g_helpers[dev];
@@ -149,7 +157,7 @@ mxf_status check_desc(const mxf_mlp_desc* d) {
                 (long long)d->m_capacity, d->pad_multiple);
   if (d->m_capacity > (int64_t)1 << 30)
     return fail(MXF_E_SHAPE, "m_capacity = %lld: larger than 2^30 rows", (long long)d->m_capacity);
-  if (d->flags & ~(uint32_t)(MXF_OUT_F32 | MXF_DEBUG_F32))
+  if (d->flags & ~(uint32_t)(MXF_OUT_F32 | MXF_DEBUG_F32 | MXF_SERIAL))
     return fail(MXF_E_ARG, "flags = 0x%x: unknown bits", d->flags);
   return MXF_OK;
 }
@@ -316,14 +324,17 @@ mxf_status grouped_mlp_fwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   // W2 is needed only by FC2: its (HBM-bound) quantization runs on a helper stream beside FC1,
   // whose main loop is bound by L2 -> LDS traffic and leaves HBM bandwidth spare
   Helpers* H = nullptr;
-  if ((s = get_helpers(&H)) != MXF_OK) return s;
-  MXF_HIP(hipEventRecord(H->fork, st), "hipEventRecord");
-  MXF_HIP(hipStreamWaitEvent(H->s[0], H->fork, 0), "hipStreamWaitEvent");
+  if ((s = get_helpers(&H, desc->flags, st)) != MXF_OK) return s;
+  const bool fork = H->s[0] != st;
+  if (fork) {
+    MXF_HIP(hipEventRecord(H->fork, st), "hipEventRecord");
+    MXF_HIP(hipStreamWaitEvent(H->s[0], H->fork, 0), "hipStreamWaitEvent");
+  }
   MXF_HIP(timed("quant_w2", H->s[0], [&] {
             return mxf_launch_quant_weights(w2, nullptr, false, E, D, F, T(MXF_T_W2Q_R), T(MXF_T_W2S_R),
                                             T(MXF_T_W2Q_C), T(MXF_T_W2S_C), H->s[0]);
           }), "W2 quantize launch");
-  MXF_HIP(hipEventRecord(H->join[0], H->s[0]), "hipEventRecord");
+  if (fork) MXF_HIP(hipEventRecord(H->join[0], H->s[0]), "hipEventRecord");
 
   mxf::GemmParams p = {};
   p.offs = offs;
@@ -350,7 +361,7 @@ mxf_status grouped_mlp_fwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   p.N = D; p.K = F;
   p.C = y; p.ldc = D; p.out_f32 = (desc->flags & MXF_OUT_F32) ? 1 : 0;
   p.dbg = nullptr;
-  MXF_HIP(hipStreamWaitEvent(st, H->join[0], 0), "hipStreamWaitEvent");
+  if (fork) MXF_HIP(hipStreamWaitEvent(st, H->join[0], 0), "hipStreamWaitEvent");
   MXF_HIP(timed("fc2", st, [&] { return mxf_launch_gemm_mgroup(0, p, st); }), "FC2 launch");
   return MXF_OK;
 }
@@ -406,17 +417,20 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   // disjoint outputs: the two wgrads run on helper streams beside FC1 dgrad, so each kernel's
   // last partial round of tiles overlaps the others' work
   Helpers* H = nullptr;
-  if ((s = get_helpers(&H)) != MXF_OK) return s;
-  MXF_HIP(hipEventRecord(H->fork, st), "hipEventRecord");
-  MXF_HIP(hipStreamWaitEvent(H->s[0], H->fork, 0), "hipStreamWaitEvent");
-  MXF_HIP(hipStreamWaitEvent(H->s[1], H->fork, 0), "hipStreamWaitEvent");
+  if ((s = get_helpers(&H, desc->flags, st)) != MXF_OK) return s;
+  const bool fork = H->s[0] != st;
+  if (fork) {
+    MXF_HIP(hipEventRecord(H->fork, st), "hipEventRecord");
+    MXF_HIP(hipStreamWaitEvent(H->s[0], H->fork, 0), "hipStreamWaitEvent");
+    MXF_HIP(hipStreamWaitEvent(H->s[1], H->fork, 0), "hipStreamWaitEvent");
+  }
   // FC2 wgrad: dW2[e] = dY^T h over the expert's tokens
   p.A = T(MXF_T_DYQ_C); p.As = T(MXF_T_DYS_C); p.lda = M; p.ldas = 4; p.kbsa = 4 * D;
   p.B = T(MXF_T_HQ_C); p.Bs = T(MXF_T_HS_C); p.ldb = M; p.ldbs = 4; p.kbsb = 4 * F;
   p.M = D; p.N = F; p.K = M;
   p.C = dw2; p.ldc = F; p.c_es = D * F;
   MXF_HIP(timed("fc2_wgrad", H->s[0], [&] { return mxf_launch_gemm_kgroup(0, p, H->s[0]); }), "FC2 wgrad launch");
-  MXF_HIP(hipEventRecord(H->join[0], H->s[0]), "hipEventRecord");
+  if (fork) MXF_HIP(hipEventRecord(H->join[0], H->s[0]), "hipEventRecord");
   // FC1 dgrad: dX = dH13 W13
   p.M = M;
   p.A = T(MXF_T_DHQ_R); p.As = T(MXF_T_DHS_R); p.lda = 2 * F; p.ldas = 4; p.kbsa = 4 * M;
@@ -431,10 +445,12 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   p.M = 2 * F; p.N = D; p.K = M;
   p.C = dw1; p.C2 = dw3; p.ldc = D; p.c_es = F * D;
   MXF_HIP(timed("fc1_wgrad", H->s[1], [&] { return mxf_launch_gemm_kgroup(3, p, H->s[1]); }), "FC1 wgrad launch");
-  MXF_HIP(hipEventRecord(H->join[1], H->s[1]), "hipEventRecord");
+  if (fork) MXF_HIP(hipEventRecord(H->join[1], H->s[1]), "hipEventRecord");
   MXF_HIP(timed("fc1_dgrad", st, [&] { return mxf_launch_gemm_mgroup(0, p_dgrad1, st); }), "FC1 dgrad launch");
-  MXF_HIP(hipStreamWaitEvent(st, H->join[0], 0), "hipStreamWaitEvent");
-  MXF_HIP(hipStreamWaitEvent(st, H->join[1], 0), "hipStreamWaitEvent");
+  if (fork) {
+    MXF_HIP(hipStreamWaitEvent(st, H->join[0], 0), "hipStreamWaitEvent");
+    MXF_HIP(hipStreamWaitEvent(st, H->join[1], 0), "hipStreamWaitEvent");
+  }
   return MXF_OK;
 }
 

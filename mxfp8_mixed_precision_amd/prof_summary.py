@@ -17,9 +17,10 @@ Outputs (in OUTDIR): <kernel-group>_<workload>.md summaries and traffic.json (HB
 per launch, with the sha256 of the kernel sources they were measured on; bench.py only
 reports them while the sources are unchanged).
 
-Kernel dispatches are named by their position in a bench.py step: the MLP step launches, in
-order, quant_w13, quant_w2, quant_x, fc1_swiglu, fc2, quant_dy, fc2_dgrad_dswiglu, fc2_wgrad,
-fc1_dgrad, fc1_wgrad; a --quant-only run launches `quantize` only.
+Kernel dispatches are named by their position in a bench.py step: the MLP step enqueues, in
+order, quant_w13, quant_x, quant_w2, fc1_swiglu, fc2, quant_dy, fc2_dgrad_dswiglu, fc2_wgrad,
+fc1_wgrad, fc1_dgrad; a --quant-only run launches `quantize` only. Profile with
+`bench.py --serial` so that every kernel runs alone (durations not stretched by overlap).
 """
 import argparse
 import csv
@@ -30,8 +31,8 @@ import os
 import re
 from collections import defaultdict
 
-MLP_SEQUENCE = ["quant_w13", "quant_w2", "quant_x", "fc1_swiglu", "fc2", "quant_dy", "fc2_dgrad_dswiglu",
-                "fc2_wgrad", "fc1_dgrad", "fc1_wgrad"]
+MLP_SEQUENCE = ["quant_w13", "quant_x", "quant_w2", "fc1_swiglu", "fc2", "quant_dy", "fc2_dgrad_dswiglu",
+                "fc2_wgrad", "fc1_wgrad", "fc1_dgrad"]
 # expected kernel template per logical name: (kernel family, SCHED/KIND, EPI/ROW,COL)
 EXPECT = {
     "quant_w13": "quant_dual_kernel<2,", "quant_w2": "quant_dual_kernel<0,", "quant_x": "quant_dual_kernel<1,",

@@ -226,6 +226,20 @@ def test_deterministic(tiny):
         assert torch.equal(r[k][:, :w], r2[k][:, :w]), k
 
 
+def test_serial_launches_match_concurrent(tiny):
+    """MXF_SERIAL (every kernel on the caller's stream) and the default helper-stream fork/join
+    give bit-identical outputs and saved tensors."""
+    mx, prob, r = tiny
+    r2 = run_mlp(mx, prob, mx.OUT_F32 | mx.DEBUG_F32 | mx.SERIAL)
+    m = prob["offs"][-1]
+    for k in ("y", "dx", "dw1", "dw3", "dw2"):
+        assert torch.equal(r[k], r2[k]), k
+    for k in ("HQ_R", "DHQ_R"):  # rows at or past offs[E] are never written
+        assert torch.equal(r[k][:m], r2[k][:m]), k
+    for k in ("W2Q_R", "W2S_R", "W2Q_C"):
+        assert torch.equal(r[k], r2[k]), k
+
+
 def test_nan_poisoned_pad_and_tail(tiny):
     mx, prob, r = tiny
     poisoned = workloads.mlp_problem("tiny", m_capacity=1536, pad_fill=float("nan"), tail_fill=float("nan"))
