@@ -393,60 +393,76 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
                                            T(MXF_T_DYS_R), T(MXF_T_DYQ_C), T(MXF_T_DYS_C),
                                            (int32_t*)T(MXF_T_STATUS), st);
           }), "dY quantize launch");
-  mxf::GemmParams p = {};
-  p.offs = offs;
-  p.counts = counts;
-  p.E = (int)E;
-  p.pad = desc->pad_multiple;
-  p.mcap = M;
-  // FC2 dgrad + dSwiGLU + dual quantization of dH13
-  p.M = M;
-  // every scale tensor is in 128-k planes: row stride 4, plane stride 4 x rows
-  p.A = T(MXF_T_DYQ_R); p.As = T(MXF_T_DYS_R); p.lda = D; p.ldas = 4; p.kbsa = 4 * M;
-  p.B = T(MXF_T_W2Q_C); p.Bs = T(MXF_T_W2S_C); p.ldb = D; p.ldbs = 4; p.kbsb = 4 * F;
-  p.b_es = F * D; p.bs_es = F * D / 32;
-  p.N = F; p.K = D;
-  p.h13 = (uint16_t*)T(MXF_T_H13);
-  p.q_r = T(MXF_T_DHQ_R); p.s_r = T(MXF_T_DHS_R); p.q_c = T(MXF_T_DHQ_C); p.s_c = T(MXF_T_DHS_C);
-  p.sr_rs = 4; p.sr_kbs = 4 * M; p.sc_rs = 4; p.sc_kbs = 4 * 2 * F;
-  p.dbg = dbg ? (float*)T(MXF_T_DH_F32) : nullptr;
-  MXF_HIP(timed("fc2_dgrad_dswiglu", st, [&] { return mxf_launch_gemm_mgroup(2, p, st); }), "FC2 dgrad launch");
-  p.dbg = nullptr;
-  p.out_f32 = of32;
-  // FC2 wgrad, FC1 dgrad and FC1 wgrad only read what the launches above wrote and write
-  // disjoint outputs: the two wgrads run on helper streams beside FC1 dgrad, so each kernel's
-  // last partial round of tiles overlaps the others' work
+  mxf::GemmParams base = {};
+  base.offs = offs;
+  base.counts = counts;
+  base.E = (int)E;
+  base.pad = desc->pad_multiple;
+  base.mcap = M;
+  base.out_f32 = of32;
+  // After dY's quantization the backward is a small graph: FC2 wgrad needs only dY and the
+  // saved h, so it runs on a helper stream beside FC2 dgrad; FC1 dgrad (caller's stream) and
+  // FC1 wgrad (second helper) both need dH13 from FC2 dgrad and run beside each other. Each
+  // kernel's last partial round of tiles then overlaps another kernel's work.
   Helpers* H = nullptr;
   if ((s = get_helpers(&H, desc->flags, st)) != MXF_OK) return s;
   const bool fork = H->s[0] != st;
-  if (fork) {
-    MXF_HIP(hipEventRecord(H->fork, st), "hipEventRecord");
-    MXF_HIP(hipStreamWaitEvent(H->s[0], H->fork, 0), "hipStreamWaitEvent");
-    MXF_HIP(hipStreamWaitEvent(H->s[1], H->fork, 0), "hipStreamWaitEvent");
-  }
   // FC2 wgrad: dW2[e] = dY^T h over the expert's tokens
-  p.A = T(MXF_T_DYQ_C); p.As = T(MXF_T_DYS_C); p.lda = M; p.ldas = 4; p.kbsa = 4 * D;
-  p.B = T(MXF_T_HQ_C); p.Bs = T(MXF_T_HS_C); p.ldb = M; p.ldbs = 4; p.kbsb = 4 * F;
-  p.M = D; p.N = F; p.K = M;
-  p.C = dw2; p.ldc = F; p.c_es = D * F;
-  MXF_HIP(timed("fc2_wgrad", H->s[0], [&] { return mxf_launch_gemm_kgroup(0, p, H->s[0]); }), "FC2 wgrad launch");
-  if (fork) MXF_HIP(hipEventRecord(H->join[0], H->s[0]), "hipEventRecord");
-  // FC1 dgrad: dX = dH13 W13
-  p.M = M;
-  p.A = T(MXF_T_DHQ_R); p.As = T(MXF_T_DHS_R); p.lda = 2 * F; p.ldas = 4; p.kbsa = 4 * M;
-  p.B = T(MXF_T_W13Q_C); p.Bs = T(MXF_T_W13S_C); p.ldb = 2 * F; p.ldbs = 4; p.kbsb = 4 * D;
-  p.b_es = D * 2 * F; p.bs_es = D * 2 * F / 32;
-  p.N = D; p.K = 2 * F;
-  p.C = dx; p.ldc = D;
-  const mxf::GemmParams p_dgrad1 = p;
+  {
+    mxf::GemmParams p = base;
+    // every scale tensor is in 128-k planes: row stride 4, plane stride 4 x rows
+    p.A = T(MXF_T_DYQ_C); p.As = T(MXF_T_DYS_C); p.lda = M; p.ldas = 4; p.kbsa = 4 * D;
+    p.B = T(MXF_T_HQ_C); p.Bs = T(MXF_T_HS_C); p.ldb = M; p.ldbs = 4; p.kbsb = 4 * F;
+    p.M = D; p.N = F; p.K = M;
+    p.C = dw2; p.ldc = F; p.c_es = D * F;
+    if (fork) {
+      MXF_HIP(hipEventRecord(H->fork, st), "hipEventRecord");
+      MXF_HIP(hipStreamWaitEvent(H->s[0], H->fork, 0), "hipStreamWaitEvent");
+    }
+    MXF_HIP(timed("fc2_wgrad", H->s[0], [&] { return mxf_launch_gemm_kgroup(0, p, H->s[0]); }),
+            "FC2 wgrad launch");
+    if (fork) MXF_HIP(hipEventRecord(H->join[0], H->s[0]), "hipEventRecord");
+  }
+  // FC2 dgrad + dSwiGLU + dual quantization of dH13
+  {
+    mxf::GemmParams p = base;
+    p.M = M;
+    p.A = T(MXF_T_DYQ_R); p.As = T(MXF_T_DYS_R); p.lda = D; p.ldas = 4; p.kbsa = 4 * M;
+    p.B = T(MXF_T_W2Q_C); p.Bs = T(MXF_T_W2S_C); p.ldb = D; p.ldbs = 4; p.kbsb = 4 * F;
+    p.b_es = F * D; p.bs_es = F * D / 32;
+    p.N = F; p.K = D;
+    p.h13 = (uint16_t*)T(MXF_T_H13);
+    p.q_r = T(MXF_T_DHQ_R); p.s_r = T(MXF_T_DHS_R); p.q_c = T(MXF_T_DHQ_C); p.s_c = T(MXF_T_DHS_C);
+    p.sr_rs = 4; p.sr_kbs = 4 * M; p.sc_rs = 4; p.sc_kbs = 4 * 2 * F;
+    p.dbg = dbg ? (float*)T(MXF_T_DH_F32) : nullptr;
+    MXF_HIP(timed("fc2_dgrad_dswiglu", st, [&] { return mxf_launch_gemm_mgroup(2, p, st); }), "FC2 dgrad launch");
+  }
   // FC1 wgrad: dW13[e] = dH13^T X over the expert's tokens, unpacked into dW1 / dW3
-  p.A = T(MXF_T_DHQ_C); p.As = T(MXF_T_DHS_C); p.lda = M; p.ldas = 4; p.kbsa = 4 * 2 * F;
-  p.B = T(MXF_T_XQ_C); p.Bs = T(MXF_T_XS_C); p.ldb = M; p.ldbs = 4; p.kbsb = 4 * D;
-  p.M = 2 * F; p.N = D; p.K = M;
-  p.C = dw1; p.C2 = dw3; p.ldc = D; p.c_es = F * D;
-  MXF_HIP(timed("fc1_wgrad", H->s[1], [&] { return mxf_launch_gemm_kgroup(3, p, H->s[1]); }), "FC1 wgrad launch");
-  if (fork) MXF_HIP(hipEventRecord(H->join[1], H->s[1]), "hipEventRecord");
-  MXF_HIP(timed("fc1_dgrad", st, [&] { return mxf_launch_gemm_mgroup(0, p_dgrad1, st); }), "FC1 dgrad launch");
+  {
+    mxf::GemmParams p = base;
+    p.A = T(MXF_T_DHQ_C); p.As = T(MXF_T_DHS_C); p.lda = M; p.ldas = 4; p.kbsa = 4 * 2 * F;
+    p.B = T(MXF_T_XQ_C); p.Bs = T(MXF_T_XS_C); p.ldb = M; p.ldbs = 4; p.kbsb = 4 * D;
+    p.M = 2 * F; p.N = D; p.K = M;
+    p.C = dw1; p.C2 = dw3; p.ldc = D; p.c_es = F * D;
+    if (fork) {
+      MXF_HIP(hipEventRecord(H->fork, st), "hipEventRecord");
+      MXF_HIP(hipStreamWaitEvent(H->s[1], H->fork, 0), "hipStreamWaitEvent");
+    }
+    MXF_HIP(timed("fc1_wgrad", H->s[1], [&] { return mxf_launch_gemm_kgroup(3, p, H->s[1]); }),
+            "FC1 wgrad launch");
+    if (fork) MXF_HIP(hipEventRecord(H->join[1], H->s[1]), "hipEventRecord");
+  }
+  // FC1 dgrad: dX = dH13 W13
+  {
+    mxf::GemmParams p = base;
+    p.M = M;
+    p.A = T(MXF_T_DHQ_R); p.As = T(MXF_T_DHS_R); p.lda = 2 * F; p.ldas = 4; p.kbsa = 4 * M;
+    p.B = T(MXF_T_W13Q_C); p.Bs = T(MXF_T_W13S_C); p.ldb = 2 * F; p.ldbs = 4; p.kbsb = 4 * D;
+    p.b_es = D * 2 * F; p.bs_es = D * 2 * F / 32;
+    p.N = D; p.K = 2 * F;
+    p.C = dx; p.ldc = D;
+    MXF_HIP(timed("fc1_dgrad", st, [&] { return mxf_launch_gemm_mgroup(0, p, st); }), "FC1 dgrad launch");
+  }
   if (fork) {
     MXF_HIP(hipStreamWaitEvent(st, H->join[0], 0), "hipStreamWaitEvent");
     MXF_HIP(hipStreamWaitEvent(st, H->join[1], 0), "hipStreamWaitEvent");

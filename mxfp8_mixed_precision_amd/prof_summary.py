@@ -18,7 +18,7 @@ per launch, with the sha256 of the kernel sources they were measured on; bench.p
 reports them while the sources are unchanged).
 
 Kernel dispatches are named by their position in a bench.py step: the MLP step enqueues, in
-order, quant_w13, quant_x, quant_w2, fc1_swiglu, fc2, quant_dy, fc2_dgrad_dswiglu, fc2_wgrad,
+order, quant_w13, quant_x, quant_w2, fc1_swiglu, fc2, quant_dy, fc2_wgrad, fc2_dgrad_dswiglu,
 fc1_wgrad, fc1_dgrad; a --quant-only run launches `quantize` only. Profile with
 `bench.py --serial` so that every kernel runs alone (durations not stretched by overlap).
 """
@@ -31,8 +31,8 @@ import os
 import re
 from collections import defaultdict
 
-MLP_SEQUENCE = ["quant_w13", "quant_x", "quant_w2", "fc1_swiglu", "fc2", "quant_dy", "fc2_dgrad_dswiglu",
-                "fc2_wgrad", "fc1_wgrad", "fc1_dgrad"]
+MLP_SEQUENCE = ["quant_w13", "quant_x", "quant_w2", "fc1_swiglu", "fc2", "quant_dy", "fc2_wgrad",
+                "fc2_dgrad_dswiglu", "fc1_wgrad", "fc1_dgrad"]
 # expected kernel template per logical name: (kernel family, SCHED/KIND, EPI/ROW,COL)
 EXPECT = {
     "quant_w13": "quant_dual_kernel<2,", "quant_w2": "quant_dual_kernel<0,", "quant_x": "quant_dual_kernel<1,",
