@@ -27,7 +27,7 @@ contiguous; the scales likewise [cols, rows/32].
 """
 import numpy as np
 
-from .formats import E4M3_MAX, E4M3_TABLE, bf16_bits_to_f64, e4m3_to_f64, e8m0_to_f64
+from .formats import E4M3_MAX, E4M3_TABLE, bf16_bits_to_f64, e4m3_to_f64, e8m0_to_f64, f64_to_bf16_bits
 
 BLOCK = 32
 
@@ -124,6 +124,34 @@ def dequantize_rowwise(q, s):
     r, c = q.shape
     x = e8m0_to_f64(s).reshape(r, c // BLOCK, 1)
     return (e4m3_to_f64(q).reshape(r, c // BLOCK, BLOCK) * x).reshape(r, c)
+
+
+def dequantize_groups(q, s):
+    """Row-wise MXFP8 decode when the last group of a row may be short (afd-plugin PR #475
+    "quantize the A2E FFN transport to MXFP8", third review: hidden sizes that are not a
+    multiple of 32 leave a final group of fewer than 32 elements, which has its own scale).
+
+    q [R, C] uint8 codes for any C >= 0; s [R, ceil(C/32)] uint8 scale bytes.
+    deq[r, c] = E4M3(q[r, c]) * E8M0(s[r, c // 32]), exact in fp64 (E8M0 0x00 = 2^-127,
+    0xFF = NaN; E4M3 0x7F / 0xFF = NaN).
+    """
+    q = np.asarray(q, dtype=np.uint8)
+    r, c = q.shape
+    s = np.asarray(s, dtype=np.uint8)
+    assert s.shape == (r, -(-c // BLOCK))
+    grp = np.arange(c) // BLOCK
+    return e4m3_to_f64(q) * e8m0_to_f64(s)[:, grp]
+
+
+def dequantize_to(q, s, dtype):
+    """dequantize_groups rounded once to the output format: "bf16" (RNE, returned as uint16
+    bit patterns) or "f32" (RNE, returned as float32). Both overflow to infinity."""
+    v = dequantize_groups(q, s)
+    if dtype == "bf16":
+        return f64_to_bf16_bits(v)
+    assert dtype == "f32"
+    with np.errstate(over="ignore", invalid="ignore"):
+        return v.astype(np.float32)
 
 
 def quantize_bf16_rowwise(bits):

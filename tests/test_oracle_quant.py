@@ -215,3 +215,60 @@ def test_rowwise_and_colwise_layout():
     assert np.array_equal(qc[7, 32:64], qb[0]) and sc[7, 1] == sb[0]
     d = dequantize_rowwise(q, s)
     assert np.max(np.abs(d - a) / np.max(np.abs(a))) < 2 ** -3
+
+
+# ------------------------------------------------------------------ dequantize (short groups)
+
+def test_dequantize_all_codes_all_scales_against_torch_decoders():
+    """Every (E4M3 code, E8M0 byte) pair decodes to the product of torch's own float8_e4m3fn
+    and float8_e8m0fnu decoders (library routines, independent of the oracle's tables),
+    including byte 0x00 = 2^-127 and 0xFF = NaN."""
+    from oracle.mx import dequantize_groups
+    codes = np.tile(np.arange(256, dtype=np.uint8), (256, 1))          # row b: all codes
+    scales = np.arange(256, dtype=np.uint8)[:, None].repeat(8, axis=1)  # 256 columns = 8 groups
+    got = dequantize_groups(codes, scales)
+    e4 = torch.from_numpy(np.arange(256, dtype=np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+    e8 = torch.from_numpy(np.arange(256, dtype=np.uint8)).view(torch.float8_e8m0fnu).double().numpy()
+    want = e8[:, None] * e4[None, :]
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+    assert e8[0] == 2.0 ** -127 and np.isnan(e8[255])
+
+
+@pytest.mark.parametrize("cols", [1, 31, 33, 63, 100, 129])
+def test_dequantize_short_last_group_uses_its_own_scale(cols):
+    """With C % 32 != 0 the last group of each row is short and has its own scale byte;
+    full-width rows decode like the row-wise decoder on the padded matrix."""
+    from oracle.mx import dequantize_groups
+    rng = np.random.default_rng(cols)
+    g = -(-cols // 32)
+    q = rng.integers(0, 256, size=(5, cols), dtype=np.uint8)
+    s = rng.integers(100, 150, size=(5, g), dtype=np.uint8)
+    got = dequantize_groups(q, s)
+    qp = np.zeros((5, g * 32), dtype=np.uint8)
+    qp[:, :cols] = q
+    want = dequantize_rowwise(qp, s)[:, :cols]
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    assert np.array_equal(got[~np.isnan(got)], want[~np.isnan(want)])
+    # element c of a row is scaled by byte s[r, c // 32] alone
+    k = cols - 1
+    v = e4m3_to_f64(q[:, k]) * e8m0_to_f64(s[:, k // 32])
+    assert np.array_equal(np.nan_to_num(got[:, k], nan=-1.0), np.nan_to_num(v, nan=-1.0))
+
+
+def test_dequantize_output_rounding_and_overflow():
+    """BF16 / FP32 outputs are one RNE rounding of the exact product; 448 * 2^127 overflows
+    both to infinity, and 2^-9 * 2^-127 = 2^-136 is an FP32 subnormal but rounds to zero in
+    BF16 (below half of its smallest subnormal 2^-133)."""
+    from oracle.mx import dequantize_to
+    q = np.array([[0x7E, 0x01, 0x38, 0xFE]], dtype=np.uint8)   # 448, 2^-9, 1.0, -448
+    for byte, bf16_want, f32_want in (
+        # 448 * 2^127 -> inf; 2^118 -> exponent field 245; 2^127 -> field 254
+        (254, [0x7F80, 0x7A80, 0x7F00, 0xFF80], [np.inf, 2.0 ** 118, 2.0 ** 127, -np.inf]),
+        # 1.75 * 2^-119 -> field 8, mantissa 0x60; 2^-136 -> 0; 2^-127 -> subnormal 0x40
+        (0, [0x0460, 0x0000, 0x0040, 0x8460], [448 * 2.0 ** -127, 2.0 ** -136, 2.0 ** -127, -448 * 2.0 ** -127]),
+    ):
+        s = np.array([[byte]], dtype=np.uint8)
+        assert dequantize_to(q, s, "bf16").tolist() == [bf16_want]
+        assert dequantize_to(q, s, "f32").astype(np.float64).tolist() == [f32_want]
