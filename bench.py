@@ -265,6 +265,7 @@ def main():
 
     if not args.no_quant:
         out["quantize"] = bench_quantize(mx, torch, dev, args)
+        out["dequantize"] = bench_dequantize(mx, torch, dev, args)
 
     if not args.no_cpu_baseline:
         cpu_prob = workloads.mlp_problem(args.workload, seed=42)
@@ -302,6 +303,34 @@ def bench_quantize(mx, torch, dev, args):
             "roofline": {"bound": "hbm", "kernel": "quantize", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": traffic_for("quantize", "quant")}}
+
+
+def bench_dequantize(mx, torch, dev, args):
+    """MXFP8 -> BF16 decode of the quantizer workload's row-wise output (3 rotating inputs)."""
+    import workloads
+    rows, cols = workloads.QUANT_CONFIG["rows"], workloads.QUANT_CONFIG["cols"]
+    qs = []
+    for s in range(3):
+        q, sc, _, _ = mx.quantize(workloads.quant_matrix(rows, cols, seed=42 + s, device=dev), mx.ROW)
+        qs.append((q, sc))
+    out = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+    n = max(args.steps, 10)
+    for i in range(3):
+        mx.mxfp8_dequantize(qs[i][0], qs[i][1], rows, cols, mx.DEQ_BF16, out)
+    torch.cuda.synchronize()
+    mx.profile_begin(n)
+    for i in range(n):
+        mx.mxfp8_dequantize(qs[i % 3][0], qs[i % 3][1], rows, cols, mx.DEQ_BF16, out)
+    torch.cuda.synchronize()
+    prof = mx.profile_end()
+    cnt, tot = prof["dequantize"]
+    avg_s = tot / cnt / 1e3
+    nbytes = rows * cols * (1 + 1.0 / 32 + 2)
+    gbs = nbytes / avg_s / 1e9
+    return {"workload": f"E4M3 + E8M0 [{rows}, {cols}] row-wise -> BF16", "value": round(gbs, 1),
+            "unit": "GB/s", "avg_us": round(avg_s * 1e6, 2),
+            "roofline": {"bound": "hbm", "kernel": "dequantize", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
 
 if __name__ == "__main__":

@@ -95,6 +95,25 @@ const char* mxf_last_error(void);
 mxf_status mxfp8_quantize(const void* x, int64_t rows, int64_t cols, uint32_t mode,
                           void* q_row, void* s_row, void* q_col, void* s_col, void* stream);
 
+/* ------------------------------------------------------------------ dequantization */
+
+#define MXF_DEQ_BF16 0u  /* out is BF16 */
+#define MXF_DEQ_F32 1u   /* out is FP32 */
+
+/* Decode of row-wise MXFP8 (the receive side of an MXFP8 transport; afd-plugin PR #475
+ * "quantize the A2E FFN transport to MXFP8", third review on E8M0 decoding and on hidden sizes
+ * that are not a multiple of 32).
+ * q [rows, cols] u8 E4M3 codes; s [rows, ceil(cols/32)] u8 E8M0 bytes: element (r, c) uses
+ * s[r, c / 32], so when cols % 32 != 0 the last group of a row is short and has its own byte.
+ * out [rows, cols] row-major = E4M3(q) * 2^(s - 127) rounded once (RNE) to BF16 or FP32
+ * (out_type MXF_DEQ_BF16 / MXF_DEQ_F32); overflow gives +-Inf. Scale byte 0x00 is 2^-127
+ * (not zero), 0xFF is NaN (the whole group decodes to NaN); codes 0x7F / 0xFF are NaN (the sign
+ * and payload of a NaN result are unspecified).
+ * Any rows, cols >= 0 (empty is a no-op accepting NULL); q and out 16-byte aligned.
+ * Errors: MXF_E_NULL, MXF_E_SHAPE, MXF_E_ALIGN, MXF_E_ARG (out_type), MXF_E_DEVICE, MXF_E_HIP. */
+mxf_status mxfp8_dequantize(const void* q, const void* s, int64_t rows, int64_t cols, uint32_t out_type,
+                            void* out, void* stream);
+
 /* ------------------------------------------------------------------ routed-experts MLP */
 
 #define MXF_OUT_F32 1u     /* y, dx, dw1, dw3, dw2 are FP32 instead of BF16 */

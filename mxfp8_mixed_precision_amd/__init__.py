@@ -5,7 +5,8 @@ this package is its Python binding. ``MlpContext`` allocates the caller-owned
 ``saved`` and ``workspace`` buffers with torch and exposes the library's
 documented intermediate tensors as views, for tests and inspection.
 """
-from ._abi import (CAP_GFX950, COL, DEBUG_F32, DEV_BAD_OFFSETS, DEV_OK, EXPORTS, LIB_PATH, OUT_F32, SERIAL,
+from ._abi import (CAP_GFX950, COL, DEBUG_F32, DEQ_BF16, DEQ_F32, DEV_BAD_OFFSETS, DEV_OK, EXPORTS, LIB_PATH,
+                   OUT_F32, SERIAL, dequantize, mxfp8_dequantize,
                    ROW, T, TENSORS, MlpDesc, MxfError, abi_version, grouped_mlp_bwd, grouped_mlp_fwd,
                    last_error, lib, make_desc, mlp_saved_bytes, mlp_tensor, mlp_workspace_bytes,
                    mxfp8_quantize, pack_w13, profile_begin, profile_end, quantize, query_device,

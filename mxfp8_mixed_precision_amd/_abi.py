@@ -22,6 +22,7 @@ DEV_OK, DEV_BAD_OFFSETS = 0, 1
 CAP_GFX950 = 1
 ROW, COL = 1, 2
 OUT_F32, DEBUG_F32, SERIAL = 1, 2, 4
+DEQ_BF16, DEQ_F32 = 0, 1
 
 # tensor ids (mxf_tensor)
 TENSORS = ["STATUS", "XQ_R", "XS_R", "XQ_C", "XS_C", "W13Q_R", "W13S_R", "W13Q_C", "W13S_C",
@@ -30,7 +31,7 @@ TENSORS = ["STATUS", "XQ_R", "XS_R", "XQ_C", "XS_C", "W13Q_R", "W13S_R", "W13Q_C
            "H13_F32", "DH_F32"]
 T = {name: i for i, name in enumerate(TENSORS)}
 
-EXPORTS = ["mxf_abi_version", "mxf_query_device", "mxf_last_error", "mxfp8_quantize",
+EXPORTS = ["mxf_abi_version", "mxf_query_device", "mxf_last_error", "mxfp8_quantize", "mxfp8_dequantize",
            "mxf_mlp_saved_bytes", "mxf_mlp_workspace_bytes", "mxf_mlp_tensor", "grouped_mlp_fwd",
            "grouped_mlp_bwd", "mxf_read_status", "mxf_profile_begin", "mxf_profile_end",
            "mxf_pack_w13", "mxf_unpack_w13"]
@@ -70,6 +71,7 @@ def lib():
             "mxf_query_device": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(u32)]),
             "mxf_last_error": (ctypes.c_char_p, []),
             "mxfp8_quantize": (ctypes.c_int, [vp, i64, i64, u32, vp, vp, vp, vp, vp]),
+            "mxfp8_dequantize": (ctypes.c_int, [vp, vp, i64, i64, u32, vp, vp]),
             "mxf_mlp_saved_bytes": (sz, [pdesc]),
             "mxf_mlp_workspace_bytes": (sz, [pdesc]),
             "mxf_mlp_tensor": (ctypes.c_int, [pdesc, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
@@ -152,6 +154,24 @@ def quantize(x, mode=ROW | COL, stream=None):
         s_col = torch.empty((cols, max(rows // 32, 0)), dtype=torch.uint8, device=dev)
     mxfp8_quantize(x, rows, cols, mode, q_row, s_row, q_col, s_col, stream)
     return q_row, s_row, q_col, s_col
+
+
+def mxfp8_dequantize(q, s, rows, cols, out_type, out, stream=None):
+    """Raw call: pointers (tensors or ints) and sizes, as in the C header."""
+    _check(lib().mxfp8_dequantize(_ptr(q), _ptr(s), rows, cols, out_type, _ptr(out), _stream(stream)))
+
+
+def dequantize(q, s, out_dtype=None, stream=None):
+    """Decode row-wise MXFP8 codes q [rows, cols] u8 with scales s [rows, ceil(cols/32)] u8
+    (CUDA tensors); allocates and returns a BF16 (default) or FP32 tensor."""
+    import torch
+    out_dtype = out_dtype or torch.bfloat16
+    assert q.dtype == torch.uint8 and q.dim() == 2 and q.is_contiguous()
+    rows, cols = q.shape
+    assert s.dtype == torch.uint8 and s.is_contiguous() and tuple(s.shape) == (rows, -(-cols // 32))
+    out = torch.empty((rows, cols), dtype=out_dtype, device=q.device)
+    mxfp8_dequantize(q, s, rows, cols, DEQ_BF16 if out_dtype == torch.bfloat16 else DEQ_F32, out, stream)
+    return out
 
 
 def make_desc(E, D, F, pad_multiple, m_capacity, flags=0):

@@ -254,6 +254,26 @@ mxf_status mxfp8_quantize(const void* x, int64_t rows, int64_t cols, uint32_t mo
   return MXF_OK;
 }
 
+mxf_status mxfp8_dequantize(const void* q, const void* s, int64_t rows, int64_t cols, uint32_t out_type,
+                            void* out, void* stream) {
+  g_err.clear();
+  if (out_type != MXF_DEQ_BF16 && out_type != MXF_DEQ_F32)
+    return fail(MXF_E_ARG, "out_type = %u: must be MXF_DEQ_BF16 or MXF_DEQ_F32", out_type);
+  if (rows < 0 || cols < 0) return fail(MXF_E_SHAPE, "rows = %lld, cols = %lld: negative", (long long)rows, (long long)cols);
+  if (rows > ((int64_t)1 << 40) / (cols > 0 ? cols : 1))
+    return fail(MXF_E_SHAPE, "rows = %lld, cols = %lld: more than 2^40 elements", (long long)rows, (long long)cols);
+  if (rows == 0 || cols == 0) return MXF_OK;
+  if (!q || !s || !out) return fail(MXF_E_NULL, "q, s or out is NULL");
+  if (!aligned16(q)) return fail(MXF_E_ALIGN, "q is not 16-byte aligned");
+  if (!aligned16(out)) return fail(MXF_E_ALIGN, "out is not 16-byte aligned");
+  mxf_status st = check_device();
+  if (st != MXF_OK) return st;
+  MXF_HIP(timed("dequantize", (hipStream_t)stream, [&] {
+            return mxf_launch_dequantize(q, s, rows, cols, out_type == MXF_DEQ_BF16, out, (hipStream_t)stream);
+          }), "dequantize launch");
+  return MXF_OK;
+}
+
 size_t mxf_mlp_saved_bytes(const mxf_mlp_desc* desc) {
   if (check_desc(desc) != MXF_OK) return 0;
   Layout L;

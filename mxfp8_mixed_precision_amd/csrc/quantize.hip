@@ -182,6 +182,68 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
   }
 }
 
+// ------------------------------------------------------------------ dequantization
+
+// E4M3 code -> its exact fp32 value, from the bit fields (OCP FP8): exponent field 0 is m * 2^-9,
+// S.1111.111 is NaN, otherwise (1 + m/8) * 2^(e-7), i.e. fp32 exponent field e + 120.
+__device__ __forceinline__ float e4m3_f32(uint32_t c) {
+  const uint32_t sign = (c & 0x80u) << 24;
+  const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+  const uint32_t normal = sign | ((e + 120u) << 23) | (m << 20);
+  const uint32_t sub = sign | __float_as_uint((float)m * 0.001953125f);  // m * 2^-9, exact
+  const uint32_t nan = sign | 0x7FC00000u;
+  return __uint_as_float((c & 0x7Fu) == 0x7Fu ? nan : (e == 0 ? sub : normal));
+}
+
+// E8M0 byte -> 2^(b - 127) as fp32: 0x00 is the subnormal 2^-127 (bits 0x00400000), 0xFF is NaN.
+__device__ __forceinline__ float e8m0_f32(uint32_t b) {
+  return __uint_as_float(b == 0xFFu ? 0x7FC00000u : (b == 0u ? 0x00400000u : b << 23));
+}
+
+// out[r, c] = E4M3(q[r, c]) * E8M0(s[r, c / 32]) rounded once to BF16 or FP32. The fp32 product
+// of a 4-significant-bit code and a power of two is exact whenever it is in range (down to
+// 2^-136 = 2^-9 * 2^-127, an fp32 subnormal), so the only rounding is the output conversion.
+// Rows of 16-multiple width take 16 codes per thread; other widths one code per thread.
+template <bool BF16>
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* q, const uint8_t* s, int64_t rows,
+                                                      int64_t cols, void* out) {
+  const int64_t G = (cols + 31) >> 5;  // scale bytes per row (the last group may be short)
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  if ((cols & 15) == 0) {
+    const int64_t cpr = cols >> 4;
+    const int64_t total = rows * cpr;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
+      const int64_t r = t / cpr, c16 = t - r * cpr;
+      const uint4 v = *reinterpret_cast<const uint4*>(q + r * cols + c16 * 16);
+      const float sc = e8m0_f32(s[r * G + (c16 >> 1)]);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      float f[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) f[i] = e4m3_f32((w[i >> 2] >> (8 * (i & 3))) & 0xFFu) * sc;
+      if (BF16) {
+        uint32_t h[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) h[i] = bf16_bits(f[2 * i]) | (bf16_bits(f[2 * i + 1]) << 16);
+        uint4* o = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + r * cols + c16 * 16);
+        o[0] = make_uint4(h[0], h[1], h[2], h[3]);
+        o[1] = make_uint4(h[4], h[5], h[6], h[7]);
+      } else {
+        float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + r * cols + c16 * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = make_float4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]);
+      }
+    }
+  } else {
+    const int64_t total = rows * cols;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
+      const int64_t r = t / cols, c = t - r * cols;
+      const float f = e4m3_f32(q[t]) * e8m0_f32(s[r * G + (c >> 5)]);
+      if (BF16) reinterpret_cast<uint16_t*>(out)[t] = (uint16_t)bf16_bits(f);
+      else reinterpret_cast<float*>(out)[t] = f;
+    }
+  }
+}
+
 // 32-row-block interleave of w1/w3 into [E, 2F, D] and back (BF16, 16-byte copies).
 template <bool PACK>
 __global__ __launch_bounds__(256) void pack13_kernel(const uint16_t* a, const uint16_t* b,
@@ -299,6 +361,20 @@ hipError_t mxf_launch_quant_weights(const void* w, const void* w3, bool pack13, 
   p.sr_rs = 4; p.sr_kbs = 4 * rows;  // 128-k planes per matrix
   p.sc_rs = 4; p.sc_kbs = 4 * cols;
   return mxf::launch_quant(pack13 ? mxf::QK_PACK13 : mxf::QK_PLAIN, 3, p, E, st);
+}
+
+hipError_t mxf_launch_dequantize(const void* q, const void* s, int64_t rows, int64_t cols, bool bf16,
+                                 void* out, hipStream_t st) {
+  const int64_t units = (cols % 16 == 0) ? rows * (cols / 16) : rows * cols;
+  if (units == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((units + 255) / 256, 8192);
+  if (bf16)
+    hipLaunchKernelGGL(mxf::dequant_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st, (const uint8_t*)q,
+                       (const uint8_t*)s, rows, cols, out);
+  else
+    hipLaunchKernelGGL(mxf::dequant_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st, (const uint8_t*)q,
+                       (const uint8_t*)s, rows, cols, out);
+  return hipGetLastError();
 }
 
 hipError_t mxf_launch_pack13(const void* w1, const void* w3, void* w13, int64_t E, int64_t F,

@@ -181,3 +181,17 @@ def test_scale_planes_match_documented_order():
         want = ((torch.arange(n)[:, None, None] * 1000 + torch.arange(R)[None, :, None]) * 100
                 + torch.arange(G)[None, None, :]).reshape(*lead, R, G)
         assert torch.equal(rm, want)
+
+
+def test_dequantize_rejections_before_any_launch():
+    """Argument errors of mxfp8_dequantize are reported without touching a device."""
+    from mxfp8_mixed_precision_amd import _abi
+    def st(*a):
+        with pytest.raises(mx.MxfError) as ei:
+            mx.mxfp8_dequantize(*a, stream=0)
+        return ei.value.status
+    assert st(16, 16, 4, 32, 7, 16) == _abi.E_ARG              # unknown out_type
+    assert st(16, 16, -1, 32, 0, 16) == _abi.E_SHAPE           # negative rows
+    assert st(0, 16, 4, 32, 0, 16) == _abi.E_NULL              # q NULL with work to do
+    assert st(16, 16, 4, 32, 0, 24) == _abi.E_ALIGN            # out not 16-byte aligned
+    mx.mxfp8_dequantize(0, 0, 0, 5, 0, 0, stream=0)            # empty: no-op with NULLs
