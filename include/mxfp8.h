@@ -119,6 +119,10 @@ mxf_status mxfp8_dequantize(const void* q, const void* s, int64_t rows, int64_t 
 #define MXF_OUT_F32 1u     /* y, dx, dw1, dw3, dw2 are FP32 instead of BF16 */
 #define MXF_DEBUG_F32 2u   /* also store the FP32 FC1 output and FP32 dh (FC2 dgrad) in the
                               workspace (tensors MXF_T_H13_F32, MXF_T_DH_F32) */
+#define MXF_UNFUSED 8u     /* the unfused plan, for A/B comparison: FC1 and FC2 dgrad write BF16
+                              (the FC1 output g | u row-major into MXF_T_H13, dh into MXF_T_DH16)
+                              and standalone SwiGLU / dSwiGLU + dual-quantization kernels read
+                              them back; same results as the fused plan. Not with MXF_DEBUG_F32. */
 #define MXF_SERIAL 4u      /* launch every kernel on the caller's stream, one after another
                               (by default independent launches run concurrently on two helper
                               streams forked from and joined into the caller's stream); for
@@ -130,14 +134,14 @@ typedef struct {
   int32_t F;             /* expert hidden dim, multiple of 128 */
   int32_t pad_multiple;  /* 128 or 256: every expert segment is a multiple of this */
   int64_t m_capacity;    /* rows allocated in x/y/dy/dx; multiple of pad_multiple */
-  uint32_t flags;        /* MXF_OUT_F32 | MXF_DEBUG_F32 | MXF_SERIAL */
+  uint32_t flags;        /* MXF_OUT_F32 | MXF_DEBUG_F32 | MXF_SERIAL | MXF_UNFUSED */
 } mxf_mlp_desc;
 
 /* Tensors held in the caller's buffers (for tests and inspection). Region: 0 = workspace,
  * 1 = saved (forward -> backward context). Codes u8, scales u8 (E8M0), h13 BF16.
  *
- * MXF_T_H13 (the BF16-rounded FC1 output g | u, kept for the backward pass) is stored
- * fragment-tiled, in the order the matrix-core accumulators produce and consume it: records
+ * MXF_T_H13 (the BF16-rounded FC1 output g | u, kept for the backward pass) is row-major
+ * [Mcap, 2F] in packed order under MXF_UNFUSED; otherwise it is stored fragment-tiled, in the order the matrix-core accumulators produce and consume it: records
  * of 2048 BF16 values, record R * (F/32) + J holding rows 32R .. 32R+31 and h columns
  * 32J .. 32J+31; inside a record, index ((s * 64) + c + 32 b) * 16 + 4 k + j (s = 0 gate,
  * 1 up; b < 2, c < 32, k < 4, j < 4) holds row 32R + 8k + 4b + j, column 32J + c of the
@@ -164,6 +168,7 @@ typedef enum {
   MXF_T_DHQ_C, MXF_T_DHS_C,                               /* [2F, Mcap], [2F, Mcap/32]     (ws)    */
   MXF_T_H13_F32,                                          /* [Mcap, 2F] FP32 (ws, MXF_DEBUG_F32)   */
   MXF_T_DH_F32,                                           /* [Mcap, F] FP32  (ws, MXF_DEBUG_F32)   */
+  MXF_T_DH16,                                             /* [Mcap, F] BF16  (ws, MXF_UNFUSED)     */
   MXF_T_COUNT
 } mxf_tensor;
 

@@ -6,7 +6,7 @@ this package is its Python binding. ``MlpContext`` allocates the caller-owned
 documented intermediate tensors as views, for tests and inspection.
 """
 from ._abi import (CAP_GFX950, COL, DEBUG_F32, DEQ_BF16, DEQ_F32, DEV_BAD_OFFSETS, DEV_OK, EXPORTS, LIB_PATH,
-                   OUT_F32, SERIAL, dequantize, mxfp8_dequantize,
+                   OUT_F32, SERIAL, UNFUSED, dequantize, mxfp8_dequantize,
                    ROW, T, TENSORS, MlpDesc, MxfError, abi_version, grouped_mlp_bwd, grouped_mlp_fwd,
                    last_error, lib, make_desc, mlp_saved_bytes, mlp_tensor, mlp_workspace_bytes,
                    mxfp8_quantize, pack_w13, profile_begin, profile_end, quantize, query_device,
@@ -28,6 +28,7 @@ _SHAPES = {
     "DHQ_R": lambda E, D, F, M: (M, 2 * F), "DHS_R": lambda E, D, F, M: (M, 2 * F // 32),
     "DHQ_C": lambda E, D, F, M: (2 * F, M), "DHS_C": lambda E, D, F, M: (2 * F, M // 32),
     "H13_F32": lambda E, D, F, M: (M, 2 * F), "DH_F32": lambda E, D, F, M: (M, F),
+    "DH16": lambda E, D, F, M: (M, F),
     "STATUS": lambda E, D, F, M: (1,),
 }
 
@@ -86,7 +87,11 @@ class MlpContext:
         raw = self.view_raw(name)
         shape = _SHAPES[name](self.E, self.D, self.F, self.m_capacity)
         if name == "H13":
+            if self.flags & UNFUSED:
+                return raw.view(torch.bfloat16).view(shape)
             return h13_rowmajor(raw.view(torch.bfloat16), self.F)
+        if name == "DH16":
+            return raw.view(torch.bfloat16).view(shape)
         if name in _PLANE_SCALES:
             return scales_rowmajor(raw, shape)
         if name in ("H13_F32", "DH_F32"):

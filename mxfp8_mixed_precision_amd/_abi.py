@@ -21,14 +21,14 @@ STATUS_NAMES = {OK: "MXF_OK", E_NULL: "MXF_E_NULL", E_SHAPE: "MXF_E_SHAPE", E_AL
 DEV_OK, DEV_BAD_OFFSETS = 0, 1
 CAP_GFX950 = 1
 ROW, COL = 1, 2
-OUT_F32, DEBUG_F32, SERIAL = 1, 2, 4
+OUT_F32, DEBUG_F32, SERIAL, UNFUSED = 1, 2, 4, 8
 DEQ_BF16, DEQ_F32 = 0, 1
 
 # tensor ids (mxf_tensor)
 TENSORS = ["STATUS", "XQ_R", "XS_R", "XQ_C", "XS_C", "W13Q_R", "W13S_R", "W13Q_C", "W13S_C",
            "W2Q_R", "W2S_R", "W2Q_C", "W2S_C", "H13", "HQ_R", "HS_R", "HQ_C", "HS_C",
            "DYQ_R", "DYS_R", "DYQ_C", "DYS_C", "DHQ_R", "DHS_R", "DHQ_C", "DHS_C",
-           "H13_F32", "DH_F32"]
+           "H13_F32", "DH_F32", "DH16"]
 T = {name: i for i, name in enumerate(TENSORS)}
 
 EXPORTS = ["mxf_abi_version", "mxf_query_device", "mxf_last_error", "mxfp8_quantize", "mxfp8_dequantize",

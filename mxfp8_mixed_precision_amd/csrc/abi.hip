@@ -157,8 +157,10 @@ mxf_status check_desc(const mxf_mlp_desc* d) {
                 (long long)d->m_capacity, d->pad_multiple);
   if (d->m_capacity > (int64_t)1 << 30)
     return fail(MXF_E_SHAPE, "m_capacity = %lld: larger than 2^30 rows", (long long)d->m_capacity);
-  if (d->flags & ~(uint32_t)(MXF_OUT_F32 | MXF_DEBUG_F32 | MXF_SERIAL))
+  if (d->flags & ~(uint32_t)(MXF_OUT_F32 | MXF_DEBUG_F32 | MXF_SERIAL | MXF_UNFUSED))
     return fail(MXF_E_ARG, "flags = 0x%x: unknown bits", d->flags);
+  if ((d->flags & MXF_UNFUSED) && (d->flags & MXF_DEBUG_F32))
+    return fail(MXF_E_ARG, "flags = 0x%x: MXF_DEBUG_F32 is not available with MXF_UNFUSED", d->flags);
   return MXF_OK;
 }
 
@@ -205,6 +207,7 @@ void make_layout(const mxf_mlp_desc* d, Layout* L) {
   put(MXF_T_DHQ_C, 0, &bw, 2 * F * M);
   put(MXF_T_DHS_C, 0, &bw, 2 * F * M / 32);
   put(MXF_T_DH_F32, 0, &bw, dbg ? M * F * 4 : 0);
+  put(MXF_T_DH16, 0, &bw, (d->flags & MXF_UNFUSED) ? M * F * 2 : 0);
   L->ws_total = fw > bw ? fw : bw;
 }
 
@@ -373,7 +376,18 @@ mxf_status grouped_mlp_fwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   p.q_r = T(MXF_T_HQ_R); p.s_r = T(MXF_T_HS_R); p.q_c = T(MXF_T_HQ_C); p.s_c = T(MXF_T_HS_C);
   p.sr_rs = 4; p.sr_kbs = 4 * M; p.sc_rs = 4; p.sc_kbs = 4 * F;
   p.dbg = dbg ? (float*)T(MXF_T_H13_F32) : nullptr;
-  MXF_HIP(timed("fc1_swiglu", st, [&] { return mxf_launch_gemm_mgroup(1, p, st); }), "FC1 launch");
+  if (desc->flags & MXF_UNFUSED) {
+    // plain FC1 into the BF16 h13 (row-major), then the standalone SwiGLU + dual quantization
+    mxf::GemmParams q1 = p;
+    q1.C = T(MXF_T_H13); q1.ldc = 2 * F; q1.out_f32 = 0;
+    MXF_HIP(timed("fc1", st, [&] { return mxf_launch_gemm_mgroup(0, q1, st); }), "FC1 launch");
+    MXF_HIP(timed("swiglu_quant", st, [&] {
+              return mxf_launch_swiglu_quant(T(MXF_T_H13), M, F, offs, counts, (int)E, desc->pad_multiple,
+                                             T(MXF_T_HQ_R), T(MXF_T_HS_R), T(MXF_T_HQ_C), T(MXF_T_HS_C), st);
+            }), "SwiGLU quantize launch");
+  } else {
+    MXF_HIP(timed("fc1_swiglu", st, [&] { return mxf_launch_gemm_mgroup(1, p, st); }), "FC1 launch");
+  }
   // FC2
   p.A = T(MXF_T_HQ_R); p.As = T(MXF_T_HS_R); p.lda = F; p.ldas = 4; p.kbsa = 4 * M;
   p.B = T(MXF_T_W2Q_R); p.Bs = T(MXF_T_W2S_R); p.ldb = F; p.ldbs = 4; p.kbsb = 4 * D;
@@ -455,7 +469,18 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
     p.q_r = T(MXF_T_DHQ_R); p.s_r = T(MXF_T_DHS_R); p.q_c = T(MXF_T_DHQ_C); p.s_c = T(MXF_T_DHS_C);
     p.sr_rs = 4; p.sr_kbs = 4 * M; p.sc_rs = 4; p.sc_kbs = 4 * 2 * F;
     p.dbg = dbg ? (float*)T(MXF_T_DH_F32) : nullptr;
-    MXF_HIP(timed("fc2_dgrad_dswiglu", st, [&] { return mxf_launch_gemm_mgroup(2, p, st); }), "FC2 dgrad launch");
+    if (desc->flags & MXF_UNFUSED) {
+      // plain FC2 dgrad into the BF16 dh, then the standalone dSwiGLU + dual quantization
+      p.C = T(MXF_T_DH16); p.ldc = F; p.out_f32 = 0;
+      MXF_HIP(timed("fc2_dgrad", st, [&] { return mxf_launch_gemm_mgroup(0, p, st); }), "FC2 dgrad launch");
+      MXF_HIP(timed("dswiglu_quant", st, [&] {
+                return mxf_launch_dswiglu_quant(T(MXF_T_DH16), T(MXF_T_H13), M, F, offs, counts, (int)E,
+                                                desc->pad_multiple, T(MXF_T_DHQ_R), T(MXF_T_DHS_R), T(MXF_T_DHQ_C),
+                                                T(MXF_T_DHS_C), st);
+              }), "dSwiGLU quantize launch");
+    } else {
+      MXF_HIP(timed("fc2_dgrad_dswiglu", st, [&] { return mxf_launch_gemm_mgroup(2, p, st); }), "FC2 dgrad launch");
+    }
   }
   // FC1 wgrad: dW13[e] = dH13^T X over the expert's tokens, unpacked into dW1 / dW3
   {

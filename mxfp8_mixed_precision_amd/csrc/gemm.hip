@@ -458,11 +458,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
             const int q = 2 * t + s;
-            const float gv = acc[i][2 * jp][q], uv = acc[i][2 * jp + 1][q];
-            gb[s] = bf16_bits(gv);
-            ub[s] = bf16_bits(uv);
-            const float gf = bf16_to_f32(gb[s]), uf = bf16_to_f32(ub[s]);
-            hb[s] = bf16_bits(gf * sigmoid_f(gf) * uf);
+            gb[s] = bf16_bits(acc[i][2 * jp][q]);
+            ub[s] = bf16_bits(acc[i][2 * jp + 1][q]);
+            hb[s] = swiglu_h(gb[s], ub[s]);
           }
           gw[t] = gb[0] | (gb[1] << 16);
           uw[t] = ub[0] | (ub[1] << 16);
@@ -594,13 +592,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
               const int q = 2 * t + s;
-              const float dv = acc[i][j][q];
-              const float dh = bf16_to_f32(bf16_bits(dv));
-              const float gf = bf16_to_f32((gw[t] >> (16 * s)) & 0xFFFFu);
-              const float uf = bf16_to_f32((uw[t] >> (16 * s)) & 0xFFFFu);
-              const float sg = sigmoid_f(gf);
-              og |= bf16_bits(dh * uf * sg * (1.0f + gf * (1.0f - sg))) << (16 * s);
-              ou |= bf16_bits(dh * gf * sg) << (16 * s);
+              uint32_t dg, du;
+              dswiglu(bf16_bits(acc[i][j][q]), (gw[t] >> (16 * s)) & 0xFFFFu, (uw[t] >> (16 * s)) & 0xFFFFu, dg, du);
+              og |= dg << (16 * s);
+              ou |= du << (16 * s);
             }
             dgw[t] = og;
             duw[t] = ou;

@@ -47,6 +47,12 @@ hipError_t mxf_launch_quant_tokens(const void* x, int64_t mcap, int64_t D, const
 hipError_t mxf_launch_quant_weights(const void* w, const void* w3, bool pack13, int64_t E, int64_t rows,
                                     int64_t cols, void* q_r, void* s_r, void* q_c, void* s_c,
                                     hipStream_t st);
+hipError_t mxf_launch_swiglu_quant(const void* h13, int64_t mcap, int64_t F, const int32_t* offs,
+                                   const int32_t* counts, int E, int pad, void* q_r, void* s_r, void* q_c,
+                                   void* s_c, hipStream_t st);
+hipError_t mxf_launch_dswiglu_quant(const void* dh, const void* h13, int64_t mcap, int64_t F, const int32_t* offs,
+                                    const int32_t* counts, int E, int pad, void* q_r, void* s_r, void* q_c,
+                                    void* s_c, hipStream_t st);
 hipError_t mxf_launch_dequantize(const void* q, const void* s, int64_t rows, int64_t cols, bool bf16,
                                  void* out, hipStream_t st);
 hipError_t mxf_launch_pack13(const void* w1, const void* w3, void* w13, int64_t E, int64_t F,

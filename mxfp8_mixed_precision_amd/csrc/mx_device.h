@@ -140,6 +140,21 @@ __device__ __forceinline__ float sigmoid_f(float g) {
   return g >= 0.0f ? r : e * r;
 }
 
+// The SwiGLU rounding points (shared by the fused GEMM epilogues and the standalone kernels, so
+// both compute bit-identical values): from the BF16 g, u of the FC1 output,
+// h = BF16(silu(g) * u); in backward, from BF16 dh, dG = BF16(dh u s (1 + g (1 - s))) and
+// dU = BF16(dh g s) with s = sigmoid(g). Arguments and results are BF16 bit patterns.
+__device__ __forceinline__ uint32_t swiglu_h(uint32_t gb, uint32_t ub) {
+  const float gf = bf16_to_f32(gb), uf = bf16_to_f32(ub);
+  return bf16_bits(gf * sigmoid_f(gf) * uf);
+}
+__device__ __forceinline__ void dswiglu(uint32_t dhb, uint32_t gb, uint32_t ub, uint32_t& dg, uint32_t& du) {
+  const float dh = bf16_to_f32(dhb), gf = bf16_to_f32(gb), uf = bf16_to_f32(ub);
+  const float sg = sigmoid_f(gf);
+  dg = bf16_bits(dh * uf * sg * (1.0f + gf * (1.0f - sg)));
+  du = bf16_bits(dh * gf * sg);
+}
+
 // Device-side check of the token-offset contract, done by one whole wavefront; every lane
 // returns the same answer. offs [E+1], counts [E] or null.
 __device__ __forceinline__ bool offsets_valid(const int32_t* offs, const int32_t* counts, int E,

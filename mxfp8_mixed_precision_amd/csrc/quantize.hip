@@ -22,11 +22,14 @@
 
 namespace mxf {
 
-enum QuantKind { QK_PLAIN = 0, QK_MASKED = 1, QK_PACK13 = 2 };
+// QK_SWIGLU / QK_DSWIGLU are the standalone SwiGLU / dSwiGLU + dual-quantization kernels of the
+// unfused plan: they read the BF16 FC1 output (and dh) that the plain GEMMs wrote, apply the
+// same rounding points as the fused epilogues, and quantize like QK_MASKED.
+enum QuantKind { QK_PLAIN = 0, QK_MASKED = 1, QK_PACK13 = 2, QK_SWIGLU = 3, QK_DSWIGLU = 4 };
 
 struct QuantParams {
   const uint16_t* src;   // BF16 bits; QK_PACK13: w1 [E, F, D]
-  const uint16_t* src2;  // QK_PACK13: w3 [E, F, D]
+  const uint16_t* src2;  // QK_PACK13: w3 [E, F, D]; QK_DSWIGLU: g | u [rows, cols] (packed order)
   int64_t rows, cols;    // logical matrix per batch entry (QK_PACK13: rows = 2F, cols = D)
   int64_t src_bs;        // elements between batch entries of src / src2
   uint8_t* q_r;
@@ -68,11 +71,11 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
   int64_t valid_end = p.rows;  // rows at or past this read as zero
   const uint16_t* src = p.src + e * p.src_bs;
   int64_t src_row0 = rw0;      // source row of the wavefront's first row
-  if (KIND == QK_MASKED) {
+  if (KIND == QK_MASKED || KIND == QK_SWIGLU || KIND == QK_DSWIGLU) {
     // every wavefront reads the offsets (same answers everywhere); mend and the block's rows
     // are multiples of 128, so a block is either wholly before offs[E] or wholly past it
     const Offsets ofs = read_offsets(p.offs, p.counts, p.E, p.pad, p.rows);
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *p.status = ofs.ok ? 0 : 1;
+    if (KIND == QK_MASKED && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *p.status = ofs.ok ? 0 : 1;
     if (!ofs.ok) return;
     if (row0 >= ofs.mend) return;  // tail rows: never read or written
     const int ex = ofs.expert(rw0);
@@ -90,7 +93,33 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int64_t r = r0 + j;
-    if (colok && r < rend) {
+    if (colok && r < rend && KIND == QK_SWIGLU) {
+      // h column col of row r: gate at packed column 64 (col / 32) + col % 32, up 32 further
+      const uint16_t* row = src + r * (2 * p.cols) + (col >> 5) * 64 + (col & 31);
+      const uint4 gv = *reinterpret_cast<const uint4*>(row);
+      const uint4 uv = *reinterpret_cast<const uint4*>(row + 32);
+      const uint32_t g4[4] = {gv.x, gv.y, gv.z, gv.w}, u4[4] = {uv.x, uv.y, uv.z, uv.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        x[j][k] = swiglu_h(g4[k] & 0xFFFFu, u4[k] & 0xFFFFu) | (swiglu_h(g4[k] >> 16, u4[k] >> 16) << 16);
+    } else if (colok && r < rend && KIND == QK_DSWIGLU) {
+      // packed column col: dG (col % 64 < 32) or dU of dh column 32 (col / 64) + col % 32
+      const int64_t F = p.cols >> 1;
+      const int64_t j32 = col >> 6, cc = col & 31;
+      const uint4 dv = *reinterpret_cast<const uint4*>(src + r * F + j32 * 32 + cc);
+      const uint16_t* gu = p.src2 + r * p.cols + j32 * 64 + cc;
+      const uint4 gv = *reinterpret_cast<const uint4*>(gu);
+      const uint4 uv = *reinterpret_cast<const uint4*>(gu + 32);
+      const uint32_t d4[4] = {dv.x, dv.y, dv.z, dv.w}, g4[4] = {gv.x, gv.y, gv.z, gv.w}, u4[4] = {uv.x, uv.y, uv.z, uv.w};
+      const bool up = (col & 32) != 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint32_t dg0, du0, dg1, du1;
+        dswiglu(d4[k] & 0xFFFFu, g4[k] & 0xFFFFu, u4[k] & 0xFFFFu, dg0, du0);
+        dswiglu(d4[k] >> 16, g4[k] >> 16, u4[k] >> 16, dg1, du1);
+        x[j][k] = up ? (du0 | (du1 << 16)) : (dg0 | (dg1 << 16));
+      }
+    } else if (colok && r < rend) {
       const uint4 v = *reinterpret_cast<const uint4*>(src + (src_row0 + 8 * s + j) * p.cols + col);
       x[j][0] = v.x; x[j][1] = v.y; x[j][2] = v.z; x[j][3] = v.w;
     } else {
@@ -286,6 +315,10 @@ static hipError_t launch_quant(int kind, uint32_t mode, const QuantParams& p, in
     else MXF_QLAUNCH(QK_PLAIN, false, true);
   } else if (kind == QK_MASKED) {
     MXF_QLAUNCH(QK_MASKED, true, true);
+  } else if (kind == QK_SWIGLU) {
+    MXF_QLAUNCH(QK_SWIGLU, true, true);
+  } else if (kind == QK_DSWIGLU) {
+    MXF_QLAUNCH(QK_DSWIGLU, true, true);
   } else {
     MXF_QLAUNCH(QK_PACK13, true, true);
   }
@@ -335,6 +368,41 @@ hipError_t mxf_launch_quant_tokens(const void* x, int64_t mcap, int64_t D, const
   p.pad = pad;
   p.status = status;
   return mxf::launch_quant(mxf::QK_MASKED, 3, p, 1, st);
+}
+
+// Unfused plan: h = SwiGLU of the BF16 FC1 output h13 [mcap, 2F] (packed gate/up order),
+// dual-quantized like the token operands (hq_r [mcap, F], hq_c [F, mcap], 128-k plane scales).
+hipError_t mxf_launch_swiglu_quant(const void* h13, int64_t mcap, int64_t F, const int32_t* offs,
+                                   const int32_t* counts, int E, int pad, void* q_r, void* s_r, void* q_c,
+                                   void* s_c, hipStream_t st) {
+  mxf::QuantParams p = {};
+  p.src = (const uint16_t*)h13;
+  p.rows = mcap;
+  p.cols = F;
+  p.q_r = (uint8_t*)q_r; p.s_r = (uint8_t*)s_r; p.q_c = (uint8_t*)q_c; p.s_c = (uint8_t*)s_c;
+  p.ldc = mcap;
+  p.sr_rs = 4; p.sr_kbs = 4 * mcap;
+  p.sc_rs = 4; p.sc_kbs = 4 * F;
+  p.offs = offs; p.counts = counts; p.E = E; p.pad = pad;
+  return mxf::launch_quant(mxf::QK_SWIGLU, 3, p, 1, st);
+}
+
+// Unfused plan: dH13 = pack(dG, dU) from the BF16 dh [mcap, F] and h13 [mcap, 2F], dual-quantized
+// (dhq_r [mcap, 2F], dhq_c [2F, mcap], 128-k plane scales).
+hipError_t mxf_launch_dswiglu_quant(const void* dh, const void* h13, int64_t mcap, int64_t F, const int32_t* offs,
+                                    const int32_t* counts, int E, int pad, void* q_r, void* s_r, void* q_c,
+                                    void* s_c, hipStream_t st) {
+  mxf::QuantParams p = {};
+  p.src = (const uint16_t*)dh;
+  p.src2 = (const uint16_t*)h13;
+  p.rows = mcap;
+  p.cols = 2 * F;
+  p.q_r = (uint8_t*)q_r; p.s_r = (uint8_t*)s_r; p.q_c = (uint8_t*)q_c; p.s_c = (uint8_t*)s_c;
+  p.ldc = mcap;
+  p.sr_rs = 4; p.sr_kbs = 4 * mcap;
+  p.sc_rs = 4; p.sc_kbs = 4 * 2 * F;
+  p.offs = offs; p.counts = counts; p.E = E; p.pad = pad;
+  return mxf::launch_quant(mxf::QK_DSWIGLU, 3, p, 1, st);
 }
 
 // Dual quantization of a batch of E weight matrices [rows, cols], scales in 128-k planes per

@@ -240,6 +240,60 @@ def test_serial_launches_match_concurrent(tiny):
         assert torch.equal(r[k], r2[k]), k
 
 
+@pytest.mark.parametrize("case", [
+    None,                                                             # tiny, pad 128
+    dict(counts=[0, 200, 0, 57], E=4, D=256, F=384, pad=256),        # zero-token experts, pad 256
+    dict(counts=[300, 77, 515], E=3, D=384, F=256, pad=128),         # ragged
+])
+def test_unfused_plan_matches_fused(case):
+    """The unfused plan (plain GEMMs writing BF16, standalone SwiGLU / dSwiGLU + dual
+    quantization kernels) computes the same rounding points as the fused epilogues: outputs
+    and every saved or intermediate tensor are bit-identical."""
+    mx = require_gpu()
+    if case is None:
+        prob = workloads.mlp_problem("tiny", m_capacity=1536)
+    else:
+        prob = workloads.mlp_problem(None, seed=5, counts=case["counts"], E=case["E"], D=case["D"], F=case["F"],
+                                     pad=case["pad"], m_capacity=workloads.padded_offsets(case["counts"], case["pad"])[-1])
+    ra = run_mlp(mx, prob, mx.OUT_F32)
+    rb = run_mlp(mx, prob, mx.OUT_F32 | mx.UNFUSED)
+    m = prob["offs"][-1]
+    for k in ("dw1", "dw3", "dw2"):
+        assert torch.equal(ra[k], rb[k]), k
+    for k in ("y", "dx"):
+        assert torch.equal(ra[k][:m], rb[k][:m]), k
+
+
+def test_unfused_plan_intermediates_match_fused():
+    """Saved h13 and the dual-quantized h and dH13 (codes and scales) of both plans agree."""
+    mx = require_gpu()
+    prob = workloads.mlp_problem("tiny", m_capacity=1536)
+    out = {}
+    for plan, flags in (("fused", 0), ("unfused", mx.UNFUSED)):
+        E, D, F, pad, mcap = prob["E"], prob["D"], prob["F"], prob["pad"], prob["m_capacity"]
+        ctx = mx.MlpContext(E, D, F, pad, mcap, flags=flags)
+        offs = torch.tensor(prob["offs"], dtype=torch.int32, device="cuda")
+        cnt = torch.tensor(prob["counts"], dtype=torch.int32, device="cuda")
+        x, w1, w3, w2, dy = (prob[k].cuda() for k in ("x", "w1", "w3", "w2", "dy"))
+        y = torch.empty((mcap, D), dtype=torch.bfloat16, device="cuda")
+        dx = torch.empty_like(y)
+        dw1 = torch.empty((E, F, D), dtype=torch.bfloat16, device="cuda")
+        dw3, dw2 = torch.empty_like(dw1), torch.empty((E, D, F), dtype=torch.bfloat16, device="cuda")
+        ctx.fwd(offs, cnt, x, w1, w3, w2, y)
+        ctx.bwd(offs, cnt, dy, dx, dw1, dw3, dw2)
+        torch.cuda.synchronize()
+        out[plan] = {n: ctx.view(n).cpu() for n in ("H13", "HQ_R", "HS_R", "HQ_C", "HS_C", "DHQ_R", "DHS_R",
+                                                     "DHQ_C", "DHS_C")}
+    m = prob["offs"][-1]
+    a, b = out["fused"], out["unfused"]
+    for n in ("H13", "HQ_R", "HS_R", "DHQ_R", "DHS_R"):
+        assert torch.equal(a[n][:m].view(torch.uint8), b[n][:m].view(torch.uint8)), n
+    for n in ("HQ_C", "DHQ_C"):
+        assert torch.equal(a[n][:, :m], b[n][:, :m]), n
+    for n in ("HS_C", "DHS_C"):
+        assert torch.equal(a[n][:, :m // 32], b[n][:, :m // 32]), n
+
+
 def test_nan_poisoned_pad_and_tail(tiny):
     mx, prob, r = tiny
     poisoned = workloads.mlp_problem("tiny", m_capacity=1536, pad_fill=float("nan"), tail_fill=float("nan"))
