@@ -263,6 +263,7 @@ def main():
         "serial_ms_per_step": round((t3 - t2) * 1e3 / args.steps, 4),
     }
 
+    out["plans"] = bench_plans(mx, torch, dev, args, sets, counts, E, D, F, y, dx, dw1, dw3, dw2)
     if not args.no_quant:
         out["quantize"] = bench_quantize(mx, torch, dev, args)
         out["dequantize"] = bench_dequantize(mx, torch, dev, args)
@@ -303,6 +304,40 @@ def bench_quantize(mx, torch, dev, args):
             "roofline": {"bound": "hbm", "kernel": "quantize", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": traffic_for("quantize", "quant")}}
+
+
+def bench_plans(mx, torch, dev, args, sets, counts, E, D, F, y, dx, dw1, dw3, dw2):
+    """Fused vs unfused plan (MXF_UNFUSED: plain GEMMs + standalone SwiGLU / dSwiGLU
+    quantization kernels), each at pad_multiple 256 and 128, on the same routed rows."""
+    import workloads
+    m_real = sum(counts)
+    res = {}
+    for plan, flags in (("fused", 0), ("unfused", mx.UNFUSED)):
+        for pad in (256, 128):
+            offs = workloads.padded_offsets(counts, pad)
+            mcap = offs[-1]
+            offs_t = torch.tensor(offs, dtype=torch.int32, device=dev)
+            counts_t = torch.tensor(counts, dtype=torch.int32, device=dev)
+            ctx = mx.MlpContext(E, D, F, pad, mcap, flags=flags, device=dev)
+
+            def step(i):
+                s = sets[i % len(sets)]
+                ctx.fwd(offs_t, counts_t, s["x"], s["w1"], s["w3"], s["w2"], y)
+                ctx.bwd(offs_t, counts_t, s["dy"], dx, dw1, dw3, dw2)
+
+            for i in range(3):
+                step(i)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(args.steps):
+                step(i)
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) * 1e3 / args.steps
+            res[f"{plan}_pad{pad}"] = {"ms_per_step": round(ms, 4), "m_padded": mcap,
+                                       "useful_tflops": round(18.0 * m_real * D * F / (ms / 1e3) / 1e12, 1),
+                                       "launches_fwd_bwd": "5 + 5" if plan == "fused" else "6 + 6"}
+            del ctx
+    return res
 
 
 def bench_dequantize(mx, torch, dev, args):
