@@ -119,6 +119,8 @@ def main():
     ap.add_argument("--no-quant", action="store_true", help="skip the standalone quantizer measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference kernel for HBM byte counters)")
+    ap.add_argument("--no-plans", action="store_true",
+                    help="skip the fused/unfused plan A/B (profiling runs: it launches other kernels)")
     ap.add_argument("--serial", action="store_true",
                     help="time with MXF_SERIAL too (every kernel alone; for profiler runs)")
     ap.add_argument("--quant-only", action="store_true",
@@ -263,7 +265,8 @@ def main():
         "serial_ms_per_step": round((t3 - t2) * 1e3 / args.steps, 4),
     }
 
-    out["plans"] = bench_plans(mx, torch, dev, args, sets, counts, E, D, F, y, dx, dw1, dw3, dw2)
+    if not args.no_plans:
+        out["plans"] = bench_plans(mx, torch, dev, args, sets, counts, E, D, F, y, dx, dw1, dw3, dw2)
     if not args.no_quant:
         out["quantize"] = bench_quantize(mx, torch, dev, args)
         out["dequantize"] = bench_dequantize(mx, torch, dev, args)
