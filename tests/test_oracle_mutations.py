@@ -74,3 +74,42 @@ def test_rounding_mutations_are_caught(monkeypatch):
 
     monkeypatch.setattr(tq, "e4m3_rne_sat", no_sat)
     assert _fails(tq.test_brute_force_all_bf16_against_torch_cast, 127)
+
+
+def test_dispatch_mutations_are_caught(monkeypatch):
+    import test_oracle_dispatch as td
+    from oracle import dispatch
+    good_plan, good_perm = dispatch.route_plan, dispatch.permute
+
+    def reversed_segments(ids, E, pad, cap):
+        p = good_plan(ids, E, pad, cap)
+        ra = p["row_assign"].copy()
+        for e in range(E):
+            a, c = int(p["offs"][e]), int(p["counts"][e])
+            ra[a:a + c] = ra[a:a + c][::-1].copy()
+        ar = p["assign_row"].copy()
+        ar[ra[ra >= 0]] = np.nonzero(ra >= 0)[0]
+        return dict(p, row_assign=ra, assign_row=ar)
+
+    def always_one_more_block(ids, E, pad, cap):
+        p = good_plan(ids, E, pad, cap)
+        offs = np.concatenate([[0], np.cumsum(np.diff(p["offs"]) + np.where(p["counts"] % pad == 0, pad, 0))])
+        return dict(p, offs=offs)
+
+    for m in (reversed_segments, always_one_more_block):
+        monkeypatch.setattr(dispatch, "route_plan", m)
+        assert _fails(td.test_hand_worked_dispatch) or _fails(td.test_plan_invariants_and_stable_order, 1, 5000, 16, 256)
+        assert _fails(td.test_tiny_workload_layout_is_the_dispatch_of_its_tokens) or m is always_one_more_block
+    monkeypatch.setattr(dispatch, "route_plan", good_plan)
+
+    def k_major(x, ra, k, m):          # assignments read as a = k * tokens + t (transposed routing)
+        x = np.asarray(x)
+        out = np.zeros((m, x.shape[1]), dtype=x.dtype)
+        for r, a in enumerate(ra):
+            if a >= 0:
+                out[r] = x[a % x.shape[0]]
+        return out
+
+    monkeypatch.setattr(dispatch, "permute", k_major)
+    assert _fails(td.test_tiny_workload_layout_is_the_dispatch_of_its_tokens)
+    assert _fails(td.test_hand_worked_dispatch)

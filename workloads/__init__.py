@@ -130,7 +130,7 @@ def mlp_problem(name="tiny", seed=42, device="cpu", m_capacity=None, pad_fill=0.
     if name == "tiny" and counts == KNOWN_COUNTS["tiny"]:
         # each token row appears once in every expert it was routed to
         choice = tiny_routing()
-        tok = randn_bf16((choice.shape[0], D), 1.0, gen, device)
+        tok = randn_bf16((choice.shape[0], D), 1.0, gen, device)  # same draw as routed_tokens("tiny")
         for e in range(E):
             ids = torch.from_numpy(np.nonzero((choice == e).any(axis=1))[0]).to(device)
             x[offs[e]:offs[e] + counts[e]] = tok[ids]
@@ -148,6 +148,32 @@ def mlp_problem(name="tiny", seed=42, device="cpu", m_capacity=None, pad_fill=0.
         dy[offs[e] + counts[e]:offs[e + 1]] = pad_fill
     return dict(x=x, w1=w1, w3=w3, w2=w2, dy=dy, offs=offs, counts=list(counts), E=E, D=D, F=F,
                 pad=pad, m_capacity=mcap)
+
+
+DISPATCH_TOPK = {"tiny": 2, "dense": 1, "dsv3_rank": 6, "large_expert": 8}
+
+
+def routed_tokens(name="tiny", seed=42, device="cpu"):
+    """Token rows and their expert choices before dispatch: (x_tokens [T, D] bf16,
+    expert_idx [T, topk] int32 numpy).
+
+    tiny: the 512 tokens and top-2 choices that mlp_problem("tiny") lays out (same
+    generator draw). Other workloads: T = routed rows / topk tokens ~N(0,1), the expert ids
+    a seeded random permutation of each expert repeated counts[e] times (so a token may
+    name an expert twice), reshaped [T, topk].
+    """
+    cfg = MLP_CONFIGS[name]
+    counts = expert_counts(name)
+    topk = DISPATCH_TOPK[name]
+    if name == "tiny":
+        idx = tiny_routing().astype(np.int32)
+    else:
+        flat = np.repeat(np.arange(cfg["E"], dtype=np.int32), counts)
+        assert flat.size % topk == 0
+        idx = np.random.default_rng(seed).permutation(flat).reshape(-1, topk)
+    gen = _gen(seed, device)
+    x = randn_bf16((idx.shape[0], cfg["D"]), 1.0, gen, device)
+    return x, idx
 
 
 def quant_matrix(rows=QUANT_CONFIG["rows"], cols=QUANT_CONFIG["cols"], seed=42, device="cpu"):
