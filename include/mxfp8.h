@@ -57,7 +57,7 @@ typedef enum {
   MXF_OK = 0,
   MXF_E_NULL = 1,      /* a required pointer is NULL */
   MXF_E_SHAPE = 2,     /* a dimension is negative, not a required multiple, or too large */
-  MXF_E_ALIGN = 3,     /* a pointer is not 16-byte aligned */
+  MXF_E_ALIGN = 3,     /* a pointer is not aligned as required (16 bytes; int32 arrays 4) */
   MXF_E_DEVICE = 4,    /* the current device is not a gfx950 GPU */
   MXF_E_ARG = 5,       /* an enum/flag argument is out of range */
   MXF_E_HIP = 6        /* the HIP runtime reported an error (message in mxf_last_error) */
@@ -66,6 +66,8 @@ typedef enum {
 /* Device-side status word values (mxf_read_status). */
 #define MXF_DEV_OK 0
 #define MXF_DEV_BAD_OFFSETS 1   /* offs/counts violate the layout contract; no output was written */
+#define MXF_DEV_BAD_EXPERT 2    /* mxf_route_plan: an expert id outside [0, E); it was dropped */
+#define MXF_DEV_OVERFLOW 3      /* mxf_route_plan: the padded layout exceeds m_capacity */
 
 /* ABI version of the loaded library; equals MXF_ABI_VERSION of the header it was built with. */
 int mxf_abi_version(void);
@@ -123,6 +125,9 @@ mxf_status mxfp8_dequantize(const void* q, const void* s, int64_t rows, int64_t 
                               (the FC1 output g | u row-major into MXF_T_H13, dh into MXF_T_DH16)
                               and standalone SwiGLU / dSwiGLU + dual-quantization kernels read
                               them back; same results as the fused plan. Not with MXF_DEBUG_F32. */
+#define MXF_X_QUANTIZED 16u /* grouped_mlp_fwd: X's dual codes were already written into saved /
+                              workspace by mxfp8_dispatch_quantize (same desc, offs, counts);
+                              x is not read and may be NULL */
 #define MXF_SERIAL 4u      /* launch every kernel on the caller's stream, one after another
                               (by default independent launches run concurrently on two helper
                               streams forked from and joined into the caller's stream); for
@@ -134,7 +139,7 @@ typedef struct {
   int32_t F;             /* expert hidden dim, multiple of 128 */
   int32_t pad_multiple;  /* 128 or 256: every expert segment is a multiple of this */
   int64_t m_capacity;    /* rows allocated in x/y/dy/dx; multiple of pad_multiple */
-  uint32_t flags;        /* MXF_OUT_F32 | MXF_DEBUG_F32 | MXF_SERIAL | MXF_UNFUSED */
+  uint32_t flags;        /* MXF_OUT_F32 | MXF_DEBUG_F32 | MXF_SERIAL | MXF_UNFUSED | MXF_X_QUANTIZED */
 } mxf_mlp_desc;
 
 /* Tensors held in the caller's buffers (for tests and inspection). Region: 0 = workspace,
@@ -209,6 +214,55 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc /* host */, const int32_t* o
                            const int32_t* counts, const void* dy, const void* saved, void* dx,
                            void* dw1, void* dw3, void* dw2, void* workspace, void* stream);
 
+/* ------------------------------------------------------------------ dispatch */
+
+/* Dispatch of routed tokens into the padded expert-major layout the MLP consumes: every
+ * expert's rows form one segment whose length is a multiple of pad_multiple, pad rows zero
+ * (torchtitan PR #12 "Wire the fully-fused grouped-GEMM MXFP8 plan behind fusion_plan",
+ * section "What it adds": the padded dispatcher that the kernels' per-expert alignment
+ * requires; torchtitan PR #2, section "Summary"). Inside a segment, rows follow the
+ * assignment index a = t * topk + k (token t's k-th choice), so the layout is unique.
+ *
+ * Routing plan. expert_idx: int32 [tokens, topk], each in [0, E) (a token may name an expert
+ * more than once: each assignment gets its own row). Outputs (int32, caller-owned):
+ *   offs [E+1], counts [E] -- as grouped_mlp_fwd takes them (counts[e] = assignments routed to
+ *     e, offs[e+1] - offs[e] = counts[e] rounded up to pad_multiple);
+ *   row_assign [m_capacity] -- assignment held by row r, -1 for a pad row; rows at or past
+ *     offs[E] are not written;
+ *   assign_row [tokens * topk] -- row of assignment a, or -1 (dropped, or past m_capacity).
+ *   status (may be NULL): MXF_DEV_OK; MXF_DEV_BAD_EXPERT if an id is outside [0, E) (the
+ *     assignment is dropped, the rest is placed); else MXF_DEV_OVERFLOW if offs[E] >
+ *     m_capacity (offs and counts still describe the whole layout; rows past the capacity
+ *     are not written, so the MLP's offsets check rejects these offs).
+ * tokens * topk <= 2^30, 1 <= topk <= 64, 1 <= E <= 1024, 1 <= pad_multiple <= 4096,
+ * 0 <= m_capacity <= 2^30; int32 pointers 4-byte aligned. One workgroup does the whole plan
+ * (a few microseconds at tens of thousands of assignments).
+ * Errors: MXF_E_NULL, MXF_E_SHAPE, MXF_E_ALIGN, MXF_E_DEVICE, MXF_E_HIP. */
+mxf_status mxf_route_plan(const int32_t* expert_idx, int64_t tokens, int32_t topk, int32_t E,
+                          int32_t pad_multiple, int64_t m_capacity, int32_t* offs, int32_t* counts,
+                          int32_t* row_assign, int32_t* assign_row, int32_t* status, void* stream);
+
+/* BF16 permute: x_out [m_capacity, D] row r (r < min(offs[E], m_capacity)) = x_tokens
+ * [tokens, D] row row_assign[r] / topk, or zeros where row_assign[r] is -1 (or outside
+ * [0, tokens * topk)). Rows at or past offs[E] are not written. offs and row_assign as
+ * written by mxf_route_plan. D % 8 == 0; x_tokens, x_out 16-byte aligned.
+ * Errors: MXF_E_NULL, MXF_E_SHAPE, MXF_E_ALIGN, MXF_E_DEVICE, MXF_E_HIP. */
+mxf_status mxf_dispatch_permute(const void* x_tokens, int64_t tokens, int32_t topk, int64_t D, int32_t E,
+                                const int32_t* offs, const int32_t* row_assign, int64_t m_capacity,
+                                void* x_out, void* stream);
+
+/* Fused dispatch + Q_X: writes the MLP's X operand (MXF_T_XQ_R/XS_R in workspace,
+ * MXF_T_XQ_C/XS_C in saved) straight from the token rows, bit-identical to what
+ * grouped_mlp_fwd computes from the permuted BF16 matrix, and sets the workspace status word
+ * from the offsets check. Follow it with grouped_mlp_fwd under MXF_X_QUANTIZED (same desc
+ * otherwise, same offs and counts). x_tokens [tokens, desc->D] BF16, 16-byte aligned;
+ * offs, counts and row_assign as written by mxf_route_plan with desc's E, pad_multiple and
+ * m_capacity. Errors: as grouped_mlp_fwd plus MXF_E_SHAPE for tokens / topk. */
+mxf_status mxfp8_dispatch_quantize(const mxf_mlp_desc* desc /* host */, const int32_t* offs,
+                                   const int32_t* counts, const int32_t* row_assign,
+                                   const void* x_tokens, int64_t tokens, int32_t topk, void* saved,
+                                   void* workspace, void* stream);
+
 /* Synchronises `stream` and copies the device status word of the last fwd/bwd call that
  * used `workspace` into *device_status (MXF_DEV_OK or MXF_DEV_BAD_OFFSETS). */
 mxf_status mxf_read_status(const void* workspace, void* stream, int32_t* device_status /* host */);
@@ -222,7 +276,8 @@ mxf_status mxf_read_status(const void* workspace, void* stream, int32_t* device_
  * returns, per kernel name, the number of launches and their summed duration in ms; it
  * fills at most max_out entries and sets *n_out to the number filled, then stops recording.
  * Kernel names: quant_w13, quant_w2, quant_x, fc1_swiglu, fc2, quant_dy, fc2_dgrad_dswiglu,
- * fc2_wgrad, fc1_dgrad, fc1_wgrad, quantize.
+ * fc2_wgrad, fc1_dgrad, fc1_wgrad (MXF_UNFUSED: fc1, swiglu_quant, fc2_dgrad, dswiglu_quant),
+ * quantize, dequantize, route_plan, permute, dispatch_quant_x.
  * Errors: MXF_E_ARG (capacity < 1 or > 1<<20, or end without begin), MXF_E_NULL, MXF_E_HIP. */
 typedef struct {
   char name[32];

@@ -5,8 +5,9 @@ this package is its Python binding. ``MlpContext`` allocates the caller-owned
 ``saved`` and ``workspace`` buffers with torch and exposes the library's
 documented intermediate tensors as views, for tests and inspection.
 """
-from ._abi import (CAP_GFX950, COL, DEBUG_F32, DEQ_BF16, DEQ_F32, DEV_BAD_OFFSETS, DEV_OK, EXPORTS, LIB_PATH,
-                   OUT_F32, SERIAL, UNFUSED, dequantize, mxfp8_dequantize,
+from ._abi import (CAP_GFX950, COL, DEBUG_F32, DEQ_BF16, DEQ_F32, DEV_BAD_EXPERT, DEV_BAD_OFFSETS, DEV_OK,
+                   DEV_OVERFLOW, EXPORTS, LIB_PATH, OUT_F32, SERIAL, UNFUSED, X_QUANTIZED, dequantize,
+                   mxf_dispatch_permute, mxf_route_plan, mxfp8_dequantize, mxfp8_dispatch_quantize, route_plan,
                    ROW, T, TENSORS, MlpDesc, MxfError, abi_version, grouped_mlp_bwd, grouped_mlp_fwd,
                    last_error, lib, make_desc, mlp_saved_bytes, mlp_tensor, mlp_workspace_bytes,
                    mxfp8_quantize, pack_w13, profile_begin, profile_end, quantize, query_device,
@@ -66,6 +67,7 @@ class MlpContext:
         import torch
         self.E, self.D, self.F, self.pad, self.m_capacity, self.flags = E, D, F, pad_multiple, m_capacity, flags
         self.desc = make_desc(E, D, F, pad_multiple, m_capacity, flags)
+        self.desc_xq = make_desc(E, D, F, pad_multiple, m_capacity, flags | X_QUANTIZED)
         nsaved = mlp_saved_bytes(self.desc)
         nws = mlp_workspace_bytes(self.desc)
         if nsaved == 0 or nws == 0:
@@ -101,7 +103,14 @@ class MlpContext:
         return raw.view(shape)
 
     def fwd(self, offs, counts, x, w1, w3, w2, y, stream=None):
-        grouped_mlp_fwd(self.desc, offs, counts, x, w1, w3, w2, y, self.saved, self.workspace, stream)
+        """Forward; x=None means X was already quantized by dispatch_quantize (MXF_X_QUANTIZED)."""
+        desc = self.desc if x is not None else self.desc_xq
+        grouped_mlp_fwd(desc, offs, counts, x, w1, w3, w2, y, self.saved, self.workspace, stream)
+
+    def dispatch_quantize(self, offs, counts, row_assign, x_tokens, topk, stream=None):
+        """Fused dispatch + dual quantization of X from the token rows x_tokens [tokens, D]."""
+        mxfp8_dispatch_quantize(self.desc, offs, counts, row_assign, x_tokens, x_tokens.shape[0], topk, self.saved,
+                                self.workspace, stream)
 
     def bwd(self, offs, counts, dy, dx, dw1, dw3, dw2, stream=None):
         grouped_mlp_bwd(self.desc, offs, counts, dy, self.saved, dx, dw1, dw3, dw2, self.workspace, stream)

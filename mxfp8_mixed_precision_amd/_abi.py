@@ -18,10 +18,10 @@ ABI_VERSION = 1
 OK, E_NULL, E_SHAPE, E_ALIGN, E_DEVICE, E_ARG, E_HIP = range(7)
 STATUS_NAMES = {OK: "MXF_OK", E_NULL: "MXF_E_NULL", E_SHAPE: "MXF_E_SHAPE", E_ALIGN: "MXF_E_ALIGN",
                 E_DEVICE: "MXF_E_DEVICE", E_ARG: "MXF_E_ARG", E_HIP: "MXF_E_HIP"}
-DEV_OK, DEV_BAD_OFFSETS = 0, 1
+DEV_OK, DEV_BAD_OFFSETS, DEV_BAD_EXPERT, DEV_OVERFLOW = 0, 1, 2, 3
 CAP_GFX950 = 1
 ROW, COL = 1, 2
-OUT_F32, DEBUG_F32, SERIAL, UNFUSED = 1, 2, 4, 8
+OUT_F32, DEBUG_F32, SERIAL, UNFUSED, X_QUANTIZED = 1, 2, 4, 8, 16
 DEQ_BF16, DEQ_F32 = 0, 1
 
 # tensor ids (mxf_tensor)
@@ -34,7 +34,8 @@ T = {name: i for i, name in enumerate(TENSORS)}
 EXPORTS = ["mxf_abi_version", "mxf_query_device", "mxf_last_error", "mxfp8_quantize", "mxfp8_dequantize",
            "mxf_mlp_saved_bytes", "mxf_mlp_workspace_bytes", "mxf_mlp_tensor", "grouped_mlp_fwd",
            "grouped_mlp_bwd", "mxf_read_status", "mxf_profile_begin", "mxf_profile_end",
-           "mxf_pack_w13", "mxf_unpack_w13"]
+           "mxf_pack_w13", "mxf_unpack_w13", "mxf_route_plan", "mxf_dispatch_permute",
+           "mxfp8_dispatch_quantize"]
 
 
 class MxfError(RuntimeError):
@@ -83,6 +84,9 @@ def lib():
             "mxf_profile_end": (ctypes.c_int, [ctypes.POINTER(KernelTime), i32, ctypes.POINTER(i32)]),
             "mxf_pack_w13": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp]),
             "mxf_unpack_w13": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp]),
+            "mxf_route_plan": (ctypes.c_int, [vp, i64, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp]),
+            "mxf_dispatch_permute": (ctypes.c_int, [vp, i64, i32, i64, i32, vp, vp, i64, vp, vp]),
+            "mxfp8_dispatch_quantize": (ctypes.c_int, [pdesc, vp, vp, vp, vp, i64, i32, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -206,6 +210,45 @@ def grouped_mlp_bwd(desc, offs, counts, dy, saved, dx, dw1, dw3, dw2, workspace,
     _check(lib().grouped_mlp_bwd(ctypes.byref(desc), _ptr(offs), _ptr(counts), _ptr(dy), _ptr(saved),
                                  _ptr(dx), _ptr(dw1), _ptr(dw3), _ptr(dw2), _ptr(workspace),
                                  _stream(stream)))
+
+
+def mxf_route_plan(expert_idx, tokens, topk, E, pad_multiple, m_capacity, offs, counts, row_assign, assign_row,
+                   status=None, stream=None):
+    """Raw call: pointers (tensors or ints) and sizes, as in the C header."""
+    _check(lib().mxf_route_plan(_ptr(expert_idx), tokens, topk, E, pad_multiple, m_capacity, _ptr(offs),
+                                _ptr(counts), _ptr(row_assign), _ptr(assign_row), _ptr(status), _stream(stream)))
+
+
+def route_plan(expert_idx, E, pad_multiple, m_capacity, stream=None):
+    """Routing plan of expert ids [tokens, topk] (int32 CUDA tensor); allocates and returns
+    dict(offs, counts, row_assign, assign_row, status) as int32 CUDA tensors."""
+    import torch
+    assert expert_idx.dtype == torch.int32 and expert_idx.dim() == 2 and expert_idx.is_contiguous()
+    tokens, topk = expert_idx.shape
+    dev = expert_idx.device
+    out = {"offs": torch.empty(E + 1, dtype=torch.int32, device=dev),
+           "counts": torch.empty(E, dtype=torch.int32, device=dev),
+           "row_assign": torch.empty(max(m_capacity, 1), dtype=torch.int32, device=dev),
+           "assign_row": torch.empty(max(tokens * topk, 1), dtype=torch.int32, device=dev),
+           "status": torch.empty(1, dtype=torch.int32, device=dev)}
+    mxf_route_plan(expert_idx, tokens, topk, E, pad_multiple, m_capacity, out["offs"], out["counts"],
+                   out["row_assign"], out["assign_row"], out["status"], stream)
+    out["row_assign"] = out["row_assign"][:m_capacity]
+    out["assign_row"] = out["assign_row"][:tokens * topk]
+    return out
+
+
+def mxf_dispatch_permute(x_tokens, tokens, topk, D, E, offs, row_assign, m_capacity, x_out, stream=None):
+    """Raw call: pointers (tensors or ints) and sizes, as in the C header."""
+    _check(lib().mxf_dispatch_permute(_ptr(x_tokens), tokens, topk, D, E, _ptr(offs), _ptr(row_assign), m_capacity,
+                                      _ptr(x_out), _stream(stream)))
+
+
+def mxfp8_dispatch_quantize(desc, offs, counts, row_assign, x_tokens, tokens, topk, saved, workspace, stream=None):
+    """Raw call: pointers (tensors or ints) and sizes, as in the C header."""
+    _check(lib().mxfp8_dispatch_quantize(ctypes.byref(desc), _ptr(offs), _ptr(counts), _ptr(row_assign),
+                                         _ptr(x_tokens), tokens, topk, _ptr(saved), _ptr(workspace),
+                                         _stream(stream)))
 
 
 def read_status(workspace, stream=None):

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmxfp8.so")
-SOURCES = ["abi.hip", "quantize.hip", "gemm.hip"]
+SOURCES = ["abi.hip", "quantize.hip", "gemm.hip", "dispatch.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

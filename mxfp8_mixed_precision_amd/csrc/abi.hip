@@ -157,7 +157,7 @@ mxf_status check_desc(const mxf_mlp_desc* d) {
                 (long long)d->m_capacity, d->pad_multiple);
   if (d->m_capacity > (int64_t)1 << 30)
     return fail(MXF_E_SHAPE, "m_capacity = %lld: larger than 2^30 rows", (long long)d->m_capacity);
-  if (d->flags & ~(uint32_t)(MXF_OUT_F32 | MXF_DEBUG_F32 | MXF_SERIAL | MXF_UNFUSED))
+  if (d->flags & ~(uint32_t)(MXF_OUT_F32 | MXF_DEBUG_F32 | MXF_SERIAL | MXF_UNFUSED | MXF_X_QUANTIZED))
     return fail(MXF_E_ARG, "flags = 0x%x: unknown bits", d->flags);
   if ((d->flags & MXF_UNFUSED) && (d->flags & MXF_DEBUG_F32))
     return fail(MXF_E_ARG, "flags = 0x%x: MXF_DEBUG_F32 is not available with MXF_UNFUSED", d->flags);
@@ -319,9 +319,11 @@ mxf_status grouped_mlp_fwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   g_err.clear();
   mxf_status s = check_desc(desc);
   if (s != MXF_OK) return s;
-  const void* ptrs[] = {x, w1, w3, w2, y, saved, workspace};
-  const char* names[] = {"x", "w1", "w3", "w2", "y", "saved", "workspace"};
-  if ((s = check_mlp_ptrs(ptrs, names, 7)) != MXF_OK) return s;
+  // with MXF_X_QUANTIZED, X's codes are already in saved / workspace and x is not read
+  const bool xq = (desc->flags & MXF_X_QUANTIZED) != 0;
+  const void* ptrs[] = {w1, w3, w2, y, saved, workspace, x};
+  const char* names[] = {"w1", "w3", "w2", "y", "saved", "workspace", "x"};
+  if ((s = check_mlp_ptrs(ptrs, names, xq ? 6 : 7)) != MXF_OK) return s;
   if (!offs) return fail(MXF_E_NULL, "offs is NULL");
   if ((s = check_device()) != MXF_OK) return s;
 
@@ -338,11 +340,13 @@ mxf_status grouped_mlp_fwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
             return mxf_launch_quant_weights(w1, w3, true, E, 2 * F, D, T(MXF_T_W13Q_R), T(MXF_T_W13S_R),
                                             T(MXF_T_W13Q_C), T(MXF_T_W13S_C), st);
           }), "W13 quantize launch");
-  MXF_HIP(timed("quant_x", st, [&] {
-            return mxf_launch_quant_tokens(x, M, D, offs, counts, (int)E, desc->pad_multiple, T(MXF_T_XQ_R),
-                                           T(MXF_T_XS_R), T(MXF_T_XQ_C), T(MXF_T_XS_C),
-                                           (int32_t*)T(MXF_T_STATUS), st);
-          }), "X quantize launch");
+  if (!xq) {
+    MXF_HIP(timed("quant_x", st, [&] {
+              return mxf_launch_quant_tokens(x, M, D, offs, counts, (int)E, desc->pad_multiple, T(MXF_T_XQ_R),
+                                             T(MXF_T_XS_R), T(MXF_T_XQ_C), T(MXF_T_XS_C),
+                                             (int32_t*)T(MXF_T_STATUS), st);
+            }), "X quantize launch");
+  }
 
   // W2 is needed only by FC2: its (HBM-bound) quantization runs on a helper stream beside FC1,
   // whose main loop is bound by L2 -> LDS traffic and leaves HBM bandwidth spare
@@ -512,6 +516,101 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
     MXF_HIP(hipStreamWaitEvent(st, H->join[0], 0), "hipStreamWaitEvent");
     MXF_HIP(hipStreamWaitEvent(st, H->join[1], 0), "hipStreamWaitEvent");
   }
+  return MXF_OK;
+}
+
+// ------------------------------------------------------------------ dispatch
+
+static bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+mxf_status mxf_route_plan(const int32_t* expert_idx, int64_t tokens, int32_t topk, int32_t E, int32_t pad_multiple,
+                          int64_t m_capacity, int32_t* offs, int32_t* counts, int32_t* row_assign,
+                          int32_t* assign_row, int32_t* status, void* stream) {
+  g_err.clear();
+  if (tokens < 0) return fail(MXF_E_SHAPE, "tokens = %lld: negative", (long long)tokens);
+  if (topk < 1 || topk > 64) return fail(MXF_E_SHAPE, "topk = %d: must be in [1, 64]", topk);
+  if (tokens * topk > ((int64_t)1 << 30))
+    return fail(MXF_E_SHAPE, "tokens * topk = %lld: more than 2^30 assignments", (long long)(tokens * topk));
+  if (E < 1 || E > 1024) return fail(MXF_E_SHAPE, "E = %d: must be in [1, 1024]", E);
+  if (pad_multiple < 1 || pad_multiple > 4096)
+    return fail(MXF_E_SHAPE, "pad_multiple = %d: must be in [1, 4096]", pad_multiple);
+  if (m_capacity < 0 || m_capacity > ((int64_t)1 << 30))
+    return fail(MXF_E_SHAPE, "m_capacity = %lld: must be in [0, 2^30]", (long long)m_capacity);
+  const int64_t n = tokens * topk;
+  if (!offs || !counts) return fail(MXF_E_NULL, "offs/counts is NULL");
+  if (n > 0 && (!expert_idx || !assign_row)) return fail(MXF_E_NULL, "expert_idx/assign_row is NULL");
+  if (m_capacity > 0 && !row_assign) return fail(MXF_E_NULL, "row_assign is NULL");
+  const void* al[] = {expert_idx, offs, counts, row_assign, assign_row, status};
+  const char* an[] = {"expert_idx", "offs", "counts", "row_assign", "assign_row", "status"};
+  for (int i = 0; i < 6; ++i)
+    if (!aligned4(al[i])) return fail(MXF_E_ALIGN, "%s is not 4-byte aligned", an[i]);
+  mxf_status s = check_device();
+  if (s != MXF_OK) return s;
+  const size_t lds = mxf_route_plan_lds_bytes(E);
+  MXF_HIP(timed("route_plan", (hipStream_t)stream, [&] {
+            return mxf_launch_route_plan(expert_idx, (int32_t)n, E, pad_multiple, m_capacity, offs, counts,
+                                         row_assign, assign_row, status, (hipStream_t)stream);
+          }), lds > 65536 ? "route plan launch (LDS above 64 KiB)" : "route plan launch");
+  return MXF_OK;
+}
+
+static mxf_status check_dispatch(const void* x_tokens, int64_t tokens, int32_t topk, const int32_t* offs,
+                                 const int32_t* row_assign, int64_t m_capacity) {
+  if (tokens < 0) return fail(MXF_E_SHAPE, "tokens = %lld: negative", (long long)tokens);
+  if (topk < 1 || topk > 64) return fail(MXF_E_SHAPE, "topk = %d: must be in [1, 64]", topk);
+  if (tokens * topk > ((int64_t)1 << 30))
+    return fail(MXF_E_SHAPE, "tokens * topk = %lld: more than 2^30 assignments", (long long)(tokens * topk));
+  if (!offs) return fail(MXF_E_NULL, "offs is NULL");
+  if (m_capacity > 0 && !row_assign) return fail(MXF_E_NULL, "row_assign is NULL");
+  if (tokens > 0 && !x_tokens) return fail(MXF_E_NULL, "x_tokens is NULL");
+  if (!aligned16(x_tokens)) return fail(MXF_E_ALIGN, "x_tokens is not 16-byte aligned");
+  if (!aligned4(offs) || !aligned4(row_assign)) return fail(MXF_E_ALIGN, "offs/row_assign is not 4-byte aligned");
+  return MXF_OK;
+}
+
+mxf_status mxf_dispatch_permute(const void* x_tokens, int64_t tokens, int32_t topk, int64_t D, int32_t E,
+                                const int32_t* offs, const int32_t* row_assign, int64_t m_capacity, void* x_out,
+                                void* stream) {
+  g_err.clear();
+  if (D < 0 || D % 8) return fail(MXF_E_SHAPE, "D = %lld: must be a non-negative multiple of 8", (long long)D);
+  if (E < 1 || E > 1024) return fail(MXF_E_SHAPE, "E = %d: must be in [1, 1024]", E);
+  if (m_capacity < 0 || m_capacity > ((int64_t)1 << 30))
+    return fail(MXF_E_SHAPE, "m_capacity = %lld: must be in [0, 2^30]", (long long)m_capacity);
+  mxf_status s = check_dispatch(x_tokens, tokens, topk, offs, row_assign, m_capacity);
+  if (s != MXF_OK) return s;
+  if (m_capacity > 0 && D > 0 && !x_out) return fail(MXF_E_NULL, "x_out is NULL");
+  if (!aligned16(x_out)) return fail(MXF_E_ALIGN, "x_out is not 16-byte aligned");
+  if (m_capacity == 0 || D == 0) return MXF_OK;
+  if ((s = check_device()) != MXF_OK) return s;
+  MXF_HIP(timed("permute", (hipStream_t)stream, [&] {
+            return mxf_launch_permute(x_tokens, tokens * topk, topk, D, offs, E, row_assign, m_capacity, x_out,
+                                      (hipStream_t)stream);
+          }), "permute launch");
+  return MXF_OK;
+}
+
+mxf_status mxfp8_dispatch_quantize(const mxf_mlp_desc* desc, const int32_t* offs, const int32_t* counts,
+                                   const int32_t* row_assign, const void* x_tokens, int64_t tokens, int32_t topk,
+                                   void* saved, void* workspace, void* stream) {
+  g_err.clear();
+  mxf_status s = check_desc(desc);
+  if (s != MXF_OK) return s;
+  if ((s = check_dispatch(x_tokens, tokens, topk, offs, row_assign, desc->m_capacity)) != MXF_OK) return s;
+  const void* ptrs[] = {saved, workspace};
+  const char* names[] = {"saved", "workspace"};
+  if ((s = check_mlp_ptrs(ptrs, names, 2)) != MXF_OK) return s;
+  if ((s = check_device()) != MXF_OK) return s;
+  Layout L;
+  make_layout(desc, &L);
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* ws = (uint8_t*)workspace;
+  uint8_t* sv = (uint8_t*)saved;
+  auto T = [&](int t) -> uint8_t* { return (L.region[t] ? sv : ws) + L.off[t]; };
+  MXF_HIP(timed("dispatch_quant_x", st, [&] {
+            return mxf_launch_quant_gather(x_tokens, tokens * topk, topk, row_assign, desc->m_capacity, desc->D,
+                                           offs, counts, desc->E, desc->pad_multiple, T(MXF_T_XQ_R), T(MXF_T_XS_R),
+                                           T(MXF_T_XQ_C), T(MXF_T_XS_C), (int32_t*)T(MXF_T_STATUS), st);
+          }), "dispatch quantize launch");
   return MXF_OK;
 }
 

@@ -53,10 +53,21 @@ hipError_t mxf_launch_swiglu_quant(const void* h13, int64_t mcap, int64_t F, con
 hipError_t mxf_launch_dswiglu_quant(const void* dh, const void* h13, int64_t mcap, int64_t F, const int32_t* offs,
                                     const int32_t* counts, int E, int pad, void* q_r, void* s_r, void* q_c,
                                     void* s_c, hipStream_t st);
+hipError_t mxf_launch_quant_gather(const void* x_tokens, int64_t n_assign, int topk, const int32_t* row_assign,
+                                   int64_t mcap, int64_t D, const int32_t* offs, const int32_t* counts, int E,
+                                   int pad, void* q_r, void* s_r, void* q_c, void* s_c, int32_t* status,
+                                   hipStream_t st);
 hipError_t mxf_launch_dequantize(const void* q, const void* s, int64_t rows, int64_t cols, bool bf16,
                                  void* out, hipStream_t st);
 hipError_t mxf_launch_pack13(const void* w1, const void* w3, void* w13, int64_t E, int64_t F,
                              int64_t D, bool pack, hipStream_t st);
+// dispatch.hip
+size_t mxf_route_plan_lds_bytes(int E);
+hipError_t mxf_launch_route_plan(const int32_t* idx, int32_t n, int E, int pad, int64_t mcap, int32_t* offs,
+                                 int32_t* counts, int32_t* row_assign, int32_t* assign_row, int32_t* status,
+                                 hipStream_t st);
+hipError_t mxf_launch_permute(const void* x, int64_t n_assign, int topk, int64_t D, const int32_t* offs, int E,
+                              const int32_t* row_assign, int64_t mcap, void* out, hipStream_t st);
 // gemm.hip
 hipError_t mxf_launch_gemm_mgroup(int epi, const mxf::GemmParams& p, hipStream_t st);
 hipError_t mxf_launch_gemm_kgroup(int epi, const mxf::GemmParams& p, hipStream_t st);

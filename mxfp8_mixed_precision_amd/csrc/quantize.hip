@@ -25,7 +25,10 @@ namespace mxf {
 // QK_SWIGLU / QK_DSWIGLU are the standalone SwiGLU / dSwiGLU + dual-quantization kernels of the
 // unfused plan: they read the BF16 FC1 output (and dh) that the plain GEMMs wrote, apply the
 // same rounding points as the fused epilogues, and quantize like QK_MASKED.
-enum QuantKind { QK_PLAIN = 0, QK_MASKED = 1, QK_PACK13 = 2, QK_SWIGLU = 3, QK_DSWIGLU = 4 };
+// QK_GATHER is the fused dispatch: row r of the padded token layout is read from the token
+// row_assign[r] / topk of the unpermuted token matrix (no BF16 copy of the permuted matrix),
+// then quantized like QK_MASKED.
+enum QuantKind { QK_PLAIN = 0, QK_MASKED = 1, QK_PACK13 = 2, QK_SWIGLU = 3, QK_DSWIGLU = 4, QK_GATHER = 5 };
 
 struct QuantParams {
   const uint16_t* src;   // BF16 bits; QK_PACK13: w1 [E, F, D]
@@ -42,7 +45,10 @@ struct QuantParams {
   const int32_t* offs;                  // QK_MASKED: token offsets [E+1]
   const int32_t* counts;                // QK_MASKED: real rows per expert [E] or null
   int E, pad;
-  int32_t* status;                      // QK_MASKED: device status word (block 0 writes it)
+  int32_t* status;                      // QK_MASKED, QK_GATHER: device status word (block 0 writes it)
+  const int32_t* row_assign;            // QK_GATHER: assignment of each padded row (-1: pad)
+  int64_t n_assign;                     // QK_GATHER: tokens * topk
+  int topk;                             // QK_GATHER
 };
 
 
@@ -71,11 +77,12 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
   int64_t valid_end = p.rows;  // rows at or past this read as zero
   const uint16_t* src = p.src + e * p.src_bs;
   int64_t src_row0 = rw0;      // source row of the wavefront's first row
-  if (KIND == QK_MASKED || KIND == QK_SWIGLU || KIND == QK_DSWIGLU) {
+  if (KIND == QK_MASKED || KIND == QK_SWIGLU || KIND == QK_DSWIGLU || KIND == QK_GATHER) {
     // every wavefront reads the offsets (same answers everywhere); mend and the block's rows
     // are multiples of 128, so a block is either wholly before offs[E] or wholly past it
     const Offsets ofs = read_offsets(p.offs, p.counts, p.E, p.pad, p.rows);
-    if (KIND == QK_MASKED && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *p.status = ofs.ok ? 0 : 1;
+    if ((KIND == QK_MASKED || KIND == QK_GATHER) && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+      *p.status = ofs.ok ? 0 : 1;
     if (!ofs.ok) return;
     if (row0 >= ofs.mend) return;  // tail rows: never read or written
     const int ex = ofs.expert(rw0);
@@ -90,10 +97,26 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
   const int64_t rend = valid_end < p.rows ? valid_end : p.rows;
 
   uint32_t x[8][4];
+  int tok[8];  // QK_GATHER: token row of each of the lane's rows (-1: zero row)
+  if (KIND == QK_GATHER) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t r = r0 + j;
+      const int a = (colok && r < rend) ? p.row_assign[r] : -1;
+      tok[j] = (a >= 0 && a < p.n_assign) ? a / p.topk : -1;
+    }
+  }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int64_t r = r0 + j;
-    if (colok && r < rend && KIND == QK_SWIGLU) {
+    if (KIND == QK_GATHER) {
+      if (tok[j] >= 0) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src + (int64_t)tok[j] * p.cols + col);
+        x[j][0] = v.x; x[j][1] = v.y; x[j][2] = v.z; x[j][3] = v.w;
+      } else {
+        x[j][0] = x[j][1] = x[j][2] = x[j][3] = 0u;
+      }
+    } else if (colok && r < rend && KIND == QK_SWIGLU) {
       // h column col of row r: gate at packed column 64 (col / 32) + col % 32, up 32 further
       const uint16_t* row = src + r * (2 * p.cols) + (col >> 5) * 64 + (col & 31);
       const uint4 gv = *reinterpret_cast<const uint4*>(row);
@@ -304,7 +327,7 @@ __global__ __launch_bounds__(256) void pack13_kernel(const uint16_t* a, const ui
 static hipError_t launch_quant(int kind, uint32_t mode, const QuantParams& p, int64_t batch,
                                hipStream_t st) {
   // the token-layout kind always runs (its first block writes the status word)
-  if ((p.rows == 0 || p.cols == 0 || batch == 0) && kind != QK_MASKED) return hipSuccess;
+  if ((p.rows == 0 || p.cols == 0 || batch == 0) && kind != QK_MASKED && kind != QK_GATHER) return hipSuccess;
   const int64_t rt = (p.rows + 127) / 128, ct = (p.cols + 127) / 128;
   const dim3 grid((unsigned)(rt > 0 ? rt : 1), (unsigned)(ct > 0 ? ct : 1), (unsigned)(batch > 0 ? batch : 1));
   const dim3 block(256);
@@ -319,6 +342,8 @@ static hipError_t launch_quant(int kind, uint32_t mode, const QuantParams& p, in
     MXF_QLAUNCH(QK_SWIGLU, true, true);
   } else if (kind == QK_DSWIGLU) {
     MXF_QLAUNCH(QK_DSWIGLU, true, true);
+  } else if (kind == QK_GATHER) {
+    MXF_QLAUNCH(QK_GATHER, true, true);
   } else {
     MXF_QLAUNCH(QK_PACK13, true, true);
   }
@@ -368,6 +393,30 @@ hipError_t mxf_launch_quant_tokens(const void* x, int64_t mcap, int64_t D, const
   p.pad = pad;
   p.status = status;
   return mxf::launch_quant(mxf::QK_MASKED, 3, p, 1, st);
+}
+
+// Fused dispatch: dual quantization of the padded token layout [mcap, D] gathered from the token
+// matrix x_tokens [n_assign / topk, D] through row_assign (row r: token row_assign[r] / topk;
+// pad rows zero; rows >= offs[E] skipped); same outputs and status word as
+// mxf_launch_quant_tokens on the permuted matrix.
+hipError_t mxf_launch_quant_gather(const void* x_tokens, int64_t n_assign, int topk, const int32_t* row_assign,
+                                   int64_t mcap, int64_t D, const int32_t* offs, const int32_t* counts, int E,
+                                   int pad, void* q_r, void* s_r, void* q_c, void* s_c, int32_t* status,
+                                   hipStream_t st) {
+  mxf::QuantParams p = {};
+  p.src = (const uint16_t*)x_tokens;
+  p.rows = mcap;
+  p.cols = D;
+  p.q_r = (uint8_t*)q_r; p.s_r = (uint8_t*)s_r; p.q_c = (uint8_t*)q_c; p.s_c = (uint8_t*)s_c;
+  p.ldc = mcap;
+  p.sr_rs = 4; p.sr_kbs = 4 * mcap;
+  p.sc_rs = 4; p.sc_kbs = 4 * D;
+  p.offs = offs; p.counts = counts; p.E = E; p.pad = pad;
+  p.status = status;
+  p.row_assign = row_assign;
+  p.n_assign = n_assign;
+  p.topk = topk;
+  return mxf::launch_quant(mxf::QK_GATHER, 3, p, 1, st);
 }
 
 // Unfused plan: h = SwiGLU of the BF16 FC1 output h13 [mcap, 2F] (packed gate/up order),

@@ -77,7 +77,7 @@ def test_layout_is_consistent():
 @pytest.mark.parametrize("kw,code", [
     (dict(E=0), _abi.E_SHAPE), (dict(E=2000), _abi.E_SHAPE), (dict(D=200), _abi.E_SHAPE),
     (dict(F=96), _abi.E_SHAPE), (dict(pad=64), _abi.E_SHAPE), (dict(m=1000), _abi.E_SHAPE),
-    (dict(m=-128), _abi.E_SHAPE), (dict(flags=16), _abi.E_ARG),
+    (dict(m=-128), _abi.E_SHAPE), (dict(flags=32), _abi.E_ARG),
     (dict(flags=mx.UNFUSED | mx.DEBUG_F32), _abi.E_ARG),
 ])
 def test_descriptor_rejections(kw, code):
@@ -196,3 +196,50 @@ def test_dequantize_rejections_before_any_launch():
     assert st(0, 16, 4, 32, 0, 16) == _abi.E_NULL              # q NULL with work to do
     assert st(16, 16, 4, 32, 0, 24) == _abi.E_ALIGN            # out not 16-byte aligned
     mx.mxfp8_dequantize(0, 0, 0, 5, 0, 0, stream=0)            # empty: no-op with NULLs
+
+
+def test_dispatch_rejections_before_any_launch():
+    """Argument errors of the dispatch entry points are reported without touching a device."""
+    good = 1 << 20
+
+    def st(fn, *a):
+        with pytest.raises(mx.MxfError) as ei:
+            fn(*a, stream=0)
+        return ei.value.status
+    # mxf_route_plan(expert_idx, tokens, topk, E, pad, m_cap, offs, counts, row_assign, assign_row, status)
+    rp = mx.mxf_route_plan
+    assert st(rp, good, -1, 2, 4, 128, 256, good, good, good, good, None) == _abi.E_SHAPE      # tokens
+    assert st(rp, good, 8, 0, 4, 128, 256, good, good, good, good, None) == _abi.E_SHAPE       # topk
+    assert st(rp, good, 8, 65, 4, 128, 256, good, good, good, good, None) == _abi.E_SHAPE      # topk
+    assert st(rp, good, 1 << 29, 4, 4, 128, 256, good, good, good, good, None) == _abi.E_SHAPE  # 2^31 assignments
+    assert st(rp, good, 8, 2, 0, 128, 256, good, good, good, good, None) == _abi.E_SHAPE       # E
+    assert st(rp, good, 8, 2, 1025, 128, 256, good, good, good, good, None) == _abi.E_SHAPE    # E
+    assert st(rp, good, 8, 2, 4, 0, 256, good, good, good, good, None) == _abi.E_SHAPE         # pad
+    assert st(rp, good, 8, 2, 4, 128, -1, good, good, good, good, None) == _abi.E_SHAPE        # capacity
+    assert st(rp, None, 8, 2, 4, 128, 256, good, good, good, good, None) == _abi.E_NULL        # expert_idx
+    assert st(rp, good, 8, 2, 4, 128, 256, None, good, good, good, None) == _abi.E_NULL        # offs
+    assert st(rp, good, 8, 2, 4, 128, 256, good, good, None, good, None) == _abi.E_NULL        # row_assign
+    assert st(rp, good + 2, 8, 2, 4, 128, 256, good, good, good, good, None) == _abi.E_ALIGN   # expert_idx
+    # mxf_dispatch_permute(x_tokens, tokens, topk, D, E, offs, row_assign, m_cap, x_out)
+    dp = mx.mxf_dispatch_permute
+    assert st(dp, good, 8, 2, 12, 4, good, good, 256, good) == _abi.E_SHAPE                  # D % 8
+    assert st(dp, good, 8, 2, 64, 4, None, good, 256, good) == _abi.E_NULL                   # offs
+    assert st(dp, good, 8, 2, 64, 4, good, good, 256, None) == _abi.E_NULL                   # x_out
+    assert st(dp, good + 8, 8, 2, 64, 4, good, good, 256, good) == _abi.E_ALIGN              # x_tokens
+    assert st(dp, good, 8, 2, 64, 4, good, good, 256, good + 8) == _abi.E_ALIGN              # x_out
+    # mxfp8_dispatch_quantize(desc, offs, counts, row_assign, x_tokens, tokens, topk, saved, workspace)
+    dq = mx.mxfp8_dispatch_quantize
+    assert st(dq, _desc(D=200), good, good, good, good, 8, 2, good, good) == _abi.E_SHAPE
+    assert st(dq, _desc(), good, good, good, good, 8, 0, good, good) == _abi.E_SHAPE
+    assert st(dq, _desc(), good, good, None, good, 8, 2, good, good) == _abi.E_NULL
+    assert st(dq, _desc(), good, good, good, None, 8, 2, good, good) == _abi.E_NULL
+    assert st(dq, _desc(), good, good, good, good, 8, 2, None, good) == _abi.E_NULL
+    # grouped_mlp_fwd under MXF_X_QUANTIZED accepts x = NULL (then fails only on the device check;
+    # with a GPU present these bogus pointers would be launched on, so that case stops here)
+    import torch
+    if torch.cuda.is_available():
+        return
+    d = _desc(flags=mx.X_QUANTIZED)
+    with pytest.raises(mx.MxfError) as ei:
+        mx.grouped_mlp_fwd(d, good, None, None, good, good, good, good, good, good, stream=0)
+    assert ei.value.status in (_abi.E_HIP, _abi.E_DEVICE)
