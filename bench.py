@@ -120,7 +120,7 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference kernel for HBM byte counters)")
     ap.add_argument("--no-plans", action="store_true",
-                    help="skip the fused/unfused plan A/B (profiling runs: it launches other kernels)")
+                    help="skip the fused/unfused plan and dispatch A/B legs (profiling runs: they launch other kernels)")
     ap.add_argument("--serial", action="store_true",
                     help="time with MXF_SERIAL too (every kernel alone; for profiler runs)")
     ap.add_argument("--quant-only", action="store_true",
@@ -266,6 +266,7 @@ def main():
     }
 
     if not args.no_plans:
+        out["dispatch"] = bench_dispatch(mx, torch, dev, args, kernels["quant_x"]["avg_us"])
         out["plans"] = bench_plans(mx, torch, dev, args, sets, counts, E, D, F, y, dx, dw1, dw3, dw2)
     if not args.no_quant:
         out["quantize"] = bench_quantize(mx, torch, dev, args)
@@ -369,6 +370,63 @@ def bench_dequantize(mx, torch, dev, args):
             "unit": "GB/s", "avg_us": round(avg_s * 1e6, 2),
             "roofline": {"bound": "hbm", "kernel": "dequantize", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+
+
+def bench_dispatch(mx, torch, dev, args, quant_x_us):
+    """Dispatch of the workload's routed tokens into the padded layout: the routing plan, then
+    either the BF16 permute (followed by the forward's own Q_X, timed in the main pass) or the
+    fused gather + dual quantization of X."""
+    import workloads
+    tok, ids = workloads.routed_tokens(args.workload, device="cpu")
+    cfg = workloads.MLP_CONFIGS[args.workload]
+    E, D, F, pad = cfg["E"], cfg["D"], cfg["F"], cfg["pad"]
+    tokens, topk = ids.shape
+    counts = workloads.expert_counts(args.workload)
+    mcap = workloads.padded_offsets(counts, pad)[-1]
+    m_real = sum(counts)
+    toks = [tok.to(dev)] + [workloads.randn_bf16(tuple(tok.shape), 1.0, workloads._gen(43 + s, dev), dev)
+                            for s in range(2)]
+    ids_t = torch.from_numpy(ids).to(dev)
+    offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    cnt = torch.empty(E, dtype=torch.int32, device=dev)
+    ra = torch.empty(mcap, dtype=torch.int32, device=dev)
+    ar = torch.empty(tokens * topk, dtype=torch.int32, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    pws = torch.empty(mx.route_plan_workspace_bytes(tokens, topk, E), dtype=torch.uint8, device=dev)
+    xp = torch.empty((mcap, D), dtype=torch.bfloat16, device=dev)
+    ctx = mx.MlpContext(E, D, F, pad, mcap, device=dev)
+    n = max(args.steps, 10)
+
+    def one(i):
+        mx.mxf_route_plan(ids_t, tokens, topk, E, pad, mcap, offs, cnt, ra, ar, status, pws)
+        mx.mxf_dispatch_permute(toks[i % 3], tokens, topk, D, E, offs, ra, mcap, xp)
+        ctx.dispatch_quantize(offs, cnt, ra, toks[i % 3], topk)
+
+    for i in range(3):
+        one(i)
+    torch.cuda.synchronize()
+    assert int(status.item()) == mx.DEV_OK and ctx.status() == mx.DEV_OK
+    mx.profile_begin(3 * n)
+    for i in range(n):
+        one(i)
+    torch.cuda.synchronize()
+    prof = mx.profile_end()
+    us = {k: prof[k][1] / prof[k][0] * 1e3 for k in ("route_plan", "permute", "dispatch_quant_x")}
+    # compulsory HBM bytes: each token row read once (its topk copies come from cache), every
+    # padded row written, the row indices read
+    rd = tokens * D * 2
+    perm_bytes = rd + mcap * D * 2 + mcap * 4
+    dq_bytes = rd + mcap * D * (2 + 2.0 / 32) + m_real * 4
+    gbs = lambda b, u: round(b / (u * 1e-6) / 1e9, 1)
+    return {"workload": f"{tokens} tokens x top-{topk} -> {m_real} rows of {E} experts padded to {mcap} (pad {pad}), "
+                        f"D={D}",
+            "route_plan_us": round(us["route_plan"], 2),
+            "permute_us": round(us["permute"], 2), "permute_gbs": gbs(perm_bytes, us["permute"]),
+            "dispatch_quant_x_us": round(us["dispatch_quant_x"], 2),
+            "dispatch_quant_x_gbs": gbs(dq_bytes, us["dispatch_quant_x"]),
+            "unfused_us": round(us["permute"] + quant_x_us, 2),
+            "fused_us": round(us["dispatch_quant_x"], 2),
+            "note": "unfused = permute + the forward's quant_x (main serial pass); fused = dispatch_quant_x"}
 
 
 if __name__ == "__main__":

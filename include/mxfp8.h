@@ -234,13 +234,16 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc /* host */, const int32_t* o
  *     assignment is dropped, the rest is placed); else MXF_DEV_OVERFLOW if offs[E] >
  *     m_capacity (offs and counts still describe the whole layout; rows past the capacity
  *     are not written, so the MLP's offsets check rejects these offs).
+ *   workspace: device scratch of mxf_route_plan_workspace_bytes(tokens, topk, E) bytes
+ *     (4 * (E + 1) per 1024 assignments); its contents on entry do not matter.
  * tokens * topk <= 2^30, 1 <= topk <= 64, 1 <= E <= 1024, 1 <= pad_multiple <= 4096,
- * 0 <= m_capacity <= 2^30; int32 pointers 4-byte aligned. One workgroup does the whole plan
- * (a few microseconds at tens of thousands of assignments).
+ * 0 <= m_capacity <= 2^30; int32 pointers and workspace 4-byte aligned. Three short launches.
  * Errors: MXF_E_NULL, MXF_E_SHAPE, MXF_E_ALIGN, MXF_E_DEVICE, MXF_E_HIP. */
+size_t mxf_route_plan_workspace_bytes(int64_t tokens, int32_t topk, int32_t E); /* 0 if invalid */
 mxf_status mxf_route_plan(const int32_t* expert_idx, int64_t tokens, int32_t topk, int32_t E,
                           int32_t pad_multiple, int64_t m_capacity, int32_t* offs, int32_t* counts,
-                          int32_t* row_assign, int32_t* assign_row, int32_t* status, void* stream);
+                          int32_t* row_assign, int32_t* assign_row, int32_t* status, void* workspace,
+                          void* stream);
 
 /* BF16 permute: x_out [m_capacity, D] row r (r < min(offs[E], m_capacity)) = x_tokens
  * [tokens, D] row row_assign[r] / topk, or zeros where row_assign[r] is -1 (or outside

@@ -34,7 +34,7 @@ T = {name: i for i, name in enumerate(TENSORS)}
 EXPORTS = ["mxf_abi_version", "mxf_query_device", "mxf_last_error", "mxfp8_quantize", "mxfp8_dequantize",
            "mxf_mlp_saved_bytes", "mxf_mlp_workspace_bytes", "mxf_mlp_tensor", "grouped_mlp_fwd",
            "grouped_mlp_bwd", "mxf_read_status", "mxf_profile_begin", "mxf_profile_end",
-           "mxf_pack_w13", "mxf_unpack_w13", "mxf_route_plan", "mxf_dispatch_permute",
+           "mxf_pack_w13", "mxf_unpack_w13", "mxf_route_plan_workspace_bytes", "mxf_route_plan", "mxf_dispatch_permute",
            "mxfp8_dispatch_quantize"]
 
 
@@ -84,7 +84,8 @@ def lib():
             "mxf_profile_end": (ctypes.c_int, [ctypes.POINTER(KernelTime), i32, ctypes.POINTER(i32)]),
             "mxf_pack_w13": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp]),
             "mxf_unpack_w13": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp]),
-            "mxf_route_plan": (ctypes.c_int, [vp, i64, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp]),
+            "mxf_route_plan_workspace_bytes": (sz, [i64, i32, i32]),
+            "mxf_route_plan": (ctypes.c_int, [vp, i64, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, vp]),
             "mxf_dispatch_permute": (ctypes.c_int, [vp, i64, i32, i64, i32, vp, vp, i64, vp, vp]),
             "mxfp8_dispatch_quantize": (ctypes.c_int, [pdesc, vp, vp, vp, vp, i64, i32, vp, vp, vp]),
         }
@@ -212,11 +213,16 @@ def grouped_mlp_bwd(desc, offs, counts, dy, saved, dx, dw1, dw3, dw2, workspace,
                                  _stream(stream)))
 
 
+def route_plan_workspace_bytes(tokens, topk, E):
+    return lib().mxf_route_plan_workspace_bytes(tokens, topk, E)
+
+
 def mxf_route_plan(expert_idx, tokens, topk, E, pad_multiple, m_capacity, offs, counts, row_assign, assign_row,
-                   status=None, stream=None):
+                   status, workspace, stream=None):
     """Raw call: pointers (tensors or ints) and sizes, as in the C header."""
     _check(lib().mxf_route_plan(_ptr(expert_idx), tokens, topk, E, pad_multiple, m_capacity, _ptr(offs),
-                                _ptr(counts), _ptr(row_assign), _ptr(assign_row), _ptr(status), _stream(stream)))
+                                _ptr(counts), _ptr(row_assign), _ptr(assign_row), _ptr(status), _ptr(workspace),
+                                _stream(stream)))
 
 
 def route_plan(expert_idx, E, pad_multiple, m_capacity, stream=None):
@@ -231,8 +237,9 @@ def route_plan(expert_idx, E, pad_multiple, m_capacity, stream=None):
            "row_assign": torch.empty(max(m_capacity, 1), dtype=torch.int32, device=dev),
            "assign_row": torch.empty(max(tokens * topk, 1), dtype=torch.int32, device=dev),
            "status": torch.empty(1, dtype=torch.int32, device=dev)}
+    ws = torch.empty(route_plan_workspace_bytes(tokens, topk, E), dtype=torch.uint8, device=dev)
     mxf_route_plan(expert_idx, tokens, topk, E, pad_multiple, m_capacity, out["offs"], out["counts"],
-                   out["row_assign"], out["assign_row"], out["status"], stream)
+                   out["row_assign"], out["assign_row"], out["status"], ws, stream)
     out["row_assign"] = out["row_assign"][:m_capacity]
     out["assign_row"] = out["assign_row"][:tokens * topk]
     return out

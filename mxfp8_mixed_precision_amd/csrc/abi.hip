@@ -523,34 +523,44 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
 
 static bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-mxf_status mxf_route_plan(const int32_t* expert_idx, int64_t tokens, int32_t topk, int32_t E, int32_t pad_multiple,
-                          int64_t m_capacity, int32_t* offs, int32_t* counts, int32_t* row_assign,
-                          int32_t* assign_row, int32_t* status, void* stream) {
-  g_err.clear();
+static mxf_status check_plan_sizes(int64_t tokens, int32_t topk, int32_t E) {
   if (tokens < 0) return fail(MXF_E_SHAPE, "tokens = %lld: negative", (long long)tokens);
   if (topk < 1 || topk > 64) return fail(MXF_E_SHAPE, "topk = %d: must be in [1, 64]", topk);
   if (tokens * topk > ((int64_t)1 << 30))
     return fail(MXF_E_SHAPE, "tokens * topk = %lld: more than 2^30 assignments", (long long)(tokens * topk));
   if (E < 1 || E > 1024) return fail(MXF_E_SHAPE, "E = %d: must be in [1, 1024]", E);
+  return MXF_OK;
+}
+
+size_t mxf_route_plan_workspace_bytes(int64_t tokens, int32_t topk, int32_t E) {
+  if (check_plan_sizes(tokens, topk, E) != MXF_OK) return 0;
+  return mxf_route_plan_workspace_bytes(tokens * topk, E);
+}
+
+mxf_status mxf_route_plan(const int32_t* expert_idx, int64_t tokens, int32_t topk, int32_t E, int32_t pad_multiple,
+                          int64_t m_capacity, int32_t* offs, int32_t* counts, int32_t* row_assign,
+                          int32_t* assign_row, int32_t* status, void* workspace, void* stream) {
+  g_err.clear();
+  mxf_status s = check_plan_sizes(tokens, topk, E);
+  if (s != MXF_OK) return s;
   if (pad_multiple < 1 || pad_multiple > 4096)
     return fail(MXF_E_SHAPE, "pad_multiple = %d: must be in [1, 4096]", pad_multiple);
   if (m_capacity < 0 || m_capacity > ((int64_t)1 << 30))
     return fail(MXF_E_SHAPE, "m_capacity = %lld: must be in [0, 2^30]", (long long)m_capacity);
   const int64_t n = tokens * topk;
   if (!offs || !counts) return fail(MXF_E_NULL, "offs/counts is NULL");
+  if (!workspace) return fail(MXF_E_NULL, "workspace is NULL");
   if (n > 0 && (!expert_idx || !assign_row)) return fail(MXF_E_NULL, "expert_idx/assign_row is NULL");
   if (m_capacity > 0 && !row_assign) return fail(MXF_E_NULL, "row_assign is NULL");
-  const void* al[] = {expert_idx, offs, counts, row_assign, assign_row, status};
-  const char* an[] = {"expert_idx", "offs", "counts", "row_assign", "assign_row", "status"};
-  for (int i = 0; i < 6; ++i)
+  const void* al[] = {expert_idx, offs, counts, row_assign, assign_row, status, workspace};
+  const char* an[] = {"expert_idx", "offs", "counts", "row_assign", "assign_row", "status", "workspace"};
+  for (int i = 0; i < 7; ++i)
     if (!aligned4(al[i])) return fail(MXF_E_ALIGN, "%s is not 4-byte aligned", an[i]);
-  mxf_status s = check_device();
-  if (s != MXF_OK) return s;
-  const size_t lds = mxf_route_plan_lds_bytes(E);
+  if ((s = check_device()) != MXF_OK) return s;
   MXF_HIP(timed("route_plan", (hipStream_t)stream, [&] {
             return mxf_launch_route_plan(expert_idx, (int32_t)n, E, pad_multiple, m_capacity, offs, counts,
-                                         row_assign, assign_row, status, (hipStream_t)stream);
-          }), lds > 65536 ? "route plan launch (LDS above 64 KiB)" : "route plan launch");
+                                         row_assign, assign_row, status, workspace, (hipStream_t)stream);
+          }), "route plan launch");
   return MXF_OK;
 }
 

@@ -7,15 +7,20 @@
 // segment rows follow the assignment index a = t * topk + k (a stable counting sort), so the
 // layout is unique.
 //
-//  * route_plan_kernel (one workgroup of 16 wavefronts): wavefront w owns a contiguous chunk of
-//    the assignments. Pass 1 counts its chunk per expert in its own LDS row; then one thread
-//    per expert turns the 16 rows into per-wavefront bases and the padded segment lengths are
-//    scanned into offs. Pass 2 walks the chunk again 64 assignments at a time: lanes routed to
-//    the same expert find each other with log2(E) ballots, take their rank among themselves,
-//    and the lowest of them advances the wavefront's counter for that expert -- so the order
-//    is the assignment order without any cross-wavefront atomics. Launch cost is a few
-//    microseconds at tens of thousands of assignments; the plan is latency-bound, not
-//    bandwidth-bound.
+//  * The plan is a stable counting sort in three launches. Workgroup b of the first and last
+//    owns assignments [1024 b, 1024 b + 1024), 256 per wavefront, read as 4 ids per lane with
+//    all loads in flight. Lanes routed to the same expert find each other with one ballot per
+//    bit of the id, so each LDS counter is advanced once per group of equal ids (same-address
+//    LDS atomics from 64 lanes would serialize).
+//      route_hist:  per-workgroup histogram (plus a count of out-of-range ids) -> workspace
+//                   [B][E+1];
+//      route_scan:  one workgroup: per expert, the exclusive prefix over workgroups (in place)
+//                   and the total; the padded segment lengths scanned into offs; the status;
+//      route_place: each workgroup re-counts its chunk per wavefront, takes its bases from
+//                   offs + the prefix, and places 64 assignments at a time in assignment order
+//                   (rank among equal ids + one LDS add per group); it also marks the pad rows
+//                   of the experts e = b, b + B, ... with -1.
+//    Bound by memory latency and launch overhead (three short launches), not bandwidth.
 //  * permute_kernel: one wavefront per padded row copies the token's BF16 row (16-byte
 //    loads and stores) or writes zeros for a pad row.
 // The fused gather + dual quantization (no BF16 copy) is a kind of the quantizer
@@ -24,51 +29,89 @@
 
 namespace mxf {
 
-constexpr int kPlanWaves = 16;
+constexpr int kPlanChunk = 1024;  // assignments per workgroup (4 wavefronts x 4 x 64)
 
-__global__ __launch_bounds__(1024) void route_plan_kernel(const int32_t* __restrict__ idx, int32_t n, int E,
-                                                          int pad, int64_t mcap, int32_t* __restrict__ offs,
-                                                          int32_t* __restrict__ counts,
-                                                          int32_t* __restrict__ row_assign,
-                                                          int32_t* __restrict__ assign_row, int32_t* status) {
-  extern __shared__ int32_t lds[];
-  int32_t* cnt = lds;                        // [kPlanWaves][E]: per-wavefront counts, then bases
-  int32_t* ecnt = cnt + kPlanWaves * E;      // [E] routed rows per expert
-  int32_t* eoff = ecnt + E;                  // [E + 1] segment starts
-  __shared__ int32_t wsum[kPlanWaves];
-  __shared__ int32_t bad_flag;
+// Lanes (with ok set) whose expert id equals this lane's: one ballot per bit of the id.
+__device__ __forceinline__ uint64_t same_expert(int e, bool ok, int nbits) {
+  uint64_t peers = __ballot(ok);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t m = __ballot(bit);
+    peers &= bit ? m : ~m;
+  }
+  return peers;
+}
+
+__device__ __forceinline__ int plan_nbits(int E) { return E > 1 ? 32 - __clz(E - 1) : 0; }
+
+// The 4 ids of this lane in its wavefront's quarter of workgroup b's chunk (-1 past n).
+__device__ __forceinline__ void load_ids(const int32_t* idx, int32_t n, int b, int w, int lane, int (&ev)[4]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t a = (int64_t)b * kPlanChunk + w * 256 + u * 64 + lane;
+    ev[u] = a < n ? idx[a] : -1;
+  }
+}
+
+// Per-wavefront counts of its 256 ids into cnt[E] (cnt[E] counts ids outside [0, E)).
+__device__ __forceinline__ void count_ids(const int (&ev)[4], int32_t n, int b, int w, int lane, int E,
+                                          int32_t* cnt) {
+  const int nbits = plan_nbits(E);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t a = (int64_t)b * kPlanChunk + w * 256 + u * 64 + lane;
+    const bool in = a < n;
+    const bool ok = in && (unsigned)ev[u] < (unsigned)E;
+    const uint64_t peers = same_expert(ev[u], ok, nbits);
+    if (ok && __ffsll((unsigned long long)peers) - 1 == lane) atomicAdd(&cnt[ev[u]], __popcll(peers));
+    const uint64_t badm = __ballot(in && !ok);
+    if (badm && lane == 0) atomicAdd(&cnt[E], __popcll(badm));
+  }
+}
+
+__global__ __launch_bounds__(256) void route_hist_kernel(const int32_t* __restrict__ idx, int32_t n, int E,
+                                                         int32_t* __restrict__ hist) {
+  extern __shared__ int32_t lds[];  // [E + 1]
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, b = blockIdx.x;
+  int ev[4];
+  load_ids(idx, n, b, w, lane, ev);
+  for (int e = tid; e <= E; e += 256) lds[e] = 0;
+  __syncthreads();
+  count_ids(ev, n, b, w, lane, E, lds);
+  __syncthreads();
+  for (int e = tid; e <= E; e += 256) hist[(int64_t)b * (E + 1) + e] = lds[e];
+}
+
+// One workgroup of 1024 threads; thread e <= E owns column e of hist [B][E+1].
+__global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ hist, int B, int E, int pad,
+                                                          int64_t mcap, int32_t* __restrict__ offs,
+                                                          int32_t* __restrict__ counts, int32_t* status) {
+  __shared__ int32_t wsum[16];
+  __shared__ int32_t etot[1025];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  for (int i = tid; i < kPlanWaves * E; i += 1024) cnt[i] = 0;
-  if (tid == 0) bad_flag = 0;
-  __syncthreads();
-
-  const int chunk = (int)(((int64_t)n + kPlanWaves * 64 - 1) / (kPlanWaves * 64) * 64);
-  const int a0 = (int)min<int64_t>((int64_t)w * chunk, n);
-  const int a1 = (int)min<int64_t>((int64_t)a0 + chunk, n);
-  int32_t* mine = cnt + w * E;
-  bool bad = false;
-  for (int a = a0 + lane; a < a1; a += 64) {
-    const int e = idx[a];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&mine[e], 1);
-    else bad = true;
-  }
-  if (bad) bad_flag = 1;
-  __syncthreads();
-
-  // per expert: total, and each wavefront's base inside the expert's segment
-  for (int e = tid; e < E; e += 1024) {
-    int run = 0;
-    for (int ww = 0; ww < kPlanWaves; ++ww) {
-      const int c = cnt[ww * E + e];
-      cnt[ww * E + e] = run;
-      run += c;
+  for (int col = tid; col <= E; col += 1024) {
+    int total = 0;
+    int b = 0;
+    for (; b + 8 <= B; b += 8) {
+      int v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = hist[(int64_t)(b + i) * (E + 1) + col];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        hist[(int64_t)(b + i) * (E + 1) + col] = total;
+        total += v[i];
+      }
     }
-    ecnt[e] = run;
+    for (; b < B; ++b) {
+      const int v = hist[(int64_t)b * (E + 1) + col];
+      hist[(int64_t)b * (E + 1) + col] = total;
+      total += v;
+    }
+    etot[col] = total;
   }
   __syncthreads();
-
-  // exclusive scan of the padded segment lengths (E <= 1024: one expert per thread)
-  const int c = tid < E ? ecnt[tid] : 0;
+  // exclusive scan of the padded segment lengths over experts (E <= 1024: one per thread)
+  const int c = tid < E ? etot[tid] : 0;
   const int seg = (c + pad - 1) / pad * pad;
   int incl = seg;
 #pragma unroll
@@ -81,29 +124,49 @@ __global__ __launch_bounds__(1024) void route_plan_kernel(const int32_t* __restr
   int wbase = 0;
   for (int ww = 0; ww < w; ++ww) wbase += wsum[ww];
   if (tid < E) {
-    eoff[tid] = wbase + incl - seg;
     offs[tid] = wbase + incl - seg;
     counts[tid] = c;
   }
   if (tid == 1023) {
-    eoff[E] = wbase + incl;
     offs[E] = wbase + incl;
+    if (status) *status = etot[E] ? 2 : ((int64_t)(wbase + incl) > mcap ? 3 : 0);
+  }
+}
+
+__global__ __launch_bounds__(256) void route_place_kernel(const int32_t* __restrict__ idx, int32_t n, int E,
+                                                          int64_t mcap, const int32_t* __restrict__ hist,
+                                                          const int32_t* __restrict__ offs,
+                                                          const int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ row_assign,
+                                                          int32_t* __restrict__ assign_row) {
+  extern __shared__ int32_t lds[];
+  int32_t* wc = lds;                 // [4][E + 1] per-wavefront counts, then bases
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, b = blockIdx.x;
+  int ev[4];
+  load_ids(idx, n, b, w, lane, ev);
+  for (int i = tid; i < 4 * (E + 1); i += 256) wc[i] = 0;
+  __syncthreads();
+  count_ids(ev, n, b, w, lane, E, wc + w * (E + 1));
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
+    int run = offs[e] + hist[(int64_t)b * (E + 1) + e];
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const int t = wc[ww * (E + 1) + e];
+      wc[ww * (E + 1) + e] = run;
+      run += t;
+    }
   }
   __syncthreads();
-
-  // stable placement, 64 assignments of the chunk at a time
-  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
-  for (int base = a0; base < a1; base += 64) {
-    const int a = base + lane;
-    const bool in = a < a1;
-    const int e = in ? idx[a] : -1;
+  int32_t* mine = wc + w * (E + 1);
+  const int nbits = plan_nbits(E);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t a = (int64_t)b * kPlanChunk + w * 256 + u * 64 + lane;
+    const bool in = a < n;
+    const int e = ev[u];
     const bool ok = in && (unsigned)e < (unsigned)E;
-    uint64_t peers = __ballot(ok);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t m = __ballot(bit);
-      peers &= bit ? m : ~m;
-    }
+    const uint64_t peers = same_expert(e, ok, nbits);
     const int rank = __popcll(peers & ((1ull << lane) - 1ull));
     const int leader = ok ? __ffsll((unsigned long long)peers) - 1 : lane;
     int first = 0;
@@ -112,22 +175,20 @@ __global__ __launch_bounds__(1024) void route_plan_kernel(const int32_t* __restr
     if (in) {
       int row = -1;
       if (ok) {
-        const int64_t r = (int64_t)eoff[e] + first + rank;
+        const int64_t r = (int64_t)first + rank;
         if (r < mcap) {
           row = (int)r;
-          row_assign[r] = a;
+          row_assign[r] = (int)a;
         }
       }
       assign_row[a] = row;
     }
   }
-
-  // pad rows of each expert (inside the capacity) map to -1
-  for (int e = w; e < E; e += kPlanWaves) {
-    const int64_t r1 = min<int64_t>(eoff[e + 1], mcap);
-    for (int64_t r = (int64_t)eoff[e] + ecnt[e] + lane; r < r1; r += 64) row_assign[r] = -1;
+  // pad rows (inside the capacity) of the experts e = b, b + B, ... map to -1
+  for (int e = b; e < E; e += gridDim.x) {
+    const int64_t r1 = min<int64_t>(offs[e + 1], mcap);
+    for (int64_t r = (int64_t)offs[e] + counts[e] + tid; r < r1; r += 256) row_assign[r] = -1;
   }
-  if (tid == 0 && status) *status = bad_flag ? 2 : ((int64_t)eoff[E] > mcap ? 3 : 0);
 }
 
 // One wavefront per row of the padded layout: row r < min(offs[E], mcap) gets token
@@ -158,20 +219,24 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint16_t* __restrict
 
 }  // namespace mxf
 
-size_t mxf_route_plan_lds_bytes(int E) { return (size_t)(mxf::kPlanWaves * E + 2 * E + 1) * sizeof(int32_t); }
+static int64_t plan_blocks(int64_t n) { return n > 0 ? (n + mxf::kPlanChunk - 1) / mxf::kPlanChunk : 1; }
+
+size_t mxf_route_plan_workspace_bytes(int64_t n, int E) { return (size_t)plan_blocks(n) * (E + 1) * sizeof(int32_t); }
 
 hipError_t mxf_launch_route_plan(const int32_t* idx, int32_t n, int E, int pad, int64_t mcap, int32_t* offs,
                                  int32_t* counts, int32_t* row_assign, int32_t* assign_row, int32_t* status,
-                                 hipStream_t st) {
-  const size_t lds = mxf_route_plan_lds_bytes(E);
-  if (lds > 65536) {
-    // above 64 KiB of dynamic LDS (E > 900) the kernel must opt in (gfx950 has 160 KiB per CU)
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mxf::route_plan_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(mxf::route_plan_kernel, dim3(1), dim3(1024), lds, st, idx, n, E, pad, mcap, offs, counts,
-                     row_assign, assign_row, status);
+                                 void* workspace, hipStream_t st) {
+  const int B = (int)plan_blocks(n);
+  int32_t* hist = (int32_t*)workspace;
+  hipLaunchKernelGGL(mxf::route_hist_kernel, dim3(B), dim3(256), (E + 1) * sizeof(int32_t), st, idx, n, E, hist);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(mxf::route_scan_kernel, dim3(1), dim3(1024), 0, st, hist, B, E, pad, mcap, offs, counts,
+                     status);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(mxf::route_place_kernel, dim3(B), dim3(256), 4 * (E + 1) * sizeof(int32_t), st, idx, n, E,
+                     mcap, hist, offs, counts, row_assign, assign_row);
   return hipGetLastError();
 }
 

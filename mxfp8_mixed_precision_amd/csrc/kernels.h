@@ -62,10 +62,10 @@ hipError_t mxf_launch_dequantize(const void* q, const void* s, int64_t rows, int
 hipError_t mxf_launch_pack13(const void* w1, const void* w3, void* w13, int64_t E, int64_t F,
                              int64_t D, bool pack, hipStream_t st);
 // dispatch.hip
-size_t mxf_route_plan_lds_bytes(int E);
+size_t mxf_route_plan_workspace_bytes(int64_t n, int E);
 hipError_t mxf_launch_route_plan(const int32_t* idx, int32_t n, int E, int pad, int64_t mcap, int32_t* offs,
                                  int32_t* counts, int32_t* row_assign, int32_t* assign_row, int32_t* status,
-                                 hipStream_t st);
+                                 void* workspace, hipStream_t st);
 hipError_t mxf_launch_permute(const void* x, int64_t n_assign, int topk, int64_t D, const int32_t* offs, int E,
                               const int32_t* row_assign, int64_t mcap, void* out, hipStream_t st);
 // gemm.hip

@@ -46,7 +46,10 @@ def route_plan(expert_idx, E, pad_multiple, m_capacity):
     ids = np.asarray(expert_idx, dtype=np.int64).reshape(-1)
     n = ids.size
     bad = bool(np.any((ids < 0) | (ids >= E)))
-    members = [[a for a in range(n) if ids[a] == e] for e in range(E)]
+    members = [[] for _ in range(E)]          # assignments of each expert, in ascending order
+    for a in range(n):
+        if 0 <= ids[a] < E:
+            members[ids[a]].append(a)
     counts = np.array([len(m) for m in members], dtype=np.int64)
     offs = np.zeros(E + 1, dtype=np.int64)
     for e in range(E):

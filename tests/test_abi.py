@@ -206,20 +206,25 @@ def test_dispatch_rejections_before_any_launch():
         with pytest.raises(mx.MxfError) as ei:
             fn(*a, stream=0)
         return ei.value.status
-    # mxf_route_plan(expert_idx, tokens, topk, E, pad, m_cap, offs, counts, row_assign, assign_row, status)
+    # mxf_route_plan(expert_idx, tokens, topk, E, pad, m_cap, offs, counts, row_assign, assign_row, status, ws)
     rp = mx.mxf_route_plan
-    assert st(rp, good, -1, 2, 4, 128, 256, good, good, good, good, None) == _abi.E_SHAPE      # tokens
-    assert st(rp, good, 8, 0, 4, 128, 256, good, good, good, good, None) == _abi.E_SHAPE       # topk
-    assert st(rp, good, 8, 65, 4, 128, 256, good, good, good, good, None) == _abi.E_SHAPE      # topk
-    assert st(rp, good, 1 << 29, 4, 4, 128, 256, good, good, good, good, None) == _abi.E_SHAPE  # 2^31 assignments
-    assert st(rp, good, 8, 2, 0, 128, 256, good, good, good, good, None) == _abi.E_SHAPE       # E
-    assert st(rp, good, 8, 2, 1025, 128, 256, good, good, good, good, None) == _abi.E_SHAPE    # E
-    assert st(rp, good, 8, 2, 4, 0, 256, good, good, good, good, None) == _abi.E_SHAPE         # pad
-    assert st(rp, good, 8, 2, 4, 128, -1, good, good, good, good, None) == _abi.E_SHAPE        # capacity
-    assert st(rp, None, 8, 2, 4, 128, 256, good, good, good, good, None) == _abi.E_NULL        # expert_idx
-    assert st(rp, good, 8, 2, 4, 128, 256, None, good, good, good, None) == _abi.E_NULL        # offs
-    assert st(rp, good, 8, 2, 4, 128, 256, good, good, None, good, None) == _abi.E_NULL        # row_assign
-    assert st(rp, good + 2, 8, 2, 4, 128, 256, good, good, good, good, None) == _abi.E_ALIGN   # expert_idx
+    assert st(rp, good, -1, 2, 4, 128, 256, good, good, good, good, None, good) == _abi.E_SHAPE      # tokens
+    assert st(rp, good, 8, 0, 4, 128, 256, good, good, good, good, None, good) == _abi.E_SHAPE       # topk
+    assert st(rp, good, 8, 65, 4, 128, 256, good, good, good, good, None, good) == _abi.E_SHAPE      # topk
+    assert st(rp, good, 1 << 29, 4, 4, 128, 256, good, good, good, good, None, good) == _abi.E_SHAPE  # 2^31 assignments
+    assert st(rp, good, 8, 2, 0, 128, 256, good, good, good, good, None, good) == _abi.E_SHAPE       # E
+    assert st(rp, good, 8, 2, 1025, 128, 256, good, good, good, good, None, good) == _abi.E_SHAPE    # E
+    assert st(rp, good, 8, 2, 4, 0, 256, good, good, good, good, None, good) == _abi.E_SHAPE         # pad
+    assert st(rp, good, 8, 2, 4, 128, -1, good, good, good, good, None, good) == _abi.E_SHAPE        # capacity
+    assert st(rp, None, 8, 2, 4, 128, 256, good, good, good, good, None, good) == _abi.E_NULL        # expert_idx
+    assert st(rp, good, 8, 2, 4, 128, 256, None, good, good, good, None, good) == _abi.E_NULL        # offs
+    assert st(rp, good, 8, 2, 4, 128, 256, good, good, None, good, None, good) == _abi.E_NULL        # row_assign
+    assert st(rp, good + 2, 8, 2, 4, 128, 256, good, good, good, good, None, good) == _abi.E_ALIGN   # expert_idx
+    assert st(rp, good, 8, 2, 4, 128, 256, good, good, good, good, None, None) == _abi.E_NULL        # workspace
+    assert mx.route_plan_workspace_bytes(8, 2, 4) == 4 * 5
+    assert mx.route_plan_workspace_bytes(1000, 8, 16) == 8 * 17 * 4
+    assert mx.route_plan_workspace_bytes(0, 8, 16) == 17 * 4
+    assert mx.route_plan_workspace_bytes(8, 2, 0) == 0 and mx.route_plan_workspace_bytes(8, 0, 4) == 0
     # mxf_dispatch_permute(x_tokens, tokens, topk, D, E, offs, row_assign, m_cap, x_out)
     dp = mx.mxf_dispatch_permute
     assert st(dp, good, 8, 2, 12, 4, good, good, 256, good) == _abi.E_SHAPE                  # D % 8

@@ -31,7 +31,8 @@ def gpu_plan(mx, ids, E, pad, mcap):
     ra = torch.full((max(mcap, 1),), SENT, dtype=torch.int32, device="cuda")
     ar = torch.full((max(tokens * topk, 1),), SENT, dtype=torch.int32, device="cuda")
     st = torch.full((1,), SENT, dtype=torch.int32, device="cuda")
-    mx.mxf_route_plan(d, tokens, topk, E, pad, mcap, offs, counts, ra, ar, st)
+    ws = torch.full((mx.route_plan_workspace_bytes(tokens, topk, E) // 4,), 12345, dtype=torch.int32, device="cuda")
+    mx.mxf_route_plan(d, tokens, topk, E, pad, mcap, offs, counts, ra, ar, st, ws)
     torch.cuda.synchronize()
     return dict(offs=offs.cpu().numpy(), counts=counts.cpu().numpy(), row_assign=ra.cpu().numpy()[:mcap],
                 assign_row=ar.cpu().numpy()[:tokens * topk], status=int(st.item()), dev=(offs, counts, ra))
@@ -64,6 +65,8 @@ PLAN_CASES = [
     ("E64_pad128", dict(seed=3, tokens=4096, topk=8, E=64, pad=128, zero=(0, 63))),
     ("E1024", dict(seed=4, tokens=20000, topk=8, E=1024, pad=128, zero=(5,))),
     ("few_tokens", dict(seed=5, tokens=3, topk=2, E=8, pad=256, zero=())),
+    ("many_blocks", dict(seed=6, tokens=40000, topk=6, E=64, pad=256, zero=(7,))),
+    ("E1024_big", dict(seed=8, tokens=70000, topk=4, E=1024, pad=128, zero=(0, 1023))),
 ]
 
 
