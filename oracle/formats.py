@@ -10,6 +10,11 @@ floating point and OCP MX v1.0 specifications:
   * E4M3: sign bit 7, exponent bits 6..3 with bias 7, mantissa bits 2..0;
     exponent field 0 is subnormal (m * 2^-9); S.1111.111 is NaN; no infinity;
     largest finite magnitude 0x7E = 448.
+  * E5M2 (the same page's description of the transport offers it as the
+    alternative element format to E4M3, under the same E8M0 block scale): sign bit 7,
+    exponent bits 6..2 with bias 15, mantissa bits 1..0; exponent field 0 is
+    subnormal (m * 2^-16); exponent field 31 is infinity (m = 0) or NaN;
+    largest finite magnitude 0x7B = 57344.
   * E8M0: an unsigned biased exponent, byte b -> 2^(b - 127); 0xFF is NaN.
     The third review on PR #475 (E8M0 decoding) pins the two endpoints: byte
     0x00 is 2^-127 (not zero) and 0xFF is NaN (not infinity).
@@ -17,6 +22,7 @@ floating point and OCP MX v1.0 specifications:
 import numpy as np
 
 E4M3_MAX = 448.0
+E5M2_MAX = 57344.0
 
 
 def bf16_bits_to_f64(bits):
@@ -87,6 +93,29 @@ E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
 def e4m3_to_f64(codes):
     """E4M3 bytes (uint8 array) -> fp64 values."""
     return E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def e5m2_value(code):
+    """Decode one E5M2 byte from its definition (see module docstring)."""
+    code = int(code)
+    s = code >> 7
+    e = (code >> 2) & 0x1F
+    m = code & 0x3
+    if e == 0x1F:
+        v = float("inf") if m == 0 else float("nan")
+    elif e == 0:
+        v = m * 2.0 ** -16
+    else:
+        v = (1.0 + m / 4.0) * 2.0 ** (e - 15)
+    return -v if s else v
+
+
+E5M2_TABLE = np.array([e5m2_value(c) for c in range(256)], dtype=np.float64)
+
+
+def e5m2_to_f64(codes):
+    """E5M2 bytes (uint8 array) -> fp64 values."""
+    return E5M2_TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
 def e8m0_to_f64(b):

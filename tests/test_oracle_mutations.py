@@ -113,3 +113,21 @@ def test_dispatch_mutations_are_caught(monkeypatch):
     monkeypatch.setattr(dispatch, "permute", k_major)
     assert _fails(td.test_tiny_workload_layout_is_the_dispatch_of_its_tokens)
     assert _fails(td.test_hand_worked_dispatch)
+
+
+def test_e5m2_mutations_are_caught(monkeypatch):
+    import test_oracle_e5m2 as te
+    good = mx.e5m2_rne_sat
+
+    def to_inf(y):                      # overflow to infinity instead of saturating
+        c = good(y)
+        big = np.abs(np.asarray(y, dtype=np.float64)) > 57344.0
+        return np.where(big, (c & 0x80) | 0x7C, c).astype(np.uint8)
+
+    monkeypatch.setattr(mx, "e5m2_rne_sat", to_inf)
+    monkeypatch.setattr(te, "e5m2_rne_sat", to_inf)
+    assert _fails(te.test_brute_force_all_bf16, 239) or _fails(te.test_saturation_beyond_top_binade)
+    monkeypatch.undo()
+    sb = mx.scale_byte
+    monkeypatch.setattr(mx, "scale_byte", lambda a, emax=8: sb(a, 14 if emax == 15 else emax))   # E4M3-like emax slip
+    assert _fails(te.test_closed_forms, 0)
