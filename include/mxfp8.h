@@ -86,9 +86,13 @@ const char* mxf_last_error(void);
 
 #define MXF_ROW 1u   /* groups along each row    -> q_row [rows, cols], s_row [rows, cols/32] */
 #define MXF_COL 2u   /* groups along each column -> q_col [cols, rows], s_col [cols, rows/32] */
+#define MXF_E5M2 4u  /* mode flag: E5M2 elements instead of E4M3 (see below) */
 
 /* MXFP8 quantization of a row-major BF16 matrix x [rows, cols] (see top of file).
- * mode: MXF_ROW, MXF_COL or both (dual: x is read once).
+ * mode: MXF_ROW, MXF_COL or both (dual: x is read once), optionally | MXF_E5M2: E5M2 elements
+ * (the alternative element format afd-plugin PR #475 offers for the transport, under the same
+ * E8M0 scale): scale exponent floor(log2(amax)) - 15, codes RNE saturated to +-57344
+ * (0x7B | sign), NaN groups 0xFF with codes 0x7F | sign.
  * Requires cols % 32 == 0; with MXF_COL also rows % 32 == 0; rows, cols >= 0. An empty matrix
  * (rows or cols 0) is a no-op that accepts NULL pointers.
  * Outputs not selected by mode may be NULL. All outputs are dense row-major u8 arrays.
@@ -101,6 +105,7 @@ mxf_status mxfp8_quantize(const void* x, int64_t rows, int64_t cols, uint32_t mo
 
 #define MXF_DEQ_BF16 0u  /* out is BF16 */
 #define MXF_DEQ_F32 1u   /* out is FP32 */
+#define MXF_DEQ_E5M2 2u  /* flag: the codes are E5M2 (field 31: +-Inf for mantissa 0, else NaN) */
 
 /* Decode of row-wise MXFP8 (the receive side of an MXFP8 transport; afd-plugin PR #475
  * "quantize the A2E FFN transport to MXFP8", third review on E8M0 decoding and on hidden sizes
@@ -108,7 +113,7 @@ mxf_status mxfp8_quantize(const void* x, int64_t rows, int64_t cols, uint32_t mo
  * q [rows, cols] u8 E4M3 codes; s [rows, ceil(cols/32)] u8 E8M0 bytes: element (r, c) uses
  * s[r, c / 32], so when cols % 32 != 0 the last group of a row is short and has its own byte.
  * out [rows, cols] row-major = E4M3(q) * 2^(s - 127) rounded once (RNE) to BF16 or FP32
- * (out_type MXF_DEQ_BF16 / MXF_DEQ_F32); overflow gives +-Inf. Scale byte 0x00 is 2^-127
+ * (out_type MXF_DEQ_BF16 / MXF_DEQ_F32, | MXF_DEQ_E5M2 for E5M2 codes); overflow gives +-Inf. Scale byte 0x00 is 2^-127
  * (not zero), 0xFF is NaN (the whole group decodes to NaN); codes 0x7F / 0xFF are NaN (the sign
  * and payload of a NaN result are unspecified).
  * Any rows, cols >= 0 (empty is a no-op accepting NULL); q and out 16-byte aligned.

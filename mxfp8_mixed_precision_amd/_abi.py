@@ -20,9 +20,9 @@ STATUS_NAMES = {OK: "MXF_OK", E_NULL: "MXF_E_NULL", E_SHAPE: "MXF_E_SHAPE", E_AL
                 E_DEVICE: "MXF_E_DEVICE", E_ARG: "MXF_E_ARG", E_HIP: "MXF_E_HIP"}
 DEV_OK, DEV_BAD_OFFSETS, DEV_BAD_EXPERT, DEV_OVERFLOW = 0, 1, 2, 3
 CAP_GFX950 = 1
-ROW, COL = 1, 2
+ROW, COL, E5M2 = 1, 2, 4
 OUT_F32, DEBUG_F32, SERIAL, UNFUSED, X_QUANTIZED = 1, 2, 4, 8, 16
-DEQ_BF16, DEQ_F32 = 0, 1
+DEQ_BF16, DEQ_F32, DEQ_E5M2 = 0, 1, 2
 
 # tensor ids (mxf_tensor)
 TENSORS = ["STATUS", "XQ_R", "XS_R", "XQ_C", "XS_C", "W13Q_R", "W13S_R", "W13Q_C", "W13S_C",
@@ -145,7 +145,8 @@ def mxfp8_quantize(x, rows, cols, mode, q_row=None, s_row=None, q_col=None, s_co
 
 
 def quantize(x, mode=ROW | COL, stream=None):
-    """Quantize a 2-D BF16 CUDA tensor; allocates and returns (q_row, s_row, q_col, s_col)."""
+    """Quantize a 2-D BF16 CUDA tensor (mode may include E5M2); allocates and returns
+    (q_row, s_row, q_col, s_col)."""
     import torch
     assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.is_contiguous()
     rows, cols = x.shape
@@ -166,16 +167,18 @@ def mxfp8_dequantize(q, s, rows, cols, out_type, out, stream=None):
     _check(lib().mxfp8_dequantize(_ptr(q), _ptr(s), rows, cols, out_type, _ptr(out), _stream(stream)))
 
 
-def dequantize(q, s, out_dtype=None, stream=None):
-    """Decode row-wise MXFP8 codes q [rows, cols] u8 with scales s [rows, ceil(cols/32)] u8
-    (CUDA tensors); allocates and returns a BF16 (default) or FP32 tensor."""
+def dequantize(q, s, out_dtype=None, e5m2=False, stream=None):
+    """Decode row-wise MXFP8 codes q [rows, cols] u8 (E4M3, or E5M2 with e5m2=True) with
+    scales s [rows, ceil(cols/32)] u8 (CUDA tensors); allocates and returns a BF16 (default)
+    or FP32 tensor."""
     import torch
     out_dtype = out_dtype or torch.bfloat16
     assert q.dtype == torch.uint8 and q.dim() == 2 and q.is_contiguous()
     rows, cols = q.shape
     assert s.dtype == torch.uint8 and s.is_contiguous() and tuple(s.shape) == (rows, -(-cols // 32))
     out = torch.empty((rows, cols), dtype=out_dtype, device=q.device)
-    mxfp8_dequantize(q, s, rows, cols, DEQ_BF16 if out_dtype == torch.bfloat16 else DEQ_F32, out, stream)
+    kind = (DEQ_BF16 if out_dtype == torch.bfloat16 else DEQ_F32) | (DEQ_E5M2 if e5m2 else 0)
+    mxfp8_dequantize(q, s, rows, cols, kind, out, stream)
     return out
 
 

@@ -234,8 +234,10 @@ mxf_status mxf_query_device(int device, uint32_t* caps) {
 mxf_status mxfp8_quantize(const void* x, int64_t rows, int64_t cols, uint32_t mode, void* q_row,
                           void* s_row, void* q_col, void* s_col, void* stream) {
   g_err.clear();
-  if (mode == 0 || (mode & ~(uint32_t)(MXF_ROW | MXF_COL)))
-    return fail(MXF_E_ARG, "mode = %u: must be MXF_ROW, MXF_COL or both", mode);
+  if ((mode & (MXF_ROW | MXF_COL)) == 0 || (mode & ~(uint32_t)(MXF_ROW | MXF_COL | MXF_E5M2)))
+    return fail(MXF_E_ARG, "mode = %u: must be MXF_ROW, MXF_COL or both, optionally | MXF_E5M2", mode);
+  const bool e5m2 = (mode & MXF_E5M2) != 0;
+  mode &= MXF_ROW | MXF_COL;
   if (rows < 0 || cols < 0) return fail(MXF_E_SHAPE, "rows = %lld, cols = %lld: negative", (long long)rows, (long long)cols);
   if (cols % 32) return fail(MXF_E_SHAPE, "cols = %lld: must be a multiple of 32", (long long)cols);
   if ((mode & MXF_COL) && rows % 32)
@@ -252,7 +254,7 @@ mxf_status mxfp8_quantize(const void* x, int64_t rows, int64_t cols, uint32_t mo
   mxf_status s = check_device();
   if (s != MXF_OK) return s;
   MXF_HIP(timed("quantize", (hipStream_t)stream, [&] {
-            return mxf_launch_quantize(x, rows, cols, mode, q_row, s_row, q_col, s_col, (hipStream_t)stream);
+            return mxf_launch_quantize(x, rows, cols, mode, e5m2, q_row, s_row, q_col, s_col, (hipStream_t)stream);
           }), "quantize launch");
   return MXF_OK;
 }
@@ -260,8 +262,8 @@ mxf_status mxfp8_quantize(const void* x, int64_t rows, int64_t cols, uint32_t mo
 mxf_status mxfp8_dequantize(const void* q, const void* s, int64_t rows, int64_t cols, uint32_t out_type,
                             void* out, void* stream) {
   g_err.clear();
-  if (out_type != MXF_DEQ_BF16 && out_type != MXF_DEQ_F32)
-    return fail(MXF_E_ARG, "out_type = %u: must be MXF_DEQ_BF16 or MXF_DEQ_F32", out_type);
+  if (out_type & ~(uint32_t)(MXF_DEQ_F32 | MXF_DEQ_E5M2))
+    return fail(MXF_E_ARG, "out_type = %u: must be MXF_DEQ_BF16 or MXF_DEQ_F32, optionally | MXF_DEQ_E5M2", out_type);
   if (rows < 0 || cols < 0) return fail(MXF_E_SHAPE, "rows = %lld, cols = %lld: negative", (long long)rows, (long long)cols);
   if (rows > ((int64_t)1 << 40) / (cols > 0 ? cols : 1))
     return fail(MXF_E_SHAPE, "rows = %lld, cols = %lld: more than 2^40 elements", (long long)rows, (long long)cols);
@@ -272,7 +274,8 @@ mxf_status mxfp8_dequantize(const void* q, const void* s, int64_t rows, int64_t 
   mxf_status st = check_device();
   if (st != MXF_OK) return st;
   MXF_HIP(timed("dequantize", (hipStream_t)stream, [&] {
-            return mxf_launch_dequantize(q, s, rows, cols, out_type == MXF_DEQ_BF16, out, (hipStream_t)stream);
+            return mxf_launch_dequantize(q, s, rows, cols, (out_type & MXF_DEQ_F32) == 0, (out_type & MXF_DEQ_E5M2) != 0,
+                                         out, (hipStream_t)stream);
           }), "dequantize launch");
   return MXF_OK;
 }

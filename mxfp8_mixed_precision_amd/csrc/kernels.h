@@ -39,7 +39,7 @@ struct GemmParams {
 }  // namespace mxf
 
 // quantize.hip
-hipError_t mxf_launch_quantize(const void* x, int64_t rows, int64_t cols, uint32_t mode, void* q_row,
+hipError_t mxf_launch_quantize(const void* x, int64_t rows, int64_t cols, uint32_t mode, bool e5m2, void* q_row,
                                void* s_row, void* q_col, void* s_col, hipStream_t st);
 hipError_t mxf_launch_quant_tokens(const void* x, int64_t mcap, int64_t D, const int32_t* offs,
                                    const int32_t* counts, int E, int pad, void* q_r, void* s_r,
@@ -57,7 +57,7 @@ hipError_t mxf_launch_quant_gather(const void* x_tokens, int64_t n_assign, int t
                                    int64_t mcap, int64_t D, const int32_t* offs, const int32_t* counts, int E,
                                    int pad, void* q_r, void* s_r, void* q_c, void* s_c, int32_t* status,
                                    hipStream_t st);
-hipError_t mxf_launch_dequantize(const void* q, const void* s, int64_t rows, int64_t cols, bool bf16,
+hipError_t mxf_launch_dequantize(const void* q, const void* s, int64_t rows, int64_t cols, bool bf16, bool e5m2,
                                  void* out, hipStream_t st);
 hipError_t mxf_launch_pack13(const void* w1, const void* w3, void* w13, int64_t E, int64_t F,
                              int64_t D, bool pack, hipStream_t st);

@@ -45,7 +45,14 @@ struct Scale {
   uint32_t byte;     // E8M0 byte
 };
 
+// Element formats: FMT_E4M3 (emax 8, largest 448 = 1.75 * 2^8) and FMT_E5M2 (emax 15, largest
+// 57344 = 1.75 * 2^15). The rule is the same with the format's emax; the clamp limit is
+// 1.75 * 2^(e + emax) and both formats' NaN code is 0x7F | sign.
+enum { FMT_E4M3 = 0, FMT_E5M2 = 1 };
+
+template <int FMT = FMT_E4M3>
 __device__ __forceinline__ Scale scale_from_amax(uint32_t amax_bits) {
+  constexpr uint32_t EMAX = FMT == FMT_E5M2 ? 15u : 8u;
   const uint32_t ef = amax_bits >> 7;
   Scale s;
   if (ef >= 255u) {
@@ -54,8 +61,8 @@ __device__ __forceinline__ Scale scale_from_amax(uint32_t amax_bits) {
     s.xf = 1.0f;
     s.nanmask = 0x7F7F7F7Fu;
   } else {
-    const uint32_t byte = ef > 8u ? ef - 8u : 0u;
-    const uint32_t lim = ((byte + 8u) << 7) | 0x60u;
+    const uint32_t byte = ef > EMAX ? ef - EMAX : 0u;
+    const uint32_t lim = ((byte + EMAX) << 7) | 0x60u;
     s.byte = byte;
     s.lim2 = lim | (lim << 16);
     s.xf = __uint_as_float(byte ? (byte << 23) : 0x00400000u);
@@ -69,18 +76,24 @@ __device__ __forceinline__ uint32_t mag2(uint32_t v) { return v & 0x7FFF7FFFu; }
 
 // Two packed BF16 (lo, hi) -> two E4M3 codes written into the low (hi=false) or high
 // (hi=true) 16 bits of `old`.
-template <bool HI>
+template <bool HI, int FMT = FMT_E4M3>
 __device__ __forceinline__ uint32_t cvt2(uint32_t old, uint32_t v, const Scale& s) {
   const uint32_t c = (v & 0x80008000u) | pk_min_u16(v & 0x7FFF7FFFu, s.lim2);
-  s16x2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(__builtin_bit_cast(s16x2, old),
-                                                       __builtin_bit_cast(bf16x2, c), s.xf, HI);
+  s16x2 r;
+  if constexpr (FMT == FMT_E5M2)
+    r = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(__builtin_bit_cast(s16x2, old), __builtin_bit_cast(bf16x2, c),
+                                                  s.xf, HI);
+  else
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(__builtin_bit_cast(s16x2, old), __builtin_bit_cast(bf16x2, c),
+                                                  s.xf, HI);
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// Four BF16 (two packed words) -> four E4M3 codes in one word (byte i = element i).
+// Four BF16 (two packed words) -> four codes in one word (byte i = element i).
+template <int FMT = FMT_E4M3>
 __device__ __forceinline__ uint32_t cvt4(uint32_t v01, uint32_t v23, const Scale& s) {
-  uint32_t r = cvt2<false>(0u, v01, s);
-  r = cvt2<true>(r, v23, s);
+  uint32_t r = cvt2<false, FMT>(0u, v01, s);
+  r = cvt2<true, FMT>(r, v23, s);
   return r | s.nanmask;
 }
 

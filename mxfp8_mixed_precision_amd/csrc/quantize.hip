@@ -52,7 +52,7 @@ struct QuantParams {
 };
 
 
-template <int KIND, bool ROW, bool COL>
+template <int KIND, bool ROW, bool COL, int FMT = FMT_E4M3>
 __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
   // Column codes of the block, transposed [128 columns][QTP bytes], and the block's scale
   // words (4 groups of a row / of a column), staged in LDS so that every global store is a
@@ -159,9 +159,9 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
       m = max(m & 0xFFFFu, m >> 16);
       m = max(m, dpp_xor1(m));
       m = max(m, dpp_xor2(m));
-      const Scale sc = scale_from_amax(m);
-      const uint32_t lo = cvt4(x[j][0], x[j][1], sc);
-      const uint32_t hi = cvt4(x[j][2], x[j][3], sc);
+      const Scale sc = scale_from_amax<FMT>(m);
+      const uint32_t lo = cvt4<FMT>(x[j][0], x[j][1], sc);
+      const uint32_t hi = cvt4<FMT>(x[j][2], x[j][3], sc);
       const int64_t r = r0 + j;
       if (colok && r < p.rows) *reinterpret_cast<uint2*>(q_r + r * p.cols + col) = make_uint2(lo, hi);
       if ((c & 3) == 0) srow_b[(r - row0) * 4 + (c >> 2)] = (uint8_t)sc.byte;
@@ -176,12 +176,12 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
       for (int j = 1; j < 8; ++j) m = pk_max_u16(m, mag2(x[j][k]));
       m = pk_max_u16(m, (uint32_t)__shfl_xor((int)m, 16));
       m = pk_max_u16(m, (uint32_t)__shfl_xor((int)m, 32));
-      const Scale slo = scale_from_amax(m & 0xFFFFu);
-      const Scale shi = scale_from_amax(m >> 16);
-      const uint32_t a0 = cvt4(pack_lo(x[0][k], x[1][k]), pack_lo(x[2][k], x[3][k]), slo);
-      const uint32_t a1 = cvt4(pack_lo(x[4][k], x[5][k]), pack_lo(x[6][k], x[7][k]), slo);
-      const uint32_t b0 = cvt4(pack_hi(x[0][k], x[1][k]), pack_hi(x[2][k], x[3][k]), shi);
-      const uint32_t b1 = cvt4(pack_hi(x[4][k], x[5][k]), pack_hi(x[6][k], x[7][k]), shi);
+      const Scale slo = scale_from_amax<FMT>(m & 0xFFFFu);
+      const Scale shi = scale_from_amax<FMT>(m >> 16);
+      const uint32_t a0 = cvt4<FMT>(pack_lo(x[0][k], x[1][k]), pack_lo(x[2][k], x[3][k]), slo);
+      const uint32_t a1 = cvt4<FMT>(pack_lo(x[4][k], x[5][k]), pack_lo(x[6][k], x[7][k]), slo);
+      const uint32_t b0 = cvt4<FMT>(pack_hi(x[0][k], x[1][k]), pack_hi(x[2][k], x[3][k]), shi);
+      const uint32_t b1 = cvt4<FMT>(pack_hi(x[4][k], x[5][k]), pack_hi(x[6][k], x[7][k]), shi);
       const int cl = c * 8 + 2 * k;  // block-local column
       const int rl = w * 32 + 8 * s;  // block-local row
       *reinterpret_cast<uint2*>(qT + cl * QTP + rl) = make_uint2(a0, a1);
@@ -247,16 +247,35 @@ __device__ __forceinline__ float e4m3_f32(uint32_t c) {
   return __uint_as_float((c & 0x7Fu) == 0x7Fu ? nan : (e == 0 ? sub : normal));
 }
 
+// E5M2 code -> its exact fp32 value, from the bit fields (OCP FP8): exponent field 0 is m * 2^-16,
+// field 31 is infinity (m = 0) or NaN, otherwise (1 + m/4) * 2^(e-15), i.e. fp32 exponent field
+// e + 112.
+__device__ __forceinline__ float e5m2_f32(uint32_t c) {
+  const uint32_t sign = (c & 0x80u) << 24;
+  const uint32_t e = (c >> 2) & 0x1Fu, m = c & 3u;
+  const uint32_t normal = sign | ((e + 112u) << 23) | (m << 21);
+  const uint32_t sub = sign | __float_as_uint((float)m * 1.52587890625e-05f);  // m * 2^-16, exact
+  const uint32_t special = sign | (m == 0 ? 0x7F800000u : 0x7FC00000u);
+  return __uint_as_float(e == 31u ? special : (e == 0 ? sub : normal));
+}
+
+template <int FMT>
+__device__ __forceinline__ float code_f32(uint32_t c) {
+  if constexpr (FMT == FMT_E5M2) return e5m2_f32(c);
+  else return e4m3_f32(c);
+}
+
 // E8M0 byte -> 2^(b - 127) as fp32: 0x00 is the subnormal 2^-127 (bits 0x00400000), 0xFF is NaN.
 __device__ __forceinline__ float e8m0_f32(uint32_t b) {
   return __uint_as_float(b == 0xFFu ? 0x7FC00000u : (b == 0u ? 0x00400000u : b << 23));
 }
 
-// out[r, c] = E4M3(q[r, c]) * E8M0(s[r, c / 32]) rounded once to BF16 or FP32. The fp32 product
-// of a 4-significant-bit code and a power of two is exact whenever it is in range (down to
-// 2^-136 = 2^-9 * 2^-127, an fp32 subnormal), so the only rounding is the output conversion.
-// Rows of 16-multiple width take 16 codes per thread; other widths one code per thread.
-template <bool BF16>
+// out[r, c] = code(q[r, c]) * E8M0(s[r, c / 32]) rounded once to BF16 or FP32, the code being
+// E4M3 or E5M2. The fp32 product of a code (at most 4 significant bits) and a power of two is
+// exact whenever it is in range (down to 2^-136 = 2^-9 * 2^-127 for E4M3 and 2^-143 for E5M2,
+// fp32 subnormals), so the only rounding is the output conversion. Rows of 16-multiple width
+// take 16 codes per thread; other widths one code per thread.
+template <bool BF16, int FMT>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* q, const uint8_t* s, int64_t rows,
                                                       int64_t cols, void* out) {
   const int64_t G = (cols + 31) >> 5;  // scale bytes per row (the last group may be short)
@@ -271,7 +290,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* q, const ui
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
       float f[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) f[i] = e4m3_f32((w[i >> 2] >> (8 * (i & 3))) & 0xFFu) * sc;
+      for (int i = 0; i < 16; ++i) f[i] = code_f32<FMT>((w[i >> 2] >> (8 * (i & 3))) & 0xFFu) * sc;
       if (BF16) {
         uint32_t h[8];
 #pragma unroll
@@ -289,7 +308,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* q, const ui
     const int64_t total = rows * cols;
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
       const int64_t r = t / cols, c = t - r * cols;
-      const float f = e4m3_f32(q[t]) * e8m0_f32(s[r * G + (c >> 5)]);
+      const float f = code_f32<FMT>(q[t]) * e8m0_f32(s[r * G + (c >> 5)]);
       if (BF16) reinterpret_cast<uint16_t*>(out)[t] = (uint16_t)bf16_bits(f);
       else reinterpret_cast<float*>(out)[t] = f;
     }
@@ -325,14 +344,18 @@ __global__ __launch_bounds__(256) void pack13_kernel(const uint16_t* a, const ui
 // ------------------------------------------------------------------ host launchers
 
 static hipError_t launch_quant(int kind, uint32_t mode, const QuantParams& p, int64_t batch,
-                               hipStream_t st) {
+                               hipStream_t st, bool e5m2 = false) {
   // the token-layout kind always runs (its first block writes the status word)
   if ((p.rows == 0 || p.cols == 0 || batch == 0) && kind != QK_MASKED && kind != QK_GATHER) return hipSuccess;
   const int64_t rt = (p.rows + 127) / 128, ct = (p.cols + 127) / 128;
   const dim3 grid((unsigned)(rt > 0 ? rt : 1), (unsigned)(ct > 0 ? ct : 1), (unsigned)(batch > 0 ? batch : 1));
   const dim3 block(256);
 #define MXF_QLAUNCH(K, R, C) hipLaunchKernelGGL((quant_dual_kernel<K, R, C>), grid, block, 0, st, p)
-  if (kind == QK_PLAIN) {
+  if (kind == QK_PLAIN && e5m2) {
+    if (mode == 3) hipLaunchKernelGGL((quant_dual_kernel<QK_PLAIN, true, true, FMT_E5M2>), grid, block, 0, st, p);
+    else if (mode == 1) hipLaunchKernelGGL((quant_dual_kernel<QK_PLAIN, true, false, FMT_E5M2>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((quant_dual_kernel<QK_PLAIN, false, true, FMT_E5M2>), grid, block, 0, st, p);
+  } else if (kind == QK_PLAIN) {
     if (mode == 3) MXF_QLAUNCH(QK_PLAIN, true, true);
     else if (mode == 1) MXF_QLAUNCH(QK_PLAIN, true, false);
     else MXF_QLAUNCH(QK_PLAIN, false, true);
@@ -354,7 +377,7 @@ static hipError_t launch_quant(int kind, uint32_t mode, const QuantParams& p, in
 }  // namespace mxf
 
 // Internal entry points used by the C ABI layer (abi.hip).
-hipError_t mxf_launch_quantize(const void* x, int64_t rows, int64_t cols, uint32_t mode, void* q_row,
+hipError_t mxf_launch_quantize(const void* x, int64_t rows, int64_t cols, uint32_t mode, bool e5m2, void* q_row,
                                void* s_row, void* q_col, void* s_col, hipStream_t st) {
   mxf::QuantParams p = {};
   p.src = (const uint16_t*)x;
@@ -367,7 +390,7 @@ hipError_t mxf_launch_quantize(const void* x, int64_t rows, int64_t cols, uint32
   p.ldc = rows;
   p.sr_rs = cols / 32; p.sr_kbs = 4;  // row-major scales
   p.sc_rs = rows / 32; p.sc_kbs = 4;
-  return mxf::launch_quant(mxf::QK_PLAIN, mode, p, 1, st);
+  return mxf::launch_quant(mxf::QK_PLAIN, mode, p, 1, st, e5m2);
 }
 
 // Dual quantization of the activation-like operand x [mcap, D] under the token layout
@@ -480,17 +503,21 @@ hipError_t mxf_launch_quant_weights(const void* w, const void* w3, bool pack13, 
   return mxf::launch_quant(pack13 ? mxf::QK_PACK13 : mxf::QK_PLAIN, 3, p, E, st);
 }
 
-hipError_t mxf_launch_dequantize(const void* q, const void* s, int64_t rows, int64_t cols, bool bf16,
+hipError_t mxf_launch_dequantize(const void* q, const void* s, int64_t rows, int64_t cols, bool bf16, bool e5m2,
                                  void* out, hipStream_t st) {
   const int64_t units = (cols % 16 == 0) ? rows * (cols / 16) : rows * cols;
   if (units == 0) return hipSuccess;
-  const int64_t blocks = std::min<int64_t>((units + 255) / 256, 8192);
-  if (bf16)
-    hipLaunchKernelGGL(mxf::dequant_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st, (const uint8_t*)q,
-                       (const uint8_t*)s, rows, cols, out);
+  const dim3 grid((unsigned)std::min<int64_t>((units + 255) / 256, 8192));
+  const uint8_t* qq = (const uint8_t*)q;
+  const uint8_t* ss = (const uint8_t*)s;
+  if (bf16 && !e5m2)
+    hipLaunchKernelGGL((mxf::dequant_kernel<true, mxf::FMT_E4M3>), grid, dim3(256), 0, st, qq, ss, rows, cols, out);
+  else if (!e5m2)
+    hipLaunchKernelGGL((mxf::dequant_kernel<false, mxf::FMT_E4M3>), grid, dim3(256), 0, st, qq, ss, rows, cols, out);
+  else if (bf16)
+    hipLaunchKernelGGL((mxf::dequant_kernel<true, mxf::FMT_E5M2>), grid, dim3(256), 0, st, qq, ss, rows, cols, out);
   else
-    hipLaunchKernelGGL(mxf::dequant_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st, (const uint8_t*)q,
-                       (const uint8_t*)s, rows, cols, out);
+    hipLaunchKernelGGL((mxf::dequant_kernel<false, mxf::FMT_E5M2>), grid, dim3(256), 0, st, qq, ss, rows, cols, out);
   return hipGetLastError();
 }
 
