@@ -196,11 +196,15 @@ __device__ __forceinline__ bool offsets_valid(const int32_t* offs, const int32_t
 // answers. For E >= 64 the members fall back to the looping helpers.
 struct Offsets {
   const int32_t* offs;
+  const int32_t* counts;
   int E;
   int32_t o;     // offs[lane] (lanes 0..E)
+  int32_t c;     // real rows of expert lane - 1 (lanes 1..E)
   bool ok;
   int64_t mend;  // offs[E]
   __device__ __forceinline__ int expert(int64_t m) const;
+  // end of expert e's real rows, offs[e] + counts[e] (e wavefront-uniform)
+  __device__ __forceinline__ int64_t real_end(int e) const;
 };
 
 __device__ __forceinline__ bool offsets_valid(const int32_t* offs, const int32_t* counts, int E,
@@ -224,8 +228,10 @@ __device__ __forceinline__ Offsets read_offsets(const int32_t* offs, const int32
                                                 int64_t mcap) {
   Offsets r;
   r.offs = offs;
+  r.counts = counts;
   r.E = E;
   r.o = 0;
+  r.c = 0;
   if (E >= 64) {
     r.ok = offsets_valid(offs, counts, E, pad, mcap);
     r.mend = r.ok ? offs[E] : 0;
@@ -246,9 +252,15 @@ __device__ __forceinline__ Offsets read_offsets(const int32_t* offs, const int32
     }
   }
   r.o = o;
+  r.c = counts ? c : o - prev;
   r.ok = !__any(bad);
   r.mend = __builtin_amdgcn_readlane(o, E);  // uniform (SGPR) copy
   return r;
+}
+
+__device__ __forceinline__ int64_t Offsets::real_end(int e) const {
+  if (E >= 64) return (int64_t)offs[e] + (counts ? counts[e] : offs[e + 1] - offs[e]);
+  return (int64_t)__builtin_amdgcn_readlane(o, e) + __builtin_amdgcn_readlane(c, e + 1);
 }
 
 __device__ __forceinline__ int Offsets::expert(int64_t m) const {
