@@ -157,6 +157,11 @@ typedef struct {
  * 1 up; b < 2, c < 32, k < 4, j < 4) holds row 32R + 8k + 4b + j, column 32J + c of the
  * gate (s = 0) or up (s = 1) projection. Same size as [Mcap, 2F].
  *
+ * Every code tensor below (…Q_R, …Q_C; the shapes listed are [R, K], per expert for the
+ * weights, K the axis the 32-groups run along) is stored in 64-k panels, the order the GEMM
+ * loads it in: the byte of (row r, column k) is at (k / 64) * 64R + 64r + k % 64, so 64 k of
+ * 16 consecutive rows are one contiguous kilobyte. Same size as [R, K].
+ *
  * Every scale tensor below (…S_R, …S_C) holds the E8M0 bytes of a code tensor with R rows
  * and K columns (the shapes listed are [R, K/32], per expert for the weights) in 128-k
  * planes, the order the GEMM loads them in: the byte of (row r, 32-group g) is at

@@ -34,6 +34,9 @@ _SHAPES = {
 }
 
 
+_PANEL_CODES = ("XQ_R", "XQ_C", "W13Q_R", "W13Q_C", "W2Q_R", "W2Q_C", "HQ_R", "HQ_C", "DYQ_R", "DYQ_C",
+                "DHQ_R", "DHQ_C")
+
 _PLANE_SCALES = ("XS_R", "XS_C", "W13S_R", "W13S_C", "W2S_R", "W2S_C", "HS_R", "HS_C", "DYS_R", "DYS_C",
                  "DHS_R", "DHS_C")
 
@@ -45,6 +48,15 @@ def scales_rowmajor(planes, shape):
     t = planes.reshape(*lead, G // 4, R, 4)
     n = len(lead)
     return t.permute(*range(n), n + 1, n, n + 2).reshape(*lead, R, G)
+
+
+def codes_rowmajor(panels, shape):
+    """Row-major copy [..., R, K] of a code tensor stored in 64-k panels [..., K/64, R, 64]
+    (byte of row r, column k at (k / 64) * 64R + 64r + k % 64; leading dims are experts)."""
+    *lead, R, K = shape
+    t = panels.reshape(*lead, K // 64, R, 64)
+    n = len(lead)
+    return t.permute(*range(n), n + 1, n, n + 2).reshape(*lead, R, K)
 
 
 def h13_rowmajor(tiled, F):
@@ -83,8 +95,9 @@ class MlpContext:
 
     def view(self, name):
         """A typed view of documented tensor `name` inside saved / workspace. H13 (stored
-        fragment-tiled) and the scale tensors (stored in 128-k planes; include/mxfp8.h) are
-        returned as row-major copies: [m_capacity, 2F] BF16 and [..., R, K/32] bytes."""
+        fragment-tiled), the code tensors (stored in 64-k panels) and the scale tensors (stored
+        in 128-k planes; include/mxfp8.h) are returned as row-major copies: [m_capacity, 2F]
+        BF16, [..., R, K] and [..., R, K/32] bytes."""
         import torch
         raw = self.view_raw(name)
         shape = _SHAPES[name](self.E, self.D, self.F, self.m_capacity)
@@ -96,6 +109,8 @@ class MlpContext:
             return raw.view(torch.bfloat16).view(shape)
         if name in _PLANE_SCALES:
             return scales_rowmajor(raw, shape)
+        if name in _PANEL_CODES:
+            return codes_rowmajor(raw, shape)
         if name in ("H13_F32", "DH_F32"):
             return raw.view(torch.float32).view(shape)
         if name == "STATUS":

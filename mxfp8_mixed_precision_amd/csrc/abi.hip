@@ -375,8 +375,8 @@ mxf_status grouped_mlp_fwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   p.M = M;
   // FC1 + SwiGLU + dual quantization of h
   // every scale tensor is in 128-k planes: row stride 4, plane stride 4 x rows
-  p.A = T(MXF_T_XQ_R); p.As = T(MXF_T_XS_R); p.lda = D; p.ldas = 4; p.kbsa = 4 * M;
-  p.B = T(MXF_T_W13Q_R); p.Bs = T(MXF_T_W13S_R); p.ldb = D; p.ldbs = 4; p.kbsb = 4 * 2 * F;
+  p.A = T(MXF_T_XQ_R); p.As = T(MXF_T_XS_R); p.akp = 64 * M; p.ldas = 4; p.kbsa = 4 * M;
+  p.B = T(MXF_T_W13Q_R); p.Bs = T(MXF_T_W13S_R); p.bkp = 64 * 2 * F; p.ldbs = 4; p.kbsb = 4 * 2 * F;
   p.b_es = 2 * F * D; p.bs_es = 2 * F * D / 32;
   p.N = 2 * F; p.K = D;
   p.h13 = (uint16_t*)T(MXF_T_H13);
@@ -396,8 +396,8 @@ mxf_status grouped_mlp_fwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
     MXF_HIP(timed("fc1_swiglu", st, [&] { return mxf_launch_gemm_mgroup(1, p, st); }), "FC1 launch");
   }
   // FC2
-  p.A = T(MXF_T_HQ_R); p.As = T(MXF_T_HS_R); p.lda = F; p.ldas = 4; p.kbsa = 4 * M;
-  p.B = T(MXF_T_W2Q_R); p.Bs = T(MXF_T_W2S_R); p.ldb = F; p.ldbs = 4; p.kbsb = 4 * D;
+  p.A = T(MXF_T_HQ_R); p.As = T(MXF_T_HS_R); p.akp = 64 * M; p.ldas = 4; p.kbsa = 4 * M;
+  p.B = T(MXF_T_W2Q_R); p.Bs = T(MXF_T_W2S_R); p.bkp = 64 * D; p.ldbs = 4; p.kbsb = 4 * D;
   p.b_es = D * F; p.bs_es = D * F / 32;
   p.N = D; p.K = F;
   p.C = y; p.ldc = D; p.out_f32 = (desc->flags & MXF_OUT_F32) ? 1 : 0;
@@ -452,8 +452,8 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   {
     mxf::GemmParams p = base;
     // every scale tensor is in 128-k planes: row stride 4, plane stride 4 x rows
-    p.A = T(MXF_T_DYQ_C); p.As = T(MXF_T_DYS_C); p.lda = M; p.ldas = 4; p.kbsa = 4 * D;
-    p.B = T(MXF_T_HQ_C); p.Bs = T(MXF_T_HS_C); p.ldb = M; p.ldbs = 4; p.kbsb = 4 * F;
+    p.A = T(MXF_T_DYQ_C); p.As = T(MXF_T_DYS_C); p.akp = 64 * D; p.ldas = 4; p.kbsa = 4 * D;
+    p.B = T(MXF_T_HQ_C); p.Bs = T(MXF_T_HS_C); p.bkp = 64 * F; p.ldbs = 4; p.kbsb = 4 * F;
     p.M = D; p.N = F; p.K = M;
     p.C = dw2; p.ldc = F; p.c_es = D * F;
     if (fork) {
@@ -468,8 +468,8 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   {
     mxf::GemmParams p = base;
     p.M = M;
-    p.A = T(MXF_T_DYQ_R); p.As = T(MXF_T_DYS_R); p.lda = D; p.ldas = 4; p.kbsa = 4 * M;
-    p.B = T(MXF_T_W2Q_C); p.Bs = T(MXF_T_W2S_C); p.ldb = D; p.ldbs = 4; p.kbsb = 4 * F;
+    p.A = T(MXF_T_DYQ_R); p.As = T(MXF_T_DYS_R); p.akp = 64 * M; p.ldas = 4; p.kbsa = 4 * M;
+    p.B = T(MXF_T_W2Q_C); p.Bs = T(MXF_T_W2S_C); p.bkp = 64 * F; p.ldbs = 4; p.kbsb = 4 * F;
     p.b_es = F * D; p.bs_es = F * D / 32;
     p.N = F; p.K = D;
     p.h13 = (uint16_t*)T(MXF_T_H13);
@@ -492,8 +492,8 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   // FC1 wgrad: dW13[e] = dH13^T X over the expert's tokens, unpacked into dW1 / dW3
   {
     mxf::GemmParams p = base;
-    p.A = T(MXF_T_DHQ_C); p.As = T(MXF_T_DHS_C); p.lda = M; p.ldas = 4; p.kbsa = 4 * 2 * F;
-    p.B = T(MXF_T_XQ_C); p.Bs = T(MXF_T_XS_C); p.ldb = M; p.ldbs = 4; p.kbsb = 4 * D;
+    p.A = T(MXF_T_DHQ_C); p.As = T(MXF_T_DHS_C); p.akp = 64 * 2 * F; p.ldas = 4; p.kbsa = 4 * 2 * F;
+    p.B = T(MXF_T_XQ_C); p.Bs = T(MXF_T_XS_C); p.bkp = 64 * D; p.ldbs = 4; p.kbsb = 4 * D;
     p.M = 2 * F; p.N = D; p.K = M;
     p.C = dw1; p.C2 = dw3; p.ldc = D; p.c_es = F * D;
     if (fork) {
@@ -508,8 +508,8 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   {
     mxf::GemmParams p = base;
     p.M = M;
-    p.A = T(MXF_T_DHQ_R); p.As = T(MXF_T_DHS_R); p.lda = 2 * F; p.ldas = 4; p.kbsa = 4 * M;
-    p.B = T(MXF_T_W13Q_C); p.Bs = T(MXF_T_W13S_C); p.ldb = 2 * F; p.ldbs = 4; p.kbsb = 4 * D;
+    p.A = T(MXF_T_DHQ_R); p.As = T(MXF_T_DHS_R); p.akp = 64 * M; p.ldas = 4; p.kbsa = 4 * M;
+    p.B = T(MXF_T_W13Q_C); p.Bs = T(MXF_T_W13S_C); p.bkp = 64 * D; p.ldbs = 4; p.kbsb = 4 * D;
     p.b_es = D * 2 * F; p.bs_es = D * 2 * F / 32;
     p.N = D; p.K = 2 * F;
     p.C = dx; p.ldc = D;

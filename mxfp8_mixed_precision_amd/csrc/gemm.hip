@@ -160,9 +160,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
     e = ofs.expert(m0);
     kbeg = 0;
     kend = p.K;
-    Ag = p.A + m0 * p.lda;
+    Ag = p.A + m0 * 64;
     Asg = p.As + m0 * p.ldas;
-    Bg = p.B + e * p.b_es + n0 * p.ldb;
+    Bg = p.B + e * p.b_es + n0 * 64;
     Bsg = p.Bs + e * p.bs_es + n0 * p.ldbs;
   } else {
     // Experts are taken longest-K first (their tiles start earliest, which shortens the tail).
@@ -210,9 +210,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
     kbeg = p.offs[e];
     kend = kbeg + ksp[e];
     __syncthreads();  // the LDS scratch is reused by the main loop
-    Ag = p.A + m0 * p.lda + kbeg;
+    Ag = p.A + m0 * 64 + (kbeg >> 6) * p.akp;
     Asg = p.As + m0 * p.ldas + (kbeg >> 7) * p.kbsa;
-    Bg = p.B + n0 * p.ldb + kbeg;
+    Bg = p.B + n0 * 64 + (kbeg >> 6) * p.bkp;
     Bsg = p.Bs + n0 * p.ldbs + (kbeg >> 7) * p.kbsb;
   }
   const int tr0 = wm * T::TM;  // first row / column of this wavefront within the block tile
@@ -228,22 +228,22 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
   // Direct global->LDS loads: a wavefront's 1 KB load covers 16 consecutive tile rows (starting
-  // at a multiple of 16) and writes LDS bytes [base, base + 1024) in lane order, 16 bytes per
-  // lane: lane l lands on row l / 4, LDS chunk l % 4. The swizzle is applied on the global
-  // side: that lane fetches chunk (l % 4) ^ ((row / 4) % 4) = (l % 4) ^ (l / 16), the same for
-  // every load, so one per-lane offset serves them all.
+  // at a multiple of 16) of one 64-k panel -- one contiguous kilobyte of the operand -- and
+  // writes LDS bytes [base, base + 1024) in lane order, 16 bytes per lane: lane l lands on row
+  // l / 4, LDS chunk l % 4. The swizzle is applied on the global side: that lane fetches chunk
+  // (l % 4) ^ ((row / 4) % 4) = (l % 4) ^ (l / 16), the same for every load, so one per-lane
+  // offset serves them all.
   const int r32 = lane & 31;
   const int g = lane >> 5;
   const int64_t lrow = lane >> 2;
   const uint32_t lcol = (uint32_t)(((lane & 3) ^ (lane >> 4)) << 4);
   const int wid_u = __builtin_amdgcn_readfirstlane(wid);  // wavefront-uniform (SGPR) copy
-  const uint8_t* a_s = Ag + (int64_t)wid_u * T::IA * 16 * p.lda;  // this wavefront's first rows
-  const uint8_t* b_s = Bg + (int64_t)wid_u * T::IB * 16 * p.ldb;
-  const uint32_t a_v = (uint32_t)(lrow * p.lda) + lcol;
-  const uint32_t b_v = (uint32_t)(lrow * p.ldb) + lcol;
+  const uint8_t* a_s = Ag + (int64_t)wid_u * T::IA * 1024;  // this wavefront's first rows
+  const uint8_t* b_s = Bg + (int64_t)wid_u * T::IB * 1024;
+  const uint32_t a_v = (uint32_t)(lrow * 64) + lcol;
+  const uint32_t b_v = a_v;
   const uint32_t sa_v = (uint32_t)(((wid * 64 + lane) % BM) * p.ldas);
   const uint32_t sb_v = (uint32_t)(((wid * 64 + lane) % BN) * p.ldbs);
-  const int64_t a16 = 16 * p.lda, b16 = 16 * p.ldb;
   const uint32_t lds0 = lds_addr(smem);
   // One of the L direct-to-LDS loads of stage ks into the LDS slot of stage kt (ks == kt, or
   // a surplus load of the last stage into a free slot, which keeps every step's load count
@@ -253,10 +253,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
     const int64_t k0 = (int64_t)ks * T::BK;
     const uint32_t st = lds0 + (kt % T::S) * T::STAGE;
     if (q < T::IA) {
-      g2lds16(a_s + q * a16 + k0, a_v, st + T::A_OFF + (wid_u * T::IA + q) * 1024);
+      g2lds16(a_s + q * 1024 + ks * p.akp, a_v, st + T::A_OFF + (wid_u * T::IA + q) * 1024);
     } else if (q < T::IA + T::IB) {
       const int i = q - T::IA;
-      g2lds16(b_s + i * b16 + k0, b_v, st + T::B_OFF + (wid_u * T::IB + i) * 1024);
+      g2lds16(b_s + i * 1024 + ks * p.bkp, b_v, st + T::B_OFF + (wid_u * T::IB + i) * 1024);
     } else if (q == T::IA + T::IB) {
       g2lds4(Asg + (k0 >> 7) * p.kbsa, sa_v, st + T::SA_OFF + wid_u * 256);
     } else {
@@ -486,13 +486,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
       }
     }
     __syncthreads();
-    // row-wise groups: one task = 16 columns of a row; lanes 2c and 2c+1 hold one group
+    // row-wise groups: one task = 16 columns of a row, four tasks (four lanes) per 64-column
+    // panel row, consecutive rows on consecutive lane quads, so a wavefront stores a contiguous
+    // kilobyte of a panel; lanes 2c and 2c+1 hold one group
     constexpr int CPR = HCB / 16;
-    static_assert((BM * CPR) % T::NT == 0 && CPR % 2 == 0, "whole row-pass rounds");
+    static_assert((BM * CPR) % T::NT == 0 && CPR % 4 == 0, "whole row-pass rounds");
+    const int64_t M = p.mcap;
 #pragma unroll 2
     for (int it = 0; it < BM * CPR / T::NT; ++it) {
       const int t = it * T::NT + tid;
-      const int r = t / CPR, c = t % CPR;
+      const int r = (t >> 2) % BM, c = ((t >> 2) / BM) * 4 + (t & 3);
       const uint4 a = *reinterpret_cast<const uint4*>(hR + r * HP + c * 16);
       const uint4 b = *reinterpret_cast<const uint4*>(hR + r * HP + c * 16 + 8);
       const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
@@ -500,21 +503,25 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
       am = max(am, dpp_xor1(am));
       const Scale s = scale_from_amax(am);
       const int64_t row = m0 + r;
-      *reinterpret_cast<uint4*>(p.q_r + row * F + hc0 + c * 16) =
+      const int64_t hcol = hc0 + c * 16;
+      *reinterpret_cast<uint4*>(p.q_r + (hcol >> 6) * 64 * M + row * 64 + (hcol & 63)) =
           make_uint4(cvt4(v[0], v[1], s), cvt4(v[2], v[3], s), cvt4(v[4], v[5], s), cvt4(v[6], v[7], s));
-      const int64_t grp = (hc0 + c * 16) >> 5;
+      const int64_t grp = hcol >> 5;
       if (!(c & 1)) p.s_r[row * p.sr_rs + (grp >> 2) * p.sr_kbs + (grp & 3)] = (uint8_t)s.byte;
     }
-    // column-wise codes: a column's BM codes are contiguous in hq_c
+    // column-wise codes (hq_c [F, mcap], 64-token panels): four lanes per column and panel,
+    // consecutive columns on consecutive lane quads (contiguous kilobytes)
     constexpr int CPC = BM / 16;
-    static_assert((HCB * CPC) % T::NT == 0, "whole column-copy rounds");
+    static_assert((HCB * CPC) % T::NT == 0 && CPC % 4 == 0, "whole column-copy rounds");
 #pragma unroll 2
     for (int it = 0; it < HCB * CPC / T::NT; ++it) {
       const int t = it * T::NT + tid;
-      const int hc = t / CPC, c = t % CPC;
+      const int hc = (t >> 2) % HCB, c = ((t >> 2) / HCB) * 4 + (t & 3);
       const uint2 a = *reinterpret_cast<const uint2*>(qT + hc * QP + c * 16);
       const uint2 b = *reinterpret_cast<const uint2*>(qT + hc * QP + c * 16 + 8);
-      *reinterpret_cast<uint4*>(p.q_c + (hc0 + hc) * p.mcap + m0 + c * 16) = make_uint4(a.x, a.y, b.x, b.y);
+      const int64_t tok = m0 + c * 16;
+      *reinterpret_cast<uint4*>(p.q_c + (tok >> 6) * 64 * F + (hc0 + hc) * 64 + (tok & 63)) =
+          make_uint4(a.x, a.y, b.x, b.y);
     }
     // column scales: SG groups per column (whole 128-row planes: m0 is a multiple of 128)
     for (int t = tid; t < HCB * (SG / 4); t += T::NT) {
@@ -621,12 +628,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
         if (i + 2 < T::FM) load_gu(i + 2, i & 1);
       }
       __syncthreads();
+      // four lanes per 64-column panel row, consecutive rows on consecutive lane quads
       constexpr int CPR = PCB / 16;
-      static_assert((T::TM * CPR) % T::NT == 0 && CPR % 2 == 0, "whole row-pass rounds");
+      static_assert((T::TM * CPR) % T::NT == 0 && CPR % 4 == 0, "whole row-pass rounds");
 #pragma unroll 2
       for (int it = 0; it < T::TM * CPR / T::NT; ++it) {
         const int t = it * T::NT + tid;
-        const int r = t / CPR, c = t % CPR;
+        const int r = (t >> 2) % T::TM, c = ((t >> 2) / T::TM) * 4 + (t & 3);
         const uint4 a = *reinterpret_cast<const uint4*>(dR + r * DP + c * 16);
         const uint4 b = *reinterpret_cast<const uint4*>(dR + r * DP + c * 16 + 8);
         const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
@@ -634,20 +642,26 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
         am = max(am, dpp_xor1(am));
         const Scale s = scale_from_amax(am);
         const int64_t row = m0 + brow(hh, r);
-        *reinterpret_cast<uint4*>(p.q_r + row * ld13 + pc0 + c * 16) =
+        const int64_t pcol = pc0 + c * 16;
+        *reinterpret_cast<uint4*>(p.q_r + (pcol >> 6) * 64 * p.mcap + row * 64 + (pcol & 63)) =
             make_uint4(cvt4(v[0], v[1], s), cvt4(v[2], v[3], s), cvt4(v[4], v[5], s), cvt4(v[6], v[7], s));
-        const int64_t grp = (pc0 + c * 16) >> 5;
+        const int64_t grp = pcol >> 5;
         if (!(c & 1)) p.s_r[row * p.sr_rs + (grp >> 2) * p.sr_kbs + (grp & 3)] = (uint8_t)s.byte;
       }
+      // dhq_c [2F, mcap] in 64-token panels: a round's RH consecutive block rows lie in one
+      // panel (RH = 64) or half of one (RH = 32); G lanes cover a column's run of them,
+      // consecutive columns on consecutive lane groups
       constexpr int CPC = T::TM / 16;
-      static_assert((PCB * CPC) % T::NT == 0 && RH % 16 == 0, "whole column-copy rounds");
+      constexpr int G = RH >= 64 ? 4 : RH / 16;
+      static_assert((PCB * CPC) % T::NT == 0 && RH % 16 == 0 && CPC % G == 0, "whole column-copy rounds");
 #pragma unroll 2
       for (int it = 0; it < PCB * CPC / T::NT; ++it) {
         const int t = it * T::NT + tid;
-        const int pc = t / CPC, c = t % CPC;
+        const int pc = (t / G) % PCB, c = ((t / G) / PCB) * G + (t % G);
         const uint2 a = *reinterpret_cast<const uint2*>(qT + pc * QP + c * 16);
         const uint2 b = *reinterpret_cast<const uint2*>(qT + pc * QP + c * 16 + 8);
-        *reinterpret_cast<uint4*>(p.q_c + (pc0 + pc) * p.mcap + m0 + brow(hh, c * 16)) =
+        const int64_t tok = m0 + brow(hh, c * 16);
+        *reinterpret_cast<uint4*>(p.q_c + (tok >> 6) * 64 * ld13 + (pc0 + pc) * 64 + (tok & 63)) =
             make_uint4(a.x, a.y, b.x, b.y);
       }
       for (int t = tid; t < PCB * SG; t += T::NT) {

@@ -5,16 +5,20 @@
 
 namespace mxf {
 
+// Code addressing of the MLP's GEMM operands (64-k panels): a code matrix with R rows and K
+// columns (K the contraction axis) is stored as K/64 panels [R][64]: the byte of (r, k) is at
+// (k / 64) * 64R + 64 r + k % 64. A GEMM stage (64 k of 16 consecutive rows) is then one
+// contiguous kilobyte.
 // Scale addressing (every E8M0 tensor): the byte of (row r, 32-group g) is at
 // r * rs + (g / 4) * kbs + g % 4. Row-major [R][G]: rs = G, kbs = 4. The MLP's operands use
 // 128-k planes [G/4][R][4] (rs = 4, kbs = 4R): the scale words of consecutive rows for one
 // 128-k block are contiguous, so a tile's scales for a K step are one contiguous run.
 struct GemmParams {
-  const uint8_t* A;   // codes, rows of K bytes with pitch lda
+  const uint8_t* A;   // codes in 64-k panels, panel stride akp (= 64 x rows of A)
   const uint8_t* As;  // scales: row stride ldas, 128-k plane stride kbsa
-  const uint8_t* B;
+  const uint8_t* B;   // codes in 64-k panels, panel stride bkp (per expert for M-grouped B)
   const uint8_t* Bs;
-  int64_t lda, ldas, ldb, ldbs;
+  int64_t akp, ldas, bkp, ldbs;
   int64_t kbsa, kbsb;
   int64_t b_es, bs_es;  // M-grouped: bytes between experts in B / Bs
   int64_t M, N, K;      // M-grouped: M = m_capacity. K-grouped: output [M, N] per expert
@@ -28,9 +32,9 @@ struct GemmParams {
   int64_t ldc, c_es;
   int out_f32;
   uint16_t* h13;     // SWIGLU: written, DSWIGLU: read; fragment-tiled (4 KB per 32x32 h block)
-  uint8_t* q_r;      // SWIGLU: hq_r [mcap, F];  DSWIGLU: dhq_r [mcap, 2F]
+  uint8_t* q_r;      // SWIGLU: hq_r [mcap, F];  DSWIGLU: dhq_r [mcap, 2F] (64-k panels)
   uint8_t* s_r;      // their scales: row stride sr_rs, plane stride sr_kbs
-  uint8_t* q_c;      // SWIGLU: hq_c [F, mcap];  DSWIGLU: dhq_c [2F, mcap]
+  uint8_t* q_c;      // SWIGLU: hq_c [F, mcap];  DSWIGLU: dhq_c [2F, mcap] (64-k panels)
   uint8_t* s_c;      // row stride sc_rs, plane stride sc_kbs
   int64_t sr_rs, sr_kbs, sc_rs, sc_kbs;
   float* dbg;        // optional fp32 copy of the accumulator ([mcap, N])

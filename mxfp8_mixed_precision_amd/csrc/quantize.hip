@@ -50,6 +50,9 @@ struct QuantParams {
   int64_t n_assign;                     // QK_GATHER: tokens * topk
   int topk;                             // QK_GATHER
   int col_fast;                         // grid x walks column tiles (set by the launcher)
+  int blk;                              // codes in 64-k panels (the MLP's GEMM operands): q_r byte
+                                        // (r, c) at (c/64)*64*rows + 64r + c%64, q_c byte (c, r) at
+                                        // (r/64)*64*cols + 64c + r%64; else row-major
 };
 
 
@@ -167,7 +170,10 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
       const uint32_t lo = cvt4<FMT>(x[j][0], x[j][1], sc);
       const uint32_t hi = cvt4<FMT>(x[j][2], x[j][3], sc);
       const int64_t r = r0 + j;
-      if (colok && r < p.rows) *reinterpret_cast<uint2*>(q_r + r * p.cols + col) = make_uint2(lo, hi);
+      if (colok && r < p.rows) {
+        const int64_t o = p.blk ? (col >> 6) * 64 * p.rows + r * 64 + (col & 63) : r * p.cols + col;
+        *reinterpret_cast<uint2*>(q_r + o) = make_uint2(lo, hi);
+      }
       if ((c & 3) == 0) srow_b[(r - row0) * 4 + (c >> 2)] = (uint8_t)sc.byte;
     }
   }
@@ -214,15 +220,20 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
   }
   if (COL) {
     uint8_t* q_c = p.q_c + e * p.qc_bs;
-    // a column's codes for the block's rows are contiguous in q_c: 16 bytes per task
+    // 16 bytes (one column, 16 rows) per task. Row-major: a column's codes for the block's rows
+    // are contiguous, eight tasks per column. 64-k panels: four tasks per column and panel,
+    // consecutive columns on consecutive lane quads (contiguous kilobytes).
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int t = it * 256 + tid;
-      const int cl = t >> 3, ch = t & 7;
+      const int cl = p.blk ? (t >> 2) & 127 : t >> 3;
+      const int ch = p.blk ? (t >> 9) * 4 + (t & 3) : t & 7;
       if (col0 + cl < p.cols && row0 + ch * 16 < p.rows) {
         const uint2 a = *reinterpret_cast<const uint2*>(qT + cl * QTP + ch * 16);
         const uint2 b = *reinterpret_cast<const uint2*>(qT + cl * QTP + ch * 16 + 8);
-        *reinterpret_cast<uint4*>(q_c + (col0 + cl) * p.ldc + row0 + ch * 16) = make_uint4(a.x, a.y, b.x, b.y);
+        const int64_t r = row0 + ch * 16;
+        const int64_t o = p.blk ? (r >> 6) * 64 * p.cols + (col0 + cl) * 64 + (r & 63) : (col0 + cl) * p.ldc + r;
+        *reinterpret_cast<uint4*>(q_c + o) = make_uint4(a.x, a.y, b.x, b.y);
       }
     }
     if (tid < 128 && col0 + tid < p.cols) {
@@ -410,6 +421,7 @@ hipError_t mxf_launch_quant_tokens(const void* x, int64_t mcap, int64_t D, const
                                    const int32_t* counts, int E, int pad, void* q_r, void* s_r,
                                    void* q_c, void* s_c, int32_t* status, hipStream_t st) {
   mxf::QuantParams p = {};
+  p.blk = 1;  // GEMM operands: codes in 64-k panels
   p.src = (const uint16_t*)x;
   p.rows = mcap;
   p.cols = D;
@@ -437,6 +449,7 @@ hipError_t mxf_launch_quant_gather(const void* x_tokens, int64_t n_assign, int t
                                    int pad, void* q_r, void* s_r, void* q_c, void* s_c, int32_t* status,
                                    hipStream_t st) {
   mxf::QuantParams p = {};
+  p.blk = 1;  // GEMM operands: codes in 64-k panels
   p.src = (const uint16_t*)x_tokens;
   p.rows = mcap;
   p.cols = D;
@@ -458,6 +471,7 @@ hipError_t mxf_launch_swiglu_quant(const void* h13, int64_t mcap, int64_t F, con
                                    const int32_t* counts, int E, int pad, void* q_r, void* s_r, void* q_c,
                                    void* s_c, hipStream_t st) {
   mxf::QuantParams p = {};
+  p.blk = 1;  // GEMM operands: codes in 64-k panels
   p.src = (const uint16_t*)h13;
   p.rows = mcap;
   p.cols = F;
@@ -475,6 +489,7 @@ hipError_t mxf_launch_dswiglu_quant(const void* dh, const void* h13, int64_t mca
                                     const int32_t* counts, int E, int pad, void* q_r, void* s_r, void* q_c,
                                     void* s_c, hipStream_t st) {
   mxf::QuantParams p = {};
+  p.blk = 1;  // GEMM operands: codes in 64-k panels
   p.src = (const uint16_t*)dh;
   p.src2 = (const uint16_t*)h13;
   p.rows = mcap;
@@ -494,6 +509,7 @@ hipError_t mxf_launch_quant_weights(const void* w, const void* w3, bool pack13, 
                                     int64_t cols, void* q_r, void* s_r, void* q_c, void* s_c,
                                     hipStream_t st) {
   mxf::QuantParams p = {};
+  p.blk = 1;  // GEMM operands: codes in 64-k panels
   p.src = (const uint16_t*)w;
   p.src2 = (const uint16_t*)w3;
   p.rows = rows;

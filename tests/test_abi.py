@@ -248,3 +248,23 @@ def test_dispatch_rejections_before_any_launch():
     with pytest.raises(mx.MxfError) as ei:
         mx.grouped_mlp_fwd(d, good, None, None, good, good, good, good, good, good, stream=0)
     assert ei.value.status in (_abi.E_HIP, _abi.E_DEVICE)
+
+
+def test_code_panels_match_documented_order():
+    """The binding's row-major copy of a code tensor stored in 64-k panels follows the byte
+    formula stated in include/mxfp8.h, with and without a leading expert dimension."""
+    import torch
+    for lead in ((), (3,)):
+        R, K = 40, 192
+        n = 1
+        for d in lead:
+            n *= d
+        panels = torch.empty(n * R * K, dtype=torch.int64)
+        for e in range(n):
+            for r in range(R):
+                for k in range(K):
+                    panels[e * R * K + (k // 64) * 64 * R + 64 * r + k % 64] = (e * 1000 + r) * 1000 + k
+        rm = mx.codes_rowmajor(panels, (*lead, R, K))
+        want = ((torch.arange(n)[:, None, None] * 1000 + torch.arange(R)[None, :, None]) * 1000
+                + torch.arange(K)[None, None, :]).reshape(*lead, R, K)
+        assert torch.equal(rm, want)
