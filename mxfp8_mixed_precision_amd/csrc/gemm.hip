@@ -28,6 +28,7 @@
 //   K-grouped (both wgrads): blockIdx.z = expert; K runs over the expert's token segment
 //     (the real rows rounded up to 128; pad rows are zero codes). A zero-token expert runs
 //     no K step and stores zeros.
+#include <atomic>
 #include <type_traits>
 
 #include "kernels.h"
@@ -120,101 +121,22 @@ __device__ __forceinline__ void g2lds4(const void* sbase, uint32_t voff, uint32_
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
 }
 
+// One output tile (rows [m0, m0 + BM), columns [n0, n0 + BN), contraction over [kbeg, kend)):
+// the pipelined main loop and the epilogue. smem holds Tile<BM, BN, WM, WN>::lds(EPI) bytes.
 template <int BM, int BN, int WM, int WN, int SCHED, int EPI>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
+__device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int e, int64_t m0, int64_t n0,
+                                         int64_t kbeg, int64_t kend) {
   using T = Tile<BM, BN, WM, WN>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[T::lds(EPI)];
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
   const int wm = wid / WN;
   const int wn = wid % WN;
-
-  const Offsets ofs = read_offsets(p.offs, p.counts, p.E, p.pad, p.mcap);
-  if (!ofs.ok) return;
-
-  int e;
-  int64_t m0, n0, kbeg, kend;
-  const uint8_t *Ag, *Asg, *Bg, *Bsg;
-  const int ntn = (int)(p.N / BN);
-  if (SCHED == SCHED_MGROUP) {
-    // Only the row tiles before offs[E] carry work: the grid is sized for m_capacity and the
-    // surplus blocks exit. Blocks are dispatched round-robin over the 8 XCDs (block b runs on
-    // XCD b % 8), so tile t is taken from a contiguous per-XCD range, and inside it tiles go in
-    // groups of GM row tiles x all column tiles: the ~32 blocks an XCD runs at once share a
-    // few A row panels and B column panels in that XCD's L2.
-    constexpr int GM = 4;
-    const int64_t mtu = ofs.mend / BM;
-    const int64_t ntiles = mtu * ntn;
-    const int64_t b = blockIdx.x;
-    if (b >= ntiles) return;
-    const int64_t q8 = ntiles / 8, r8 = ntiles % 8, x8 = b % 8, s8 = b / 8;
-    const int64_t t = x8 < r8 ? x8 * (q8 + 1) + s8 : r8 * (q8 + 1) + (x8 - r8) * q8 + s8;
-    const int64_t grp = t / (GM * ntn);
-    const int64_t first = grp * GM;
-    const int64_t gsz = min((int64_t)GM, mtu - first);
-    const int64_t within = t - grp * GM * ntn;
-    m0 = (first + within % gsz) * BM;
-    n0 = (within / gsz) * BN;
-    e = ofs.expert(m0);
-    kbeg = 0;
-    kend = p.K;
-    Ag = p.A + m0 * 64;
-    Asg = p.As + m0 * p.ldas;
-    Bg = p.B + e * p.b_es + n0 * 64;
-    Bsg = p.Bs + e * p.bs_es + n0 * p.ldbs;
-  } else {
-    // Experts are taken longest-K first (their tiles start earliest, which shortens the tail).
-    // Within an expert every tile streams the whole K range, so what matters is how many A
-    // row panels and B column panels each XCD's L2 must hold: block l of the expert runs on
-    // XCD l % 8, each XCD takes a contiguous run of positions, and positions walk the tile
-    // grid in strips 4 tiles wide across the smaller dimension, so a run covers a compact
-    // patch (for 11 x 8 tiles: 60 panel streams in all instead of 96 for whole rows).
-    int* ksp = reinterpret_cast<int*>(smem);  // per-expert K span, then the order (LDS scratch)
-    int* order = ksp + p.E;
-    for (int i = tid; i < p.E; i += T::NT) {
-      const int seg = p.offs[i + 1] - p.offs[i];
-      const int real = p.counts ? p.counts[i] : seg;
-      ksp[i] = min(seg, (real + 127) / 128 * 128);
-    }
-    __syncthreads();
-    for (int i = tid; i < p.E; i += T::NT) {
-      const int ki = ksp[i];
-      int rank = 0;
-      for (int j = 0; j < p.E; ++j) {
-        const int kj = ksp[j];
-        rank += (kj > ki) || (kj == ki && j < i);
-      }
-      order[rank] = i;
-    }
-    __syncthreads();
-    const int mtn = (int)(p.M / BM);
-    const int64_t per = (int64_t)mtn * ntn;
-    const int64_t t = blockIdx.x;
-    e = order[t / per];
-    const int64_t l = t % per;
-    const int64_t q8 = per / 8, r8 = per % 8, x8 = l % 8, s8 = l / 8;
-    const int64_t pos = (x8 < r8 ? x8 * (q8 + 1) : r8 * (q8 + 1) + (x8 - r8) * q8) + s8;
-    // strips of width W across the smaller grid dimension; the longer one runs inside a strip
-    const bool mlong = mtn >= ntn;
-    const int64_t nlong = mlong ? mtn : ntn, nshort = mlong ? ntn : mtn;
-    constexpr int W = 4;
-    const int64_t nstrip = (nshort + W - 1) / W;
-    const int64_t strip = min(pos / (W * nlong), nstrip - 1);
-    const int64_t sw = min((int64_t)W, nshort - strip * W);  // width of this strip
-    const int64_t within = pos - strip * W * nlong;
-    const int64_t il = within / sw, is = strip * W + within % sw;
-    m0 = (mlong ? il : is) * BM;
-    n0 = (mlong ? is : il) * BN;
-    kbeg = p.offs[e];
-    kend = kbeg + ksp[e];
-    __syncthreads();  // the LDS scratch is reused by the main loop
-    Ag = p.A + m0 * 64 + (kbeg >> 6) * p.akp;
-    Asg = p.As + m0 * p.ldas + (kbeg >> 7) * p.kbsa;
-    Bg = p.B + n0 * 64 + (kbeg >> 6) * p.bkp;
-    Bsg = p.Bs + n0 * p.ldbs + (kbeg >> 7) * p.kbsb;
-  }
+  // operand panels of the tile (M-grouped: kbeg = 0 and B is expert e's; K-grouped: b_es = 0)
+  const uint8_t* Ag = p.A + m0 * 64 + (kbeg >> 6) * p.akp;
+  const uint8_t* Asg = p.As + m0 * p.ldas + (kbeg >> 7) * p.kbsa;
+  const uint8_t* Bg = p.B + e * p.b_es + n0 * 64 + (kbeg >> 6) * p.bkp;
+  const uint8_t* Bsg = p.Bs + e * p.bs_es + n0 * p.ldbs + (kbeg >> 7) * p.kbsb;
   const int tr0 = wm * T::TM;  // first row / column of this wavefront within the block tile
   const int tc0 = wn * T::TN;
   const int KT = (int)((kend - kbeg) / T::BK);  // stages (even: K is a multiple of 128)
@@ -675,6 +597,142 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
   }
 }
 
+// Tail sub-tiles (M-grouped): when the tile count T is not a multiple of the CU count, the last
+// R = T mod #CU tiles (in raster order) would leave most CUs idle in the final round. Each of them
+// is split into Q sub-tiles (Q = 4 when 4R <= #CU, else 2 when 2R <= #CU): BM/2 x BN/2, or
+// BM x BN/2 (BN >= 256) / BM/2 x BN, computed by separate blocks with the same pipeline.
+template <int BM, int BN>
+struct TailCfg {
+  static constexpr bool Q2 = BM == 256;                 // sub-tiles keep >= 128 rows
+  static constexpr bool Q4 = BM == 256 && BN == 256;
+  static constexpr int BM2 = BN >= 256 ? BM : BM / 2;   // Q = 2
+  static constexpr int BN2 = BN >= 256 ? BN / 2 : BN;
+  static constexpr int BM4 = BM / 2, BN4 = BN / 2;      // Q = 4
+};
+
+template <int BM, int BN, int WM, int WN, int SCHED, int EPI>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
+  using T = Tile<BM, BN, WM, WN>;
+  using TC = TailCfg<BM, BN>;
+  constexpr bool SPLIT = SCHED == SCHED_MGROUP && TC::Q2;
+  constexpr int LDSZ = SPLIT ? T::imax(T::lds(EPI), T::imax(Tile<TC::BM2, TC::BN2, WM, WN>::lds(EPI),
+                                                           Tile<TC::BM4, TC::BN4, WM, WN>::lds(EPI)))
+                             : T::lds(EPI);
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDSZ];
+
+  const int tid = threadIdx.x;
+  const Offsets ofs = read_offsets(p.offs, p.counts, p.E, p.pad, p.mcap);
+  if (!ofs.ok) return;
+
+  int e;
+  int64_t m0, n0, kbeg, kend;
+  const int ntn = (int)(p.N / BN);
+  if (SCHED == SCHED_MGROUP) {
+    // Only the row tiles before offs[E] carry work: the grid is sized for m_capacity (plus the
+    // tail sub-tiles) and the surplus blocks exit. Blocks are dispatched round-robin over the 8
+    // XCDs (block b runs on XCD b % 8), so raster position t is taken from a contiguous per-XCD
+    // range, and positions go in groups of GM row tiles x all column tiles: the ~32 blocks an
+    // XCD runs at once share a few A row panels and B column panels in that XCD's L2.
+    constexpr int GM = 4;
+    const int64_t mtu = ofs.mend / BM;
+    const int64_t ntiles = mtu * ntn;
+    int64_t nfull = ntiles, rem = 0;
+    int q = 1;
+    if (SPLIT) {
+      rem = ntiles % p.ncu;
+      if (rem && TC::Q4 && 4 * rem <= p.ncu) q = 4;
+      else if (rem && 2 * rem <= p.ncu) q = 2;
+      if (q > 1) nfull = ntiles - rem;
+      else rem = 0;
+    }
+    const int64_t b = blockIdx.x;
+    const bool tail = b >= nfull;  // a sub-tile of one of the last rem tiles
+    int64_t t, part = 0;
+    if (!tail) {
+      const int64_t q8 = nfull / 8, r8 = nfull % 8, x8 = b % 8, s8 = b / 8;
+      t = x8 < r8 ? x8 * (q8 + 1) + s8 : r8 * (q8 + 1) + (x8 - r8) * q8 + s8;
+    } else {
+      if (b - nfull >= rem * q) return;
+      t = nfull + (b - nfull) / q;
+      part = (b - nfull) % q;
+    }
+    const int64_t grp = t / (GM * ntn);
+    const int64_t first = grp * GM;
+    const int64_t gsz = min((int64_t)GM, mtu - first);
+    const int64_t within = t - grp * GM * ntn;
+    m0 = (first + within % gsz) * BM;
+    n0 = (within / gsz) * BN;
+    kbeg = 0;
+    kend = p.K;
+    if constexpr (SPLIT) {
+      if constexpr (TC::Q4) {
+        if (tail && q == 4) {
+          m0 += (part >> 1) * TC::BM4;
+          n0 += (part & 1) * TC::BN4;
+          e = ofs.expert(m0);
+          tile_run<TC::BM4, TC::BN4, WM, WN, SCHED, EPI>(p, smem, e, m0, n0, kbeg, kend);
+          return;
+        }
+      }
+      if (tail && q == 2) {
+        if (TC::BM2 == BM) n0 += part * TC::BN2;
+        else m0 += part * TC::BM2;
+        e = ofs.expert(m0);
+        tile_run<TC::BM2, TC::BN2, WM, WN, SCHED, EPI>(p, smem, e, m0, n0, kbeg, kend);
+        return;
+      }
+    }
+    e = ofs.expert(m0);
+  } else {
+    // Experts are taken longest-K first (their tiles start earliest, which shortens the tail).
+    // Within an expert every tile streams the whole K range, so what matters is how many A
+    // row panels and B column panels each XCD's L2 must hold: block l of the expert runs on
+    // XCD l % 8, each XCD takes a contiguous run of positions, and positions walk the tile
+    // grid in strips 4 tiles wide across the smaller dimension, so a run covers a compact
+    // patch (for 11 x 8 tiles: 60 panel streams in all instead of 96 for whole rows).
+    int* ksp = reinterpret_cast<int*>(smem);  // per-expert K span, then the order (LDS scratch)
+    int* order = ksp + p.E;
+    for (int i = tid; i < p.E; i += T::NT) {
+      const int seg = p.offs[i + 1] - p.offs[i];
+      const int real = p.counts ? p.counts[i] : seg;
+      ksp[i] = min(seg, (real + 127) / 128 * 128);
+    }
+    __syncthreads();
+    for (int i = tid; i < p.E; i += T::NT) {
+      const int ki = ksp[i];
+      int rank = 0;
+      for (int j = 0; j < p.E; ++j) {
+        const int kj = ksp[j];
+        rank += (kj > ki) || (kj == ki && j < i);
+      }
+      order[rank] = i;
+    }
+    __syncthreads();
+    const int mtn = (int)(p.M / BM);
+    const int64_t per = (int64_t)mtn * ntn;
+    const int64_t t = blockIdx.x;
+    e = order[t / per];
+    const int64_t l = t % per;
+    const int64_t q8 = per / 8, r8 = per % 8, x8 = l % 8, s8 = l / 8;
+    const int64_t pos = (x8 < r8 ? x8 * (q8 + 1) : r8 * (q8 + 1) + (x8 - r8) * q8) + s8;
+    // strips of width W across the smaller grid dimension; the longer one runs inside a strip
+    const bool mlong = mtn >= ntn;
+    const int64_t nlong = mlong ? mtn : ntn, nshort = mlong ? ntn : mtn;
+    constexpr int W = 4;
+    const int64_t nstrip = (nshort + W - 1) / W;
+    const int64_t strip = min(pos / (W * nlong), nstrip - 1);
+    const int64_t sw = min((int64_t)W, nshort - strip * W);  // width of this strip
+    const int64_t within = pos - strip * W * nlong;
+    const int64_t il = within / sw, is = strip * W + within % sw;
+    m0 = (mlong ? il : is) * BM;
+    n0 = (mlong ? is : il) * BN;
+    kbeg = p.offs[e];
+    kend = kbeg + ksp[e];
+    __syncthreads();  // the LDS scratch is reused by the main loop
+  }
+  tile_run<BM, BN, WM, WN, SCHED, EPI>(p, smem, e, m0, n0, kbeg, kend);
+}
+
 // ------------------------------------------------------------------ host launchers
 
 // Tile configurations (4 wavefronts): 256x128 (wavefront tile 128x64) where the dimensions
@@ -685,7 +743,7 @@ static hipError_t launch_cfg(const GemmParams& p, hipStream_t st) {
   // 1-D grids: the kernel maps block ids to tiles (see the schedulers)
   int64_t nblk;
   if (SCHED == SCHED_MGROUP)
-    nblk = (p.mcap / BM) * (p.N / BN);
+    nblk = (p.mcap / BM) * (p.N / BN) + (TailCfg<BM, BN>::Q2 ? 3 * p.ncu : 0);  // + tail sub-tiles
   else
     nblk = (p.M / BM) * (p.N / BN) * p.E;
   if (nblk == 0) return hipSuccess;
@@ -707,9 +765,32 @@ static hipError_t launch(const GemmParams& p, bool big_m, hipStream_t st) {
 
 // M-grouped: C[m, n] = sum_k A[m, k] B_e[n, k] for m in expert e's segment.
 // epi: 0 store (C, ldc, out_f32), 1 SwiGLU + dual quant, 2 dSwiGLU + dual quant.
-hipError_t mxf_launch_gemm_mgroup(int epi, const mxf::GemmParams& p, hipStream_t st) {
+namespace {
+// compute units per device, looked up once (the tail sub-tiling balances the last round over them)
+std::atomic<int> g_ncu[64];
+hipError_t device_cus(int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  int n = g_ncu[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (n <= 0) return hipErrorInvalidValue;
+    g_ncu[dev].store(n, std::memory_order_relaxed);
+  }
+  *out = n;
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t mxf_launch_gemm_mgroup(int epi, const mxf::GemmParams& pin, hipStream_t st) {
   using namespace mxf;
-  if (p.mcap % 128 || p.N % 128 || p.K % 128 || p.ldc % 8) return hipErrorInvalidValue;
+  if (pin.mcap % 128 || pin.N % 128 || pin.K % 128 || pin.ldc % 8) return hipErrorInvalidValue;
+  GemmParams p = pin;
+  const hipError_t ce = device_cus(&p.ncu);
+  if (ce != hipSuccess) return ce;
   const bool big = (p.pad % 256 == 0) && (p.mcap % 256 == 0);
   switch (epi) {
     case EPI_STORE: return launch<SCHED_MGROUP, EPI_STORE>(p, big, st);

@@ -26,6 +26,7 @@ struct GemmParams {
   const int32_t* counts;
   int E, pad;
   int64_t mcap;
+  int ncu;           // compute units of the device (set by the launcher; tail sub-tiling)
   // epilogue
   void* C;           // STORE: [M, N] (+ e * c_es for K-grouped); UNPACK13: dW1
   void* C2;          // UNPACK13: dW3

@@ -310,6 +310,10 @@ def test_nan_poisoned_pad_and_tail(tiny):
     dict(counts=[0, 200, 0, 57], E=4, D=256, F=384, pad=256),        # zero-token experts, pad 256
     dict(counts=[300, 1, 129], E=3, D=384, F=256, pad=128),          # ragged counts, pad 128
     dict(counts=[512], E=1, D=512, F=640, pad=256),                  # dense (E = 1)
+    # more tiles than compute units, with a remainder: FC1 (288 tiles of 256 x 256) and FC2
+    # dgrad (288 of 256 x 128) run whole tiles plus split tail tiles; FC2 and FC1 dgrad are all
+    # tail
+    dict(counts=[2300, 2250], E=2, D=256, F=2048, pad=256),
 ])
 def test_small_shapes_stagewise(case):
     mx = require_gpu()
