@@ -14,20 +14,28 @@
 // the E8M0 scale of 32-k group g of row r (byte op_sel of its scale register). The
 // accumulator lane l holds column l%32, rows 8(j/4) + 4(l/32) + (j%4) for j < 16.
 //
-// Tiling: block tile BM x BN, K step 128 (four scale groups), WM x WN wavefronts each
-// owning a (BM/WM) x (BN/WN) tile of 32x32 MFMA fragments. A and B tiles are staged
-// through LDS with double buffering (global loads for step k+1 are in flight while step k
-// computes). LDS rows are 128 bytes; the 16-byte chunk index is XOR-swizzled with (row % 8)
-// so that the 32 lanes reading 16 bytes from 32 consecutive rows spread over all banks.
+// Operands in HBM: codes in 64-k panels (64 k of 16 consecutive rows are one contiguous
+// kilobyte), scales in 128-k planes (the four scale bytes of a row for 128 k are one word;
+// consecutive rows' words are adjacent) -- see kernels.h.
+//
+// Tiling: block tile BM x BN (256 x 256, 256 x 128 or 128 x 128), four wavefronts in a 2 x 2
+// grid, each owning a (BM/2) x (BN/2) tile of 32x32 MFMA fragments (accumulators in AGPRs).
+// K advances in 64-k stages through a ring of four LDS stages filled by direct global->LDS
+// loads (one 1 KB load per 16 rows; three stages in flight while one is consumed); the
+// fragments of the next stage are read into a second register set while the matrix
+// instructions of the current one run. LDS rows are 64 bytes; the 16-byte chunk index is
+// XOR-swizzled with (row / 4) % 4 so that a 16-lane phase of ds_read_b128 over 16
+// consecutive rows hits 16 distinct bank groups.
 //
 // Schedulers (expert-offset driven; no host synchronisation):
 //   M-grouped (FC1, FC2, both dgrads): A rows are the padded expert-major tokens; the block
 //     at row tile m0 finds its expert e from the device offsets (offs[e] <= m0 < offs[e+1])
 //     and multiplies by expert e's B. Tiles at or past offs[E] exit. BM divides
-//     pad_multiple, so no tile straddles two experts.
-//   K-grouped (both wgrads): blockIdx.z = expert; K runs over the expert's token segment
-//     (the real rows rounded up to 128; pad rows are zero codes). A zero-token expert runs
-//     no K step and stores zeros.
+//     pad_multiple, so no tile straddles two experts. Tiles are ordered per XCD for L2
+//     reuse, and the last (T mod #CU) tiles are split into sub-tiles (see TailCfg).
+//   K-grouped (both wgrads): one tile grid per expert, experts longest-K first; K runs over
+//     the expert's token segment (the real rows rounded up to 128; pad rows are zero codes).
+//     A zero-token expert runs no K step and stores zeros.
 #include <atomic>
 #include <type_traits>
 
@@ -735,9 +743,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
 
 // ------------------------------------------------------------------ host launchers
 
-// Tile configurations (4 wavefronts): 256x128 (wavefront tile 128x64) where the dimensions
-// allow, else 128x128 (64x64). M-grouped row tiles divide pad_multiple. (256x256 with a
-// 128x128 wavefront tile measured slower: only two LDS stages fit and its epilogues spill.)
+// Tile configurations (4 wavefronts): 256x256 (wavefront tile 128x128) when N is a multiple
+// of 256 and the rows allow 256-row tiles (M-grouped: pad_multiple 256; the dSwiGLU epilogue's
+// staging needs 256x128), 256x128 otherwise, 128x128 for pad_multiple 128. M-grouped row tiles
+// divide pad_multiple.
 template <int BM, int BN, int SCHED, int EPI>
 static hipError_t launch_cfg(const GemmParams& p, hipStream_t st) {
   // 1-D grids: the kernel maps block ids to tiles (see the schedulers)
