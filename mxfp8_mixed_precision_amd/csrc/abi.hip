@@ -347,7 +347,7 @@ mxf_status grouped_mlp_fwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
     MXF_HIP(timed("quant_x", st, [&] {
               return mxf_launch_quant_tokens(x, M, D, offs, counts, (int)E, desc->pad_multiple, T(MXF_T_XQ_R),
                                              T(MXF_T_XS_R), T(MXF_T_XQ_C), T(MXF_T_XS_C),
-                                             (int32_t*)T(MXF_T_STATUS), st);
+                                             (int32_t*)T(MXF_T_STATUS), true, st);
             }), "X quantize launch");
   }
 
@@ -432,7 +432,7 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   MXF_HIP(timed("quant_dy", st, [&] {
             return mxf_launch_quant_tokens(dy, M, D, offs, counts, (int)E, desc->pad_multiple, T(MXF_T_DYQ_R),
                                            T(MXF_T_DYS_R), T(MXF_T_DYQ_C), T(MXF_T_DYS_C),
-                                           (int32_t*)T(MXF_T_STATUS), st);
+                                           (int32_t*)T(MXF_T_STATUS), false, st);
           }), "dY quantize launch");
   mxf::GemmParams base = {};
   base.offs = offs;

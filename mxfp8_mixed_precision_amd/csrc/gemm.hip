@@ -343,7 +343,7 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
         dst = reinterpret_cast<uint16_t*>((row & 32) ? p.C2 : p.C) + ebase +
               ((row >> 6) * 32 + (row & 31)) * p.ldc + col;
       }
-      *reinterpret_cast<uint4*>(dst) = v;
+      store16_nt(dst, v);  // y, dx, dW are not read again by the library
     }
     return;
   }
@@ -398,10 +398,11 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
         }
         const int64_t rec = ((wrow0 + i * 32) >> 5) * (F >> 5) + ((hc0 + tc0 / 2 + jp * 32) >> 5);
         uint4* dg = reinterpret_cast<uint4*>(p.h13 + rec * 2048) + 2 * lane;
-        dg[0] = make_uint4(gw[0], gw[1], gw[2], gw[3]);
-        dg[1] = make_uint4(gw[4], gw[5], gw[6], gw[7]);
-        dg[128] = make_uint4(uw[0], uw[1], uw[2], uw[3]);
-        dg[129] = make_uint4(uw[4], uw[5], uw[6], uw[7]);
+        // saved for the backward pass: non-temporal (keeps the L2 for the GEMM operands)
+        store16_nt(dg, make_uint4(gw[0], gw[1], gw[2], gw[3]));
+        store16_nt(dg + 1, make_uint4(gw[4], gw[5], gw[6], gw[7]));
+        store16_nt(dg + 128, make_uint4(uw[0], uw[1], uw[2], uw[3]));
+        store16_nt(dg + 129, make_uint4(uw[4], uw[5], uw[6], uw[7]));
         uint32_t am = amax16(hw);
         am = max(am, (uint32_t)__shfl_xor((int)am, 32));
         const Scale s = scale_from_amax(am);
@@ -450,8 +451,8 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
       const uint2 a = *reinterpret_cast<const uint2*>(qT + hc * QP + c * 16);
       const uint2 b = *reinterpret_cast<const uint2*>(qT + hc * QP + c * 16 + 8);
       const int64_t tok = m0 + c * 16;
-      *reinterpret_cast<uint4*>(p.q_c + (tok >> 6) * 64 * F + (hc0 + hc) * 64 + (tok & 63)) =
-          make_uint4(a.x, a.y, b.x, b.y);
+      store16_nt(p.q_c + (tok >> 6) * 64 * F + (hc0 + hc) * 64 + (tok & 63),  // saved for backward
+                 make_uint4(a.x, a.y, b.x, b.y));
     }
     // column scales: SG groups per column (whole 128-row planes: m0 is a multiple of 128)
     for (int t = tid; t < HCB * (SG / 4); t += T::NT) {

@@ -48,7 +48,7 @@ hipError_t mxf_launch_quantize(const void* x, int64_t rows, int64_t cols, uint32
                                void* s_row, void* q_col, void* s_col, hipStream_t st);
 hipError_t mxf_launch_quant_tokens(const void* x, int64_t mcap, int64_t D, const int32_t* offs,
                                    const int32_t* counts, int E, int pad, void* q_r, void* s_r,
-                                   void* q_c, void* s_c, int32_t* status, hipStream_t st);
+                                   void* q_c, void* s_c, int32_t* status, bool saved_c, hipStream_t st);
 hipError_t mxf_launch_quant_weights(const void* w, const void* w3, bool pack13, int64_t E, int64_t rows,
                                     int64_t cols, void* q_r, void* s_r, void* q_c, void* s_c,
                                     hipStream_t st);

@@ -114,6 +114,14 @@ __device__ __forceinline__ uint32_t quant32(const uint32_t* v, uint32_t* codes) 
   return s.byte;
 }
 
+// 16-byte store that bypasses the caches' retention (non-temporal): for outputs no kernel of
+// the library reads back soon (the GEMM results, the tensors saved for the backward pass), so
+// they do not evict operand panels that the running GEMMs re-read from L2.
+__device__ __forceinline__ void store16_nt(void* dst, uint4 v) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store((u32x4){v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(dst));
+}
+
 // Value held by lane l ^ 1 (DPP quad permute [1,0,3,2]) and by lane l ^ 2 ([2,3,0,1]).
 __device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);

@@ -50,6 +50,7 @@ struct QuantParams {
   int64_t n_assign;                     // QK_GATHER: tokens * topk
   int topk;                             // QK_GATHER
   int col_fast;                         // grid x walks column tiles (set by the launcher)
+  int nt_c;                             // column codes saved for the backward pass: non-temporal stores
   int blk;                              // codes in 64-k panels (the MLP's GEMM operands): q_r byte
                                         // (r, c) at (c/64)*64*rows + 64r + c%64, q_c byte (c, r) at
                                         // (r/64)*64*cols + 64c + r%64; else row-major
@@ -233,7 +234,8 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
         const uint2 b = *reinterpret_cast<const uint2*>(qT + cl * QTP + ch * 16 + 8);
         const int64_t r = row0 + ch * 16;
         const int64_t o = p.blk ? (r >> 6) * 64 * p.cols + (col0 + cl) * 64 + (r & 63) : (col0 + cl) * p.ldc + r;
-        *reinterpret_cast<uint4*>(q_c + o) = make_uint4(a.x, a.y, b.x, b.y);
+        if (p.nt_c) store16_nt(q_c + o, make_uint4(a.x, a.y, b.x, b.y));
+        else *reinterpret_cast<uint4*>(q_c + o) = make_uint4(a.x, a.y, b.x, b.y);
       }
     }
     if (tid < 128 && col0 + tid < p.cols) {
@@ -419,9 +421,10 @@ hipError_t mxf_launch_quantize(const void* x, int64_t rows, int64_t cols, uint32
 // planes (row-wise [D/128][mcap][4], column-wise [mcap/128][D][4]).
 hipError_t mxf_launch_quant_tokens(const void* x, int64_t mcap, int64_t D, const int32_t* offs,
                                    const int32_t* counts, int E, int pad, void* q_r, void* s_r,
-                                   void* q_c, void* s_c, int32_t* status, hipStream_t st) {
+                                   void* q_c, void* s_c, int32_t* status, bool saved_c, hipStream_t st) {
   mxf::QuantParams p = {};
   p.blk = 1;  // GEMM operands: codes in 64-k panels
+  p.nt_c = saved_c;
   p.src = (const uint16_t*)x;
   p.rows = mcap;
   p.cols = D;
@@ -450,6 +453,7 @@ hipError_t mxf_launch_quant_gather(const void* x_tokens, int64_t n_assign, int t
                                    hipStream_t st) {
   mxf::QuantParams p = {};
   p.blk = 1;  // GEMM operands: codes in 64-k panels
+  p.nt_c = 1;  // column codes are saved for the backward pass
   p.src = (const uint16_t*)x_tokens;
   p.rows = mcap;
   p.cols = D;
@@ -472,6 +476,7 @@ hipError_t mxf_launch_swiglu_quant(const void* h13, int64_t mcap, int64_t F, con
                                    void* s_c, hipStream_t st) {
   mxf::QuantParams p = {};
   p.blk = 1;  // GEMM operands: codes in 64-k panels
+  p.nt_c = 1;  // column codes are saved for the backward pass
   p.src = (const uint16_t*)h13;
   p.rows = mcap;
   p.cols = F;
@@ -510,6 +515,7 @@ hipError_t mxf_launch_quant_weights(const void* w, const void* w3, bool pack13, 
                                     hipStream_t st) {
   mxf::QuantParams p = {};
   p.blk = 1;  // GEMM operands: codes in 64-k panels
+  p.nt_c = 1;  // column codes are saved for the backward pass
   p.src = (const uint16_t*)w;
   p.src2 = (const uint16_t*)w3;
   p.rows = rows;
