@@ -122,6 +122,12 @@ __device__ __forceinline__ void store16_nt(void* dst, uint4 v) {
   __builtin_nontemporal_store((u32x4){v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(dst));
 }
 
+__device__ __forceinline__ uint4 load16_nt(const void* src) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Value held by lane l ^ 1 (DPP quad permute [1,0,3,2]) and by lane l ^ 2 ([2,3,0,1]).
 __device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);

@@ -151,7 +151,9 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
         x[j][k] = up ? (du0 | (du1 << 16)) : (dg0 | (dg1 << 16));
       }
     } else if (colok && r < rend) {
-      const uint4 v = *reinterpret_cast<const uint4*>(src + (src_row0 + 8 * s + j) * p.cols + col);
+      // the BF16 input is read exactly once: non-temporal, so it does not evict the L2 lines of a
+      // GEMM running beside this kernel
+      const uint4 v = load16_nt(src + (src_row0 + 8 * s + j) * p.cols + col);
       x[j][0] = v.x; x[j][1] = v.y; x[j][2] = v.z; x[j][3] = v.w;
     } else {
       x[j][0] = x[j][1] = x[j][2] = x[j][3] = 0u;
