@@ -494,10 +494,10 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
       for (int j = 0; j < T::FN; ++j) {
         const int64_t rec = ((wrow0 + i * 32) >> 5) * (F >> 5) + ((wcol0 + j * 32) >> 5);
         const uint4* src = reinterpret_cast<const uint4*>(p.h13 + rec * 2048) + 2 * lane;
-        gs[buf][j][0] = src[0];
-        gs[buf][j][1] = src[1];
-        us[buf][j][0] = src[128];
-        us[buf][j][1] = src[129];
+        gs[buf][j][0] = load16_nt(src);  // read once: non-temporal
+        gs[buf][j][1] = load16_nt(src + 1);
+        us[buf][j][0] = load16_nt(src + 128);
+        us[buf][j][1] = load16_nt(src + 129);
       }
     };
     load_gu(0, 0);
