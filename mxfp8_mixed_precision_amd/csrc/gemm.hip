@@ -607,7 +607,7 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
 }
 
 // Tail sub-tiles (M-grouped): when the tile count T is not a multiple of the CU count, the last
-// R = T mod #CU tiles (in raster order) would leave most CUs idle in the final round. Each of them
+// R = T mod #CU tiles (in raster order) would leave most CUs idle in a final round. Each of them
 // is split into Q sub-tiles (Q = 4 when 4R <= #CU, else 2 when 2R <= #CU): BM/2 x BN/2, or
 // BM x BN/2 (BN >= 256) / BM/2 x BN, computed by separate blocks with the same pipeline.
 template <int BM, int BN>
@@ -654,16 +654,22 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
       if (q > 1) nfull = ntiles - rem;
       else rem = 0;
     }
+    // The sub-tile blocks take the lowest block ids (padded to whole rounds of the 8 XCDs):
+    // they finish early and their CUs move on to whole tiles out of phase with the rest, which
+    // spreads the epilogues' store bursts over time.
+    const int64_t nsub = (rem * q + 7) / 8 * 8;
     const int64_t b = blockIdx.x;
-    const bool tail = b >= nfull;  // a sub-tile of one of the last rem tiles
+    const bool tail = b < nsub;  // a sub-tile of one of the last rem tiles (raster order)
     int64_t t, part = 0;
     if (!tail) {
-      const int64_t q8 = nfull / 8, r8 = nfull % 8, x8 = b % 8, s8 = b / 8;
+      const int64_t f = b - nsub;  // whole tile f; f % 8 is still the block's XCD
+      if (f >= nfull) return;
+      const int64_t q8 = nfull / 8, r8 = nfull % 8, x8 = f % 8, s8 = f / 8;
       t = x8 < r8 ? x8 * (q8 + 1) + s8 : r8 * (q8 + 1) + (x8 - r8) * q8 + s8;
     } else {
-      if (b - nfull >= rem * q) return;
-      t = nfull + (b - nfull) / q;
-      part = (b - nfull) % q;
+      if (b >= rem * q) return;
+      t = nfull + b / q;
+      part = b % q;
     }
     const int64_t grp = t / (GM * ntn);
     const int64_t first = grp * GM;
