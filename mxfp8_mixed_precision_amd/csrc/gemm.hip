@@ -62,24 +62,27 @@ struct Tile {
   static constexpr int TN = BN / WN;
   static constexpr int FM = TM / 32;
   static constexpr int FN = TN / 32;
-  // one stage: A tile [BM][64 B], B tile [BN][64 B], then one 256-byte slot of scale words per
-  // wavefront for A and for B (rows beyond BM / BN land in unused slots). A scale word holds
-  // the four E8M0 bytes of 128 k, so both stages of a 128-k block load the same words.
+  // one stage: A tile [BM][64 B], B tile [BN][64 B]. The scale words (four E8M0 bytes of
+  // 128 k per row) of a 128-k block serve its two stages: the even stage loads them into a
+  // ring of three scale slots after the stage slots (one 256-byte piece per wavefront for A,
+  // then for B; rows beyond BM / BN land in unused bytes), the odd stage reads the same slot.
   static constexpr int A_OFF = 0;
   static constexpr int B_OFF = BM * BK;
-  static constexpr int SA_OFF = (BM + BN) * BK;
-  static constexpr int SB_OFF = SA_OFF + NW * 256;
-  static constexpr int STAGE = SB_OFF + NW * 256;
+  static constexpr int STAGE = (BM + BN) * BK;
+  static constexpr int NSC = 3;
+  static constexpr int SC_OFF = S * STAGE;
+  static constexpr int SC_SLOT = 2 * NW * 256;
   static constexpr int LDS_BYTES = 160 * 1024;
   static constexpr int IA = BM / 16 / NW;  // 1 KB direct-to-LDS loads (16 rows) of A, per wavefront
   static constexpr int IB = BN / 16 / NW;
-  static constexpr int L = IA + IB + 2;    // loads per wavefront per stage (with the scale words)
+  static constexpr int LO = IA + IB;       // loads per wavefront for an odd stage
+  static constexpr int L = LO + 2;         // for an even stage (with the scale words)
   // epilogue staging: BF16 output tile; SwiGLU: row-major h tile + transposed codes + scales;
   // dSwiGLU (one wavefront row at a time): packed dG/dU tile + transposed codes + scales
   static constexpr int EPI_ST = BM * (BN + 8) * 2;
   static constexpr int EPI_SW = BM * (BN / 2 + 8) * 2 + (BN / 2) * (BM + 8) + (BN / 2) * (BM / 32);
   static constexpr int EPI_DSW = TM * (2 * BN + 8) * 2 + 2 * BN * (TM + 8) + 2 * BN * (TM / 32);
-  static constexpr int LDS_MAIN = S * STAGE;
+  static constexpr int LDS_MAIN = S * STAGE + NSC * SC_SLOT;
   static constexpr int imax(int a, int b) { return a > b ? a : b; }
   // LDS of a kernel instance: the main loop's stages or its epilogue's staging
   static constexpr int lds(int epi) {
@@ -88,8 +91,8 @@ struct Tile {
   static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "tile/wavefront mismatch");
   static_assert(BM <= 64 * NW && BN <= 64 * NW, "one scale-word load per wavefront and operand");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 fragments");
-  static_assert(S * STAGE <= LDS_BYTES, "pipeline does not fit in LDS");
-  static_assert(S * L <= 63, "loads in flight exceed the vmcnt range");
+  static_assert(LDS_MAIN <= LDS_BYTES, "pipeline does not fit in LDS");
+  static_assert(S % 2 == 0 && (S / 2) * (L + LO) <= 63, "loads in flight exceed the vmcnt range");
 };
 
 // LDS tile layout: 64-byte rows, 16-byte chunk c of row r stored at chunk c ^ ((r / 4) % 4). A
@@ -175,22 +178,24 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
   const uint32_t sa_v = (uint32_t)(((wid * 64 + lane) % BM) * p.ldas);
   const uint32_t sb_v = (uint32_t)(((wid * 64 + lane) % BN) * p.ldbs);
   const uint32_t lds0 = lds_addr(smem);
-  // One of the L direct-to-LDS loads of stage ks into the LDS slot of stage kt (ks == kt, or
+  // One of the direct-to-LDS loads of stage ks into the LDS slot of stage kt (ks == kt, or
   // a surplus load of the last stage into a free slot, which keeps every step's load count
-  // and waits the same): q < IA are A-tile loads, then IB B-tile loads, then the A and B
-  // scale words (of the 128-k block holding the stage). q is a compile-time constant.
+  // and waits the same): q < IA are A-tile loads, then IB B-tile loads, then (even stages
+  // only) the A and B scale words of the 128-k block holding the stage, into scale slot
+  // (kt / 2) % NSC. q is a compile-time constant.
   auto issue_one = [&](int q, int ks, int kt) {
     const int64_t k0 = (int64_t)ks * T::BK;
     const uint32_t st = lds0 + (kt % T::S) * T::STAGE;
+    const uint32_t sc = lds0 + T::SC_OFF + ((kt >> 1) % T::NSC) * T::SC_SLOT;
     if (q < T::IA) {
       g2lds16(a_s + q * 1024 + ks * p.akp, a_v, st + T::A_OFF + (wid_u * T::IA + q) * 1024);
     } else if (q < T::IA + T::IB) {
       const int i = q - T::IA;
       g2lds16(b_s + i * 1024 + ks * p.bkp, b_v, st + T::B_OFF + (wid_u * T::IB + i) * 1024);
     } else if (q == T::IA + T::IB) {
-      g2lds4(Asg + (k0 >> 7) * p.kbsa, sa_v, st + T::SA_OFF + wid_u * 256);
+      g2lds4(Asg + (k0 >> 7) * p.kbsa, sa_v, sc + wid_u * 256);
     } else {
-      g2lds4(Bsg + (k0 >> 7) * p.kbsb, sb_v, st + T::SB_OFF + wid_u * 256);
+      g2lds4(Bsg + (k0 >> 7) * p.kbsb, sb_v, sc + T::NW * 256 + wid_u * 256);
     }
   };
 
@@ -207,6 +212,7 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
   auto read_one = [&](int r, int kt, auto par) {
     constexpr int B = decltype(par)::value;  // kt % 2
     const uint8_t* base = smem + (kt % T::S) * T::STAGE;
+    const uint8_t* sbase = smem + T::SC_OFF + ((kt >> 1) % T::NSC) * T::SC_SLOT;
     if (r < 2 * T::FM) {
       const int i = r >> 1, hi = r & 1;
       const uint4 v = *reinterpret_cast<const uint4*>(base + T::A_OFF + swz(tr0 + i * 32 + r32, 2 * hi + g));
@@ -219,10 +225,10 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
       fb[B][j][4 * hi + 2] = (int)v.z; fb[B][j][4 * hi + 3] = (int)v.w;
     } else if (r < 2 * (T::FM + T::FN) + T::FM) {
       const int i = r - 2 * (T::FM + T::FN);
-      sa[B][i] = base[T::SA_OFF + (tr0 + i * 32 + r32) * 4 + 2 * B + g];
+      sa[B][i] = sbase[(tr0 + i * 32 + r32) * 4 + 2 * B + g];
     } else {
       const int j = r - 2 * (T::FM + T::FN) - T::FM;
-      sb[B][j] = base[T::SB_OFF + (tc0 + j * 32 + r32) * 4 + 2 * B + g];
+      sb[B][j] = sbase[T::NW * 256 + (tc0 + j * 32 + r32) * 4 + 2 * B + g];
     }
   };
 
@@ -242,9 +248,9 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
 #pragma unroll
     for (int st = 0; st < T::S; ++st) {
 #pragma unroll
-      for (int q = 0; q < T::L; ++q) issue_one(q, st < KT ? st : KT - 1, st);
+      for (int q = 0; q < ((st & 1) ? T::LO : T::L); ++q) issue_one(q, st < KT ? st : KT - 1, st);
     }
-    wait_vmcnt<3 * T::L>();
+    wait_vmcnt<2 * T::LO + T::L>();  // stage 0 landed; stages 1 - 3 may be in flight
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < NR; ++r) read_one(r, 0, I0());
@@ -253,7 +259,8 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
   auto step = [&](int kt, auto par, auto more, auto load) {
     constexpr int P = decltype(par)::value;
     constexpr bool MORE = decltype(more)::value, LOAD = decltype(load)::value;
-    if (MORE) wait_vmcnt<2 * T::L>();
+    constexpr int LL = P ? T::LO : T::L;  // loads of stage kt + 4 (same parity as kt)
+    if (MORE) wait_vmcnt<T::L + T::LO>();  // stage kt+1 landed; kt+2 and kt+3 may be in flight
     __syncthreads();
     const int ks = kt + 4 < KT ? kt + 4 : KT - 1;
 #pragma unroll
@@ -266,12 +273,12 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
         for (int r = m * NR / NMF; r < (m + 1) * NR / NMF; ++r)
           read_one(r, kt + 1, std::integral_constant<int, 1 - P>());
       }
-      if (LOAD && m < T::L) issue_one(m, ks, kt + 4);
+      if (LOAD && m < LL) issue_one(m, ks, kt + 4);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (LOAD) {
 #pragma unroll
-      for (int q = NMF; q < T::L; ++q) issue_one(q, ks, kt + 4);
+      for (int q = NMF; q < LL; ++q) issue_one(q, ks, kt + 4);
     }
   };
   using T_ = std::true_type;
