@@ -121,8 +121,10 @@ def main():
                     help="only run a plain 1 GiB device copy (reference kernel for HBM byte counters)")
     ap.add_argument("--no-plans", action="store_true",
                     help="skip the fused/unfused plan and dispatch A/B legs (profiling runs: they launch other kernels)")
+    ap.add_argument("--concurrent", action="store_true",
+                    help="time the steps with MXF_CONCURRENT (helper streams) instead of serial launches")
     ap.add_argument("--serial", action="store_true",
-                    help="time with MXF_SERIAL too (every kernel alone; for profiler runs)")
+                    help="launch with MXF_SERIAL stated explicitly (the default order; profiler runs)")
     ap.add_argument("--quant-only", action="store_true",
                     help="only measure the standalone quantizer (for a profiler run of that kernel alone)")
     args = ap.parse_args()
@@ -167,7 +169,8 @@ def main():
         sets.append({k: p[k] for k in ("x", "w1", "w3", "w2", "dy")})
     offs_t = torch.tensor(offs, dtype=torch.int32, device=dev)
     counts_t = torch.tensor(counts, dtype=torch.int32, device=dev)
-    ctx = mx.MlpContext(E, D, F, pad, mcap, flags=mx.SERIAL if args.serial else 0, device=dev)
+    ctx = mx.MlpContext(E, D, F, pad, mcap, flags=mx.CONCURRENT if args.concurrent else (mx.SERIAL if args.serial else 0),
+                        device=dev)
     y = torch.empty((mcap, D), dtype=torch.bfloat16, device=dev)
     dx = torch.empty((mcap, D), dtype=torch.bfloat16, device=dev)
     dw1 = torch.empty((E, F, D), dtype=torch.bfloat16, device=dev)
@@ -199,9 +202,9 @@ def main():
     value = useful / (ms_per_step / 1e3) / 1e12
 
     # Per-kernel timing: library-internal HIP events on each launch's stream, over the same
-    # steps again with MXF_SERIAL, so that every kernel runs alone on the GPU (in the timed
-    # steps above some launches of a call overlap on helper streams, which would stretch each
-    # one's own duration).
+    # steps again with MXF_SERIAL, so that every kernel runs alone on the GPU (with
+    # --concurrent some launches of the timed steps overlap on helper streams, which would
+    # stretch each one's own duration; the events add a little time between launches).
     sctx = mx.MlpContext(E, D, F, pad, mcap, flags=mx.SERIAL, device=dev)
 
     def sstep(i):
@@ -260,7 +263,7 @@ def main():
         "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 4),
         "roofline": roof,
         "kernels": kernels,
-        "launches": "serial (MXF_SERIAL)" if args.serial else "concurrent where independent (helper streams)",
+        "launches": "concurrent where independent (MXF_CONCURRENT)" if args.concurrent else "serial (default)",
         "kernels_timing": "a second pass of the same steps with MXF_SERIAL (each kernel alone on the GPU)",
         "serial_ms_per_step": round((t3 - t2) * 1e3 / args.steps, 4),
     }

@@ -133,10 +133,13 @@ mxf_status mxfp8_dequantize(const void* q, const void* s, int64_t rows, int64_t 
 #define MXF_X_QUANTIZED 16u /* grouped_mlp_fwd: X's dual codes were already written into saved /
                               workspace by mxfp8_dispatch_quantize (same desc, offs, counts);
                               x is not read and may be NULL */
-#define MXF_SERIAL 4u      /* launch every kernel on the caller's stream, one after another
-                              (by default independent launches run concurrently on two helper
-                              streams forked from and joined into the caller's stream); for
-                              timing each kernel alone */
+#define MXF_SERIAL 4u      /* launch every kernel on the caller's stream, one after another:
+                              the default, stated explicitly (not with MXF_CONCURRENT) */
+#define MXF_CONCURRENT 32u /* run independent launches concurrently on two helper streams forked
+                              from and joined into the caller's stream (W2's quantization beside
+                              FC1; FC2 wgrad, FC1 wgrad and FC1 dgrad beside each other). Measured
+                              on MI355X it is slower than the serial order for the DSv3 rank
+                              shape (the GEMMs then share their L2 panels); kept for A/B runs */
 
 typedef struct {
   int32_t E;             /* local experts, 1 .. 1024 */
@@ -144,7 +147,8 @@ typedef struct {
   int32_t F;             /* expert hidden dim, multiple of 128 */
   int32_t pad_multiple;  /* 128 or 256: every expert segment is a multiple of this */
   int64_t m_capacity;    /* rows allocated in x/y/dy/dx; multiple of pad_multiple */
-  uint32_t flags;        /* MXF_OUT_F32 | MXF_DEBUG_F32 | MXF_SERIAL | MXF_UNFUSED | MXF_X_QUANTIZED */
+  uint32_t flags;        /* MXF_OUT_F32 | MXF_DEBUG_F32 | MXF_SERIAL | MXF_CONCURRENT | MXF_UNFUSED |
+                            MXF_X_QUANTIZED */
 } mxf_mlp_desc;
 
 /* Tensors held in the caller's buffers (for tests and inspection). Region: 0 = workspace,
@@ -197,9 +201,9 @@ size_t mxf_mlp_workspace_bytes(const mxf_mlp_desc* desc /* host */);
 mxf_status mxf_mlp_tensor(const mxf_mlp_desc* desc /* host */, int which, int* region /* host */,
                           size_t* offset /* host */, size_t* bytes /* host */);
 
-/* Streams: fwd and bwd enqueue their kernels asynchronously. Unless MXF_SERIAL is set, some of
- * them run on two helper streams owned by the calling host thread (one pair per device); the
- * helpers start after everything previously enqueued on `stream` and `stream` waits for them
+/* Streams: fwd and bwd enqueue their kernels asynchronously on `stream`. With MXF_CONCURRENT
+ * some of them run on two helper streams owned by the calling host thread (one pair per device);
+ * the helpers start after everything previously enqueued on `stream` and `stream` waits for them
  * before the call returns, so the call behaves as one ordered unit of work on `stream`.
  *
  * Forward. offs: int32 [E+1] (offs[0] = 0, non-decreasing, multiples of pad_multiple,

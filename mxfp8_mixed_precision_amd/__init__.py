@@ -6,7 +6,7 @@ this package is its Python binding. ``MlpContext`` allocates the caller-owned
 documented intermediate tensors as views, for tests and inspection.
 """
 from ._abi import (CAP_GFX950, COL, DEBUG_F32, DEQ_BF16, DEQ_E5M2, DEQ_F32, E5M2, DEV_BAD_EXPERT, DEV_BAD_OFFSETS, DEV_OK,
-                   DEV_OVERFLOW, EXPORTS, LIB_PATH, OUT_F32, SERIAL, UNFUSED, X_QUANTIZED, dequantize,
+                   CONCURRENT, DEV_OVERFLOW, EXPORTS, LIB_PATH, OUT_F32, SERIAL, UNFUSED, X_QUANTIZED, dequantize,
                    mxf_dispatch_permute, mxf_route_plan, route_plan_workspace_bytes, mxfp8_dequantize, mxfp8_dispatch_quantize, route_plan,
                    ROW, T, TENSORS, MlpDesc, MxfError, abi_version, grouped_mlp_bwd, grouped_mlp_fwd,
                    last_error, lib, make_desc, mlp_saved_bytes, mlp_tensor, mlp_workspace_bytes,

@@ -21,7 +21,7 @@ STATUS_NAMES = {OK: "MXF_OK", E_NULL: "MXF_E_NULL", E_SHAPE: "MXF_E_SHAPE", E_AL
 DEV_OK, DEV_BAD_OFFSETS, DEV_BAD_EXPERT, DEV_OVERFLOW = 0, 1, 2, 3
 CAP_GFX950 = 1
 ROW, COL, E5M2 = 1, 2, 4
-OUT_F32, DEBUG_F32, SERIAL, UNFUSED, X_QUANTIZED = 1, 2, 4, 8, 16
+OUT_F32, DEBUG_F32, SERIAL, UNFUSED, X_QUANTIZED, CONCURRENT = 1, 2, 4, 8, 16, 32
 DEQ_BF16, DEQ_F32, DEQ_E5M2 = 0, 1, 2
 
 # tensor ids (mxf_tensor)

@@ -111,9 +111,9 @@ struct Helpers {
 };
 thread_local Helpers g_helpers[kMaxDevices];
 
-// With MXF_SERIAL the "helpers" are the caller's stream itself (no fork, no join).
+// Unless MXF_CONCURRENT is set, the "helpers" are the caller's stream itself (no fork, no join).
 mxf_status get_helpers(Helpers** out, uint32_t flags, hipStream_t st) {
-  if (flags & MXF_SERIAL) {
+  if (!(flags & MXF_CONCURRENT)) {
     thread_local Helpers serial;
     serial.ready = true;
     serial.s[0] = serial.s[1] = st;
@@ -157,8 +157,11 @@ mxf_status check_desc(const mxf_mlp_desc* d) {
                 (long long)d->m_capacity, d->pad_multiple);
   if (d->m_capacity > (int64_t)1 << 30)
     return fail(MXF_E_SHAPE, "m_capacity = %lld: larger than 2^30 rows", (long long)d->m_capacity);
-  if (d->flags & ~(uint32_t)(MXF_OUT_F32 | MXF_DEBUG_F32 | MXF_SERIAL | MXF_UNFUSED | MXF_X_QUANTIZED))
+  if (d->flags & ~(uint32_t)(MXF_OUT_F32 | MXF_DEBUG_F32 | MXF_SERIAL | MXF_CONCURRENT | MXF_UNFUSED |
+                             MXF_X_QUANTIZED))
     return fail(MXF_E_ARG, "flags = 0x%x: unknown bits", d->flags);
+  if ((d->flags & MXF_SERIAL) && (d->flags & MXF_CONCURRENT))
+    return fail(MXF_E_ARG, "flags = 0x%x: MXF_SERIAL and MXF_CONCURRENT together", d->flags);
   if ((d->flags & MXF_UNFUSED) && (d->flags & MXF_DEBUG_F32))
     return fail(MXF_E_ARG, "flags = 0x%x: MXF_DEBUG_F32 is not available with MXF_UNFUSED", d->flags);
   return MXF_OK;

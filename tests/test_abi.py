@@ -77,8 +77,9 @@ def test_layout_is_consistent():
 @pytest.mark.parametrize("kw,code", [
     (dict(E=0), _abi.E_SHAPE), (dict(E=2000), _abi.E_SHAPE), (dict(D=200), _abi.E_SHAPE),
     (dict(F=96), _abi.E_SHAPE), (dict(pad=64), _abi.E_SHAPE), (dict(m=1000), _abi.E_SHAPE),
-    (dict(m=-128), _abi.E_SHAPE), (dict(flags=32), _abi.E_ARG),
-    (dict(flags=mx.UNFUSED | mx.DEBUG_F32), _abi.E_ARG),
+    (dict(m=-128), _abi.E_SHAPE),
+    (dict(flags=mx.UNFUSED | mx.DEBUG_F32), _abi.E_ARG), (dict(flags=mx.SERIAL | mx.CONCURRENT), _abi.E_ARG),
+    (dict(flags=64), _abi.E_ARG),
 ])
 def test_descriptor_rejections(kw, code):
     d = _desc(**kw)

@@ -227,10 +227,10 @@ def test_deterministic(tiny):
 
 
 def test_serial_launches_match_concurrent(tiny):
-    """MXF_SERIAL (every kernel on the caller's stream) and the default helper-stream fork/join
-    give bit-identical outputs and saved tensors."""
+    """The default serial launches and MXF_CONCURRENT's helper-stream fork/join give
+    bit-identical outputs and saved tensors."""
     mx, prob, r = tiny
-    r2 = run_mlp(mx, prob, mx.OUT_F32 | mx.DEBUG_F32 | mx.SERIAL)
+    r2 = run_mlp(mx, prob, mx.OUT_F32 | mx.DEBUG_F32 | mx.CONCURRENT)
     m = prob["offs"][-1]
     for k in ("y", "dx", "dw1", "dw3", "dw2"):
         assert torch.equal(r[k], r2[k]), k
