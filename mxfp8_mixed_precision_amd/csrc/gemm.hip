@@ -152,6 +152,14 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
   const int tc0 = wn * T::TN;
   const int KT = (int)((kend - kbeg) / T::BK);  // stages (even: K is a multiple of 128)
 
+  // Accumulator layout. Fragment (i, j) covers tile rows tr0 + 32 i + [0, 32) and columns
+  // tc0 + 32 j + [0, 32). Normal: lane (r32, g) holds column r32, rows 8 (q / 4) + 4 g + q % 4
+  // of it. Transposed (TRACC: the operands swap places in the matrix instruction, which then
+  // computes the fragment of C^T): lane (r32, g) holds row r32, columns 8 (q / 4) + 4 g + q % 4,
+  // so each group of four accumulators is four consecutive columns of one row -- one 8-byte
+  // BF16 write. The plain-store epilogues use it; SwiGLU and dSwiGLU pair gate/up fragments
+  // column-wise and keep the normal layout.
+  constexpr bool TRACC = (EPI == EPI_STORE || EPI == EPI_UNPACK13);
   v16f acc[T::FM][T::FN];
 #pragma unroll
   for (int i = 0; i < T::FM; ++i)
@@ -266,8 +274,12 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
 #pragma unroll
     for (int m = 0; m < NMF; ++m) {
       const int i = m / T::FN, j = m % T::FN;
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[P][i], fb[P][j], acc[i][j], 0, 0, 0,
-                                                                  (int)sa[P][i], 0, (int)sb[P][j]);
+      if constexpr (TRACC)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[P][j], fa[P][i], acc[i][j], 0, 0, 0,
+                                                                    (int)sb[P][j], 0, (int)sa[P][i]);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[P][i], fb[P][j], acc[i][j], 0, 0, 0,
+                                                                    (int)sa[P][i], 0, (int)sb[P][j]);
       if (MORE) {
 #pragma unroll
         for (int r = m * NR / NMF; r < (m + 1) * NR / NMF; ++r)
@@ -319,11 +331,12 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
         for (int j = 0; j < T::FN; ++j)
 #pragma unroll
           for (int q = 0; q < 16; ++q)
-            base[(8 * (q >> 2) + 4 * g + (q & 3)) * p.ldc + wcol0 + j * 32 + r32] = acc[i][j][q];
+            base[r32 * p.ldc + wcol0 + j * 32 + 8 * (q >> 2) + 4 * g + (q & 3)] = acc[i][j][q];
       }
       return;
     }
-    // BF16 tile [BM][BN] in LDS, then 16-byte row-contiguous copies
+    // BF16 tile [BM][BN] in LDS (8-byte writes of four columns), then 16-byte row-contiguous
+    // copies. Row stride BN + 8 elements: 16-byte aligned rows for the copy-out reads.
     constexpr int CP = BN + 8;
     uint16_t* cs = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
@@ -331,9 +344,12 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
 #pragma unroll
       for (int j = 0; j < T::FN; ++j)
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
-          cs[(tr0 + i * 32 + 8 * (q >> 2) + 4 * g + (q & 3)) * CP + tc0 + j * 32 + r32] =
-              (uint16_t)bf16_bits(acc[i][j][q]);
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t lo = bf16x2_bits(acc[i][j][4 * c], acc[i][j][4 * c + 1]);
+          const uint32_t hi = bf16x2_bits(acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]);
+          *reinterpret_cast<uint2*>(cs + (tr0 + i * 32 + r32) * CP + tc0 + j * 32 + 8 * c + 4 * g) =
+              make_uint2(lo, hi);
+        }
     __syncthreads();
     constexpr int CPR = BN / 8;  // 16-byte chunks per row
     static_assert((BM * CPR) % T::NT == 0, "whole copy rounds");
@@ -388,20 +404,12 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
 #pragma unroll
       for (int jp = 0; jp < T::FN / 2; ++jp) {
         const int hcl = tc0 / 2 + jp * 32 + r32;  // h column within the block
-        uint32_t gw[8], uw[8], hw[8];
+        uint32_t gw[8], uw[8], hw[8];  // slots 2t, 2t+1 as packed BF16 pairs
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          uint32_t gb[2], ub[2], hb[2];
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const int q = 2 * t + s;
-            gb[s] = bf16_bits(acc[i][2 * jp][q]);
-            ub[s] = bf16_bits(acc[i][2 * jp + 1][q]);
-            hb[s] = swiglu_h(gb[s], ub[s]);
-          }
-          gw[t] = gb[0] | (gb[1] << 16);
-          uw[t] = ub[0] | (ub[1] << 16);
-          hw[t] = hb[0] | (hb[1] << 16);
+          gw[t] = bf16x2_bits(acc[i][2 * jp][2 * t], acc[i][2 * jp][2 * t + 1]);
+          uw[t] = bf16x2_bits(acc[i][2 * jp + 1][2 * t], acc[i][2 * jp + 1][2 * t + 1]);
+          hw[t] = swiglu_h2(gw[t], uw[t]);
         }
         const int64_t rec = ((wrow0 + i * 32) >> 5) * (F >> 5) + ((hc0 + tc0 / 2 + jp * 32) >> 5);
         uint4* dg = reinterpret_cast<uint4*>(p.h13 + rec * 2048) + 2 * lane;
@@ -532,19 +540,8 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
                                   us[b][j][1].x, us[b][j][1].y, us[b][j][1].z, us[b][j][1].w};
           uint32_t dgw[8], duw[8];
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            uint32_t og = 0, ou = 0;
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-              const int q = 2 * t + s;
-              uint32_t dg, du;
-              dswiglu(bf16_bits(acc[i][j][q]), (gw[t] >> (16 * s)) & 0xFFFFu, (uw[t] >> (16 * s)) & 0xFFFFu, dg, du);
-              og |= dg << (16 * s);
-              ou |= du << (16 * s);
-            }
-            dgw[t] = og;
-            duw[t] = ou;
-          }
+          for (int t = 0; t < 8; ++t)
+            dswiglu2(bf16x2_bits(acc[i][j][2 * t], acc[i][j][2 * t + 1]), gw[t], uw[t], dgw[t], duw[t]);
           const int pcg = 2 * (tc0 + j * 32) + r32;  // packed column of dG (dU: + 32)
           const int rl = wm * RH + ii * 32 + 4 * g;  // staged row of slot 0
 #pragma unroll

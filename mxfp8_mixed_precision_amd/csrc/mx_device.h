@@ -157,29 +157,46 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)f);
 }
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+// Two fp32 values -> a packed BF16 pair (lo in bits 0-15), each rounded to nearest even: one
+// gfx950 two-lane conversion instead of two conversions and a pack.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+// The two halves of a packed BF16 pair as fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// sigmoid(g) without overflow for either sign: with e = exp(-|g|), 1 / (1 + e) for g >= 0 and
-// e / (1 + e) otherwise. Built from the hardware base-2 exponential and reciprocal (each
-// within about 1 ulp): the result is rounded to BF16 by every caller.
+// sigmoid(g) = 1 / (1 + 2^(-g log2 e)) from the hardware base-2 exponential and reciprocal
+// (each within about 1 ulp); every caller rounds its result to BF16. No select on the sign:
+// for g below about -87 the exponential reaches +inf (or the reciprocal leaves the fp32
+// normal range) and the result is 0 or a flushed denormal, where sigmoid itself is below
+// 2^-126; it is never NaN for a finite g.
 __device__ __forceinline__ float sigmoid_f(float g) {
-  const float e = __builtin_amdgcn_exp2f(-fabsf(g) * 1.44269504088896340736f);
-  const float r = __builtin_amdgcn_rcpf(1.0f + e);
-  return g >= 0.0f ? r : e * r;
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504088896340736f));
 }
 
 // The SwiGLU rounding points (shared by the fused GEMM epilogues and the standalone kernels, so
 // both compute bit-identical values): from the BF16 g, u of the FC1 output,
 // h = BF16(silu(g) * u); in backward, from BF16 dh, dG = BF16(dh u s (1 + g (1 - s))) and
 // dU = BF16(dh g s) with s = sigmoid(g). Arguments and results are BF16 bit patterns.
-__device__ __forceinline__ uint32_t swiglu_h(uint32_t gb, uint32_t ub) {
-  const float gf = bf16_to_f32(gb), uf = bf16_to_f32(ub);
-  return bf16_bits(gf * sigmoid_f(gf) * uf);
+// The helpers take and return packed BF16 pairs (two elements per 32-bit word).
+__device__ __forceinline__ float silu_mul(float gf, float uf) { return gf * sigmoid_f(gf) * uf; }
+__device__ __forceinline__ uint32_t swiglu_h2(uint32_t g2, uint32_t u2) {
+  return bf16x2_bits(silu_mul(bf16_lo(g2), bf16_lo(u2)), silu_mul(bf16_hi(g2), bf16_hi(u2)));
 }
-__device__ __forceinline__ void dswiglu(uint32_t dhb, uint32_t gb, uint32_t ub, uint32_t& dg, uint32_t& du) {
-  const float dh = bf16_to_f32(dhb), gf = bf16_to_f32(gb), uf = bf16_to_f32(ub);
+__device__ __forceinline__ void dswiglu_f(float dh, float gf, float uf, float& dg, float& du) {
   const float sg = sigmoid_f(gf);
-  dg = bf16_bits(dh * uf * sg * (1.0f + gf * (1.0f - sg)));
-  du = bf16_bits(dh * gf * sg);
+  dg = dh * uf * sg * (1.0f + gf * (1.0f - sg));
+  du = dh * gf * sg;
+}
+__device__ __forceinline__ void dswiglu2(uint32_t dh2, uint32_t g2, uint32_t u2, uint32_t& dg2, uint32_t& du2) {
+  float dg0, du0, dg1, du1;
+  dswiglu_f(bf16_lo(dh2), bf16_lo(g2), bf16_lo(u2), dg0, du0);
+  dswiglu_f(bf16_hi(dh2), bf16_hi(g2), bf16_hi(u2), dg1, du1);
+  dg2 = bf16x2_bits(dg0, dg1);
+  du2 = bf16x2_bits(du0, du1);
 }
 
 // Device-side check of the token-offset contract, done by one whole wavefront; every lane

@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
       const uint32_t g4[4] = {gv.x, gv.y, gv.z, gv.w}, u4[4] = {uv.x, uv.y, uv.z, uv.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        x[j][k] = swiglu_h(g4[k] & 0xFFFFu, u4[k] & 0xFFFFu) | (swiglu_h(g4[k] >> 16, u4[k] >> 16) << 16);
+        x[j][k] = swiglu_h2(g4[k], u4[k]);
     } else if (colok && r < rend && KIND == QK_DSWIGLU) {
       // packed column col: dG (col % 64 < 32) or dU of dh column 32 (col / 64) + col % 32
       const int64_t F = p.cols >> 1;
@@ -145,10 +145,9 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
       const bool up = (col & 32) != 0;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        uint32_t dg0, du0, dg1, du1;
-        dswiglu(d4[k] & 0xFFFFu, g4[k] & 0xFFFFu, u4[k] & 0xFFFFu, dg0, du0);
-        dswiglu(d4[k] >> 16, g4[k] >> 16, u4[k] >> 16, dg1, du1);
-        x[j][k] = up ? (du0 | (du1 << 16)) : (dg0 | (dg1 << 16));
+        uint32_t dg2, du2;
+        dswiglu2(d4[k], g4[k], u4[k], dg2, du2);
+        x[j][k] = up ? du2 : dg2;
       }
     } else if (colok && r < rend) {
       // the BF16 input is read exactly once: non-temporal, so it does not evict the L2 lines of a
@@ -313,7 +312,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* q, const ui
       if (BF16) {
         uint32_t h[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) h[i] = bf16_bits(f[2 * i]) | (bf16_bits(f[2 * i + 1]) << 16);
+        for (int i = 0; i < 8; ++i) h[i] = bf16x2_bits(f[2 * i], f[2 * i + 1]);
         uint4* o = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + r * cols + c16 * 16);
         o[0] = make_uint4(h[0], h[1], h[2], h[3]);
         o[1] = make_uint4(h[4], h[5], h[6], h[7]);
