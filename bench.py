@@ -131,7 +131,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE {world}) is not supported: "
-              "this build has no multi-GPU path (expert-parallel sharding is described in DESIGN.md).",
+              "the library runs one expert-parallel rank's share on one GPU and has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
 

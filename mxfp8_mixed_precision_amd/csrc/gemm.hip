@@ -479,27 +479,27 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
   }
 
   if (EPI == EPI_DSWIGLU) {
-    // N = F: acc = dh. Two rounds; in round hh every wavefront takes its fragment rows
+    // N = F: acc = dh. Two passes; in pass hh every wavefront takes its fragment rows
     // [hh FM/2, (hh+1) FM/2) (all SIMDs busy): dG = dh u s (1 + g (1 - s)), dU = dh g s with
     // s = sigmoid(g), from the saved g, u (4 KB records in accumulator order, so each lane's
     // slots arrive in its own registers), each rounded to BF16. Their column-wise groups are
     // quantized in registers (codes staged transposed in LDS) and the BF16 values staged
     // row-major in the packed order (gate group, then up group, per 32 columns); then the block
     // quantizes the staged rows' row-wise groups and copies the column codes out.
-    static_assert(T::FM % 2 == 0, "two rounds of whole fragment rows");
-    constexpr int FH = T::FM / 2;     // fragment rows per wavefront per round
-    constexpr int RH = T::TM / 2;     // rows per wavefront per round
+    static_assert(T::FM % 2 == 0, "two passes of whole fragment rows");
+    constexpr int FH = T::FM / 2;     // fragment rows per wavefront per pass
+    constexpr int RH = T::TM / 2;     // rows per wavefront per pass
     constexpr int PCB = 2 * BN;       // packed columns of the block
     constexpr int DP = PCB + 8;       // row-major tile pitch (bf16)
     constexpr int QP = T::TM + 8;     // transposed code tile pitch (bytes)
-    constexpr int SG = T::TM / 32;    // column groups staged per round
+    constexpr int SG = T::TM / 32;    // column groups staged per pass
     const int64_t F = p.N;
     const int64_t ld13 = 2 * F;
     const int64_t pc0 = 2 * n0;
     uint16_t* dR = reinterpret_cast<uint16_t*>(smem);
     uint8_t* qT = smem + T::TM * DP * 2;
     uint8_t* sT = qT + PCB * QP;
-    // staged row lr of round hh is block row (lr / RH) * TM + hh * RH + lr % RH
+    // staged row lr of pass hh is block row (lr / RH) * TM + hh * RH + lr % RH
     auto brow = [&](int hh, int lr) { return (lr / RH) * T::TM + hh * RH + lr % RH; };
     // g, u of two fragment rows (FN fragments each) in flight: row i + 2 is requested as soon
     // as row i has been consumed
@@ -583,7 +583,7 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
         const int64_t grp = pcol >> 5;
         if (!(c & 1)) p.s_r[row * p.sr_rs + (grp >> 2) * p.sr_kbs + (grp & 3)] = (uint8_t)s.byte;
       }
-      // dhq_c [2F, mcap] in 64-token panels: a round's RH consecutive block rows lie in one
+      // dhq_c [2F, mcap] in 64-token panels: a pass's RH consecutive block rows lie in one
       // panel (RH = 64) or half of one (RH = 32); G lanes cover a column's run of them,
       // consecutive columns on consecutive lane groups
       constexpr int CPC = T::TM / 16;
@@ -604,7 +604,7 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
         const int64_t rg = (m0 + brow(hh, gi * 32)) >> 5;
         p.s_c[(pc0 + pc) * p.sc_rs + (rg >> 2) * p.sc_kbs + (rg & 3)] = sT[pc * SG + gi];
       }
-      __syncthreads();  // the staging tiles are rewritten in the next round
+      __syncthreads();  // the staging tiles are rewritten in the second pass
     }
     return;
   }

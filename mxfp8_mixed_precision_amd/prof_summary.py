@@ -150,7 +150,7 @@ def main():
         lines.append("")
     cmds = open(args.commands).read().strip()
     name = "quantize" if args.quant_only else "mlp_fwd_bwd"
-    md = [f"# {name} kernels, workload `{args.workload}` (rocprofv3)", "", "Commands (repository root on the GPU box):",
+    md = [f"# {name} kernels, workload `{args.workload}` (rocprofv3)", "", "Commands (run from the repository root):",
           "", "```", cmds, "```", ""] + lines
     md.append("| kernel | launches | avg us | min us | max us | HBM read MB/launch | HBM write MB/launch |")
     md.append("|---|---|---|---|---|---|---|")

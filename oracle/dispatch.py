@@ -14,7 +14,7 @@ What is computed, and where it comes from:
   MXFP8, the Q_X step of the fused forward); a fused dispatch computes the same
   codes from the token rows without storing the permuted BF16 matrix.
 
-Readings of points the pages leave open (each one is listed in the design doc):
+Readings of points the pages leave open:
 
 * Input: expert ids [tokens, topk] (int), assignment a = t * topk + k routes
   token t's k-th choice to expert ids[t, k]. A token may name the same expert

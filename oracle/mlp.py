@@ -17,7 +17,7 @@ What is computed, and where it comes from:
   post-activation; section "Numerics and tests": the fused forward is bitwise
   equal to standalone-cast quantization.
 
-Readings of points the pages leave open (each one is listed in the design doc):
+Readings of points the pages leave open:
 
 * 32-block order: W13[e, 64j + i] = w1[e, 32j + i], W13[e, 64j + 32 + i] =
   w3[e, 32j + i] for i < 32 -- 32 gate rows then 32 up rows, alternating.

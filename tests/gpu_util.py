@@ -7,7 +7,7 @@ import workloads
 
 
 def require_gpu():
-    """Skip when no GPU is visible; on a GPU machine, fail loudly if the HIP library is unusable."""
+    """Skip when no GPU is visible; with a GPU present, fail loudly if the HIP library is unusable."""
     if not torch.cuda.is_available():
         pytest.skip("needs an MI355X GPU")
     import mxfp8_mixed_precision_amd as mx
