@@ -55,15 +55,10 @@ def traffic_for(kernel, workload):
     if not os.path.exists(path):
         return None
     try:
-        import hashlib
+        from mxfp8_mixed_precision_amd.prof_summary import source_sha256
         with open(path) as f:
             t = json.load(f)
-        h = hashlib.sha256()
-        csrc = os.path.join(ROOT, "mxfp8_mixed_precision_amd", "csrc")
-        for n in sorted(os.listdir(csrc)):
-            with open(os.path.join(csrc, n), "rb") as f:
-                h.update(f.read())
-        if t.get("source_sha256") != h.hexdigest():
+        if t.get("source_sha256") != source_sha256(ROOT):
             return None
         return t.get("kernels", {}).get(workload, {}).get(kernel)
     except Exception:

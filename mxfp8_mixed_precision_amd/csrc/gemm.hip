@@ -486,7 +486,7 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
     // quantized in registers (codes staged transposed in LDS) and the BF16 values staged
     // row-major in the packed order (gate group, then up group, per 32 columns); then the block
     // quantizes the staged rows' row-wise groups and copies the column codes out.
-    static_assert(T::FM % 2 == 0, "two passes of whole fragment rows");
+    static_assert(T::FM % 2 == 0, "two rounds of whole fragment rows");
     constexpr int FH = T::FM / 2;     // fragment rows per wavefront per pass
     constexpr int RH = T::TM / 2;     // rows per wavefront per pass
     constexpr int PCB = 2 * BN;       // packed columns of the block

@@ -41,12 +41,39 @@ EXPECT = {
 }
 
 
+def code_only(text):
+    """C/C++ source with comments removed and whitespace runs collapsed (string and character
+    literals kept as written): what the compiler sees, so that edits to comments or layout do
+    not count as kernel changes."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_sha256(root):
+    """sha256 over the kernel sources (file names and code without comments)."""
     h = hashlib.sha256()
     csrc = os.path.join(root, "mxfp8_mixed_precision_amd", "csrc")
     for n in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(csrc, n), encoding="utf-8") as f:
+            h.update(n.encode() + b"\0" + code_only(f.read()).encode())
     return h.hexdigest()
 
 
