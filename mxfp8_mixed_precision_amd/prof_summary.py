@@ -179,8 +179,8 @@ def main():
     name = "quantize" if args.quant_only else "mlp_fwd_bwd"
     md = [f"# {name} kernels, workload `{args.workload}` (rocprofv3)", "", "Commands (run from the repository root):",
           "", "```", cmds, "```", ""] + lines
-    md.append("| kernel | launches | avg us | min us | max us | HBM read MB/launch | HBM write MB/launch |")
-    md.append("|---|---|---|---|---|---|---|")
+    md.append("| kernel | launches | avg us | median us | min us | max us | HBM read MB/launch | HBM write MB/launch |")
+    md.append("|---|---|---|---|---|---|---|---|")
     order = ["quantize"] if args.quant_only else MLP_SEQUENCE
     for k in order:
         if k not in dur:
@@ -189,7 +189,8 @@ def main():
         t = traffic.get(k)
         rd = f"{t['fetch_bytes'] / 1e6:.1f}" if t else "-"
         wr = f"{t['write_bytes'] / 1e6:.1f}" if t else "-"
-        md.append(f"| {k} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} | {rd} | {wr} |")
+        med = sorted(v)[len(v) // 2]
+        md.append(f"| {k} | {len(v)} | {sum(v) / len(v):.2f} | {med:.2f} | {min(v):.2f} | {max(v):.2f} | {rd} | {wr} |")
     md.append("")
     path = os.path.join(args.out, f"{name}_{args.workload}.md")
     with open(path, "w") as f:
