@@ -50,6 +50,7 @@ struct QuantParams {
   int64_t n_assign;                     // QK_GATHER: tokens * topk
   int topk;                             // QK_GATHER
   int col_fast;                         // grid x walks column tiles (set by the launcher)
+  int macro8;                           // 1-D grid of 8x8-tile macro-tiles per XCD (launcher)
   int nt_c;                             // column codes saved for the backward pass: non-temporal stores
   int blk;                              // codes in 64-k panels (the MLP's GEMM operands): q_r byte
                                         // (r, c) at (c/64)*64*rows + 64r + c%64, q_c byte (c, r) at
@@ -76,8 +77,20 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
   const int64_t e = blockIdx.z;
   // with col_fast, consecutive blocks take the column tiles of one 128-row band, so the blocks
   // resident at a time read and write a few contiguous bands
-  const int64_t row0 = (int64_t)(p.col_fast ? blockIdx.y : blockIdx.x) * 128;
-  const int64_t col0 = (int64_t)(p.col_fast ? blockIdx.x : blockIdx.y) * 128;
+  int64_t row0 = (int64_t)(p.col_fast ? blockIdx.y : blockIdx.x) * 128;
+  int64_t col0 = (int64_t)(p.col_fast ? blockIdx.x : blockIdx.y) * 128;
+  if (p.macro8) {
+    // Row-major scales of a single matrix: a row's 32-byte scale sector spans 8 column tiles
+    // and a column's spans 8 row bands. Block L runs on XCD L % 8; each XCD takes whole
+    // macro-tiles of 8 bands x 8 column tiles, so every sector is filled inside one XCD's L2
+    // (split over XCDs, each L2 writes its few bytes back as a partial sector).
+    const int64_t L = blockIdx.x, x = L & 7, sq = L >> 3;
+    const int64_t m = x + 8 * (sq >> 6);         // macro-tile of the XCD's sq-th block
+    const int64_t w = sq & 63;                   // tile within it, band-major
+    const int64_t mcols = (p.cols + 1023) >> 10;  // macro-tiles across
+    row0 = ((m / mcols) * 8 + (w >> 3)) * 128;
+    col0 = ((m % mcols) * 8 + (w & 7)) * 128;
+  }
   const int64_t col = col0 + c * 8;
   const int64_t rw0 = row0 + w * 32;  // first row of this wavefront
   const int64_t r0 = rw0 + 8 * s;     // first row of this lane
@@ -372,7 +385,12 @@ static hipError_t launch_quant(int kind, uint32_t mode, const QuantParams& pin, 
   // slightly slower for [2048, 26112] and for the expert weight batches); grid y and z are
   // limited to 65535.
   p.col_fast = (batch == 1 && rt * 8 >= ct && rt <= 65535) || ct > 65535;
-  const dim3 grid((unsigned)(p.col_fast ? ct : rt), (unsigned)(p.col_fast ? rt : ct), (unsigned)(batch > 0 ? batch : 1));
+  // a single matrix with row-major scales on both sides: macro-tile order (see the kernel)
+  p.macro8 = kind == QK_PLAIN && batch == 1 && !p.blk && rt % 8 == 0 && ct % 8 == 0 &&
+             ((rt / 8) * (ct / 8)) % 8 == 0 && rt * ct <= 0x7FFFFFFF;
+  const dim3 grid = p.macro8 ? dim3((unsigned)(rt * ct), 1, 1)
+                             : dim3((unsigned)(p.col_fast ? ct : rt), (unsigned)(p.col_fast ? rt : ct),
+                                    (unsigned)(batch > 0 ? batch : 1));
   const dim3 block(256);
 #define MXF_QLAUNCH(K, R, C) hipLaunchKernelGGL((quant_dual_kernel<K, R, C>), grid, block, 0, st, p)
   if (kind == QK_PLAIN && e5m2) {
