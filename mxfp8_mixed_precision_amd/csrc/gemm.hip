@@ -342,7 +342,10 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
 #pragma unroll
     for (int i = 0; i < T::FM; ++i)
 #pragma unroll
-      for (int j = 0; j < T::FN; ++j)
+      for (int j = 0; j < T::FN; ++j) {
+        // the fragment stays in its AGPRs until here: its copies to VGPRs are made one fragment
+        // at a time, not all 256 ahead of the branch above (which spilled)
+        asm volatile("" : "+a"(acc[i][j]));
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const uint32_t lo = bf16x2_bits(acc[i][j][4 * c], acc[i][j][4 * c + 1]);
@@ -350,6 +353,7 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
           *reinterpret_cast<uint2*>(cs + (tr0 + i * 32 + r32) * CP + tc0 + j * 32 + 8 * c + 4 * g) =
               make_uint2(lo, hi);
         }
+      }
     __syncthreads();
     constexpr int CPR = BN / 8;  // 16-byte chunks per row
     static_assert((BM * CPR) % T::NT == 0, "whole copy rounds");
