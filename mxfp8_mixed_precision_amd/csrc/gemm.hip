@@ -101,11 +101,6 @@ struct Tile {
 // 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
-__device__ __forceinline__ void store_out(void* C, int64_t idx, float v, int f32) {
-  if (f32) reinterpret_cast<float*>(C)[idx] = v;
-  else reinterpret_cast<uint16_t*>(C)[idx] = (uint16_t)bf16_bits(v);
-}
-
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt low bits
 // [3:0] and high bits [15:14]; expcnt 7 and lgkmcnt 15 mean "no wait").
 template <int N>

@@ -97,23 +97,6 @@ __device__ __forceinline__ uint32_t cvt4(uint32_t v01, uint32_t v23, const Scale
   return r | s.nanmask;
 }
 
-// Amax magnitude bits of 32 BF16 values held in 16 packed words.
-__device__ __forceinline__ uint32_t amax32(const uint32_t* v) {
-  uint32_t m = mag2(v[0]);
-#pragma unroll
-  for (int i = 1; i < 16; ++i) m = pk_max_u16(m, mag2(v[i]));
-  return max(m & 0xFFFFu, m >> 16);
-}
-
-// Quantize 32 BF16 values (16 packed words, element order) into 32 codes (8 words) and
-// return the scale byte.
-__device__ __forceinline__ uint32_t quant32(const uint32_t* v, uint32_t* codes) {
-  const Scale s = scale_from_amax(amax32(v));
-#pragma unroll
-  for (int i = 0; i < 8; ++i) codes[i] = cvt4(v[2 * i], v[2 * i + 1], s);
-  return s.byte;
-}
-
 // 16-byte store that bypasses the caches' retention (non-temporal): for outputs no kernel of
 // the library reads back soon (the GEMM results, the tensors saved for the backward pass), so
 // they do not evict operand panels that the running GEMMs re-read from L2.
@@ -156,7 +139,6 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
 __device__ __forceinline__ uint32_t bf16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)f);
 }
-__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 // Two fp32 values -> a packed BF16 pair (lo in bits 0-15), each rounded to nearest even: one
 // gfx950 two-lane conversion instead of two conversions and a pack.
 typedef float f32x2 __attribute__((ext_vector_type(2)));
