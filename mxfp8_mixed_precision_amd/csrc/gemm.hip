@@ -81,7 +81,11 @@ struct Tile {
   // dSwiGLU (one wavefront row at a time): packed dG/dU tile + transposed codes + scales
   static constexpr int EPI_ST = BM * (BN + 8) * 2;
   static constexpr int EPI_SW = BM * (BN / 2 + 8) * 2 + (BN / 2) * (BM + 8) + (BN / 2) * (BM / 32);
-  static constexpr int EPI_DSW = TM * (2 * BN + 8) * 2 + 2 * BN * (TM + 8) + 2 * BN * (TM / 32);
+  // dSwiGLU passes: a wavefront's fragment rows in two halves (dSwiGLU runs on 64-column
+  // wavefront tiles, FN <= 2)
+  static constexpr int DSW_NP = 2;
+  static constexpr int DSW_SR = WM * (TM / DSW_NP);  // staged rows per pass
+  static constexpr int EPI_DSW = DSW_SR * (2 * BN + 8) * 2 + 2 * BN * (DSW_SR + 8) + 2 * BN * (DSW_SR / 32);
   static constexpr int LDS_MAIN = S * STAGE + NSC * SC_SLOT;
   static constexpr int imax(int a, int b) { return a > b ? a : b; }
   // LDS of a kernel instance: the main loop's stages or its epilogue's staging
@@ -478,44 +482,47 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
   }
 
   if (EPI == EPI_DSWIGLU) {
-    // N = F: acc = dh. Two passes; in pass hh every wavefront takes its fragment rows
-    // [hh FM/2, (hh+1) FM/2) (all SIMDs busy): dG = dh u s (1 + g (1 - s)), dU = dh g s with
+    // N = F: acc = dh. NP = 2 passes; in pass hh every wavefront takes its fragment rows
+    // [hh FH, (hh+1) FH) (all SIMDs busy): dG = dh u s (1 + g (1 - s)), dU = dh g s with
     // s = sigmoid(g), from the saved g, u (4 KB records in accumulator order, so each lane's
     // slots arrive in its own registers), each rounded to BF16. Their column-wise groups are
     // quantized in registers (codes staged transposed in LDS) and the BF16 values staged
     // row-major in the packed order (gate group, then up group, per 32 columns); then the block
     // quantizes the staged rows' row-wise groups and copies the column codes out.
-    static_assert(T::FM % 2 == 0, "two rounds of whole fragment rows");
-    constexpr int FH = T::FM / 2;     // fragment rows per wavefront per pass
-    constexpr int RH = T::TM / 2;     // rows per wavefront per pass
+    constexpr int NP = T::DSW_NP;     // passes (the staging of a pass fits the pipeline LDS)
+    static_assert(T::FM % NP == 0, "passes of whole fragment rows");
+    constexpr int FH = T::FM / NP;    // fragment rows per wavefront per pass
+    constexpr int RH = T::TM / NP;    // rows per wavefront per pass
+    constexpr int SR = T::DSW_SR;     // staged rows per pass (WM * RH)
     constexpr int PCB = 2 * BN;       // packed columns of the block
     constexpr int DP = PCB + 8;       // row-major tile pitch (bf16)
-    constexpr int QP = T::TM + 8;     // transposed code tile pitch (bytes)
-    constexpr int SG = T::TM / 32;    // column groups staged per pass
+    constexpr int QP = SR + 8;        // transposed code tile pitch (bytes)
+    constexpr int SG = SR / 32;       // column groups staged per pass
     const int64_t F = p.N;
     const int64_t ld13 = 2 * F;
     const int64_t pc0 = 2 * n0;
     uint16_t* dR = reinterpret_cast<uint16_t*>(smem);
-    uint8_t* qT = smem + T::TM * DP * 2;
+    uint8_t* qT = smem + SR * DP * 2;
     uint8_t* sT = qT + PCB * QP;
     // staged row lr of pass hh is block row (lr / RH) * TM + hh * RH + lr % RH
     auto brow = [&](int hh, int lr) { return (lr / RH) * T::TM + hh * RH + lr % RH; };
-    // g, u of two fragment rows (FN fragments each) in flight: row i + 2 is requested as soon
-    // as row i has been consumed
-    uint4 gs[2][T::FN][2], us[2][T::FN][2];
-    auto load_gu = [&](int i, int buf) {
-#pragma unroll
-      for (int j = 0; j < T::FN; ++j) {
-        const int64_t rec = ((wrow0 + i * 32) >> 5) * (F >> 5) + ((wcol0 + j * 32) >> 5);
-        const uint4* src = reinterpret_cast<const uint4*>(p.h13 + rec * 2048) + 2 * lane;
-        gs[buf][j][0] = load16_nt(src);  // read once: non-temporal
-        gs[buf][j][1] = load16_nt(src + 1);
-        us[buf][j][0] = load16_nt(src + 128);
-        us[buf][j][1] = load16_nt(src + 129);
-      }
+    // g, u of the fragments in flight, a ring of GR fragment slots in processing order
+    // (f = i FN + j): fragment f + GR - 1 is requested when fragment f is taken up
+    constexpr int NF = T::FM * T::FN;
+    static_assert(EPI != EPI_DSWIGLU || T::FN <= 2, "dSwiGLU runs on 64-column wavefront tiles");
+    constexpr int GR = 4;
+    uint4 gs[GR][2], us[GR][2];
+    auto load_gu = [&](int f) {
+      const int i = f / T::FN, j = f % T::FN, slot = f % GR;
+      const int64_t rec = ((wrow0 + i * 32) >> 5) * (F >> 5) + ((wcol0 + j * 32) >> 5);
+      const uint4* src = reinterpret_cast<const uint4*>(p.h13 + rec * 2048) + 2 * lane;
+      gs[slot][0] = load16_nt(src);  // read once: non-temporal
+      gs[slot][1] = load16_nt(src + 1);
+      us[slot][0] = load16_nt(src + 128);
+      us[slot][1] = load16_nt(src + 129);
     };
-    load_gu(0, 0);
-    load_gu(1, 1);
+#pragma unroll
+    for (int f = 0; f < GR - 1 && f < NF; ++f) load_gu(f);
     if (p.dbg) {
 #pragma unroll
       for (int i = 0; i < T::FM; ++i)
@@ -526,17 +533,18 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
             p.dbg[(wrow0 + i * 32 + 8 * (q >> 2) + 4 * g + (q & 3)) * F + wcol0 + j * 32 + r32] = acc[i][j][q];
     }
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int hh = 0; hh < NP; ++hh) {
 #pragma unroll
       for (int ii = 0; ii < FH; ++ii) {
         const int i = hh * FH + ii;
 #pragma unroll
         for (int j = 0; j < T::FN; ++j) {
-          const int b = i & 1;
-          const uint32_t gw[8] = {gs[b][j][0].x, gs[b][j][0].y, gs[b][j][0].z, gs[b][j][0].w,
-                                  gs[b][j][1].x, gs[b][j][1].y, gs[b][j][1].z, gs[b][j][1].w};
-          const uint32_t uw[8] = {us[b][j][0].x, us[b][j][0].y, us[b][j][0].z, us[b][j][0].w,
-                                  us[b][j][1].x, us[b][j][1].y, us[b][j][1].z, us[b][j][1].w};
+          const int f = i * T::FN + j, b = f % GR;
+          if (f + GR - 1 < NF) load_gu(f + GR - 1);
+          const uint32_t gw[8] = {gs[b][0].x, gs[b][0].y, gs[b][0].z, gs[b][0].w,
+                                  gs[b][1].x, gs[b][1].y, gs[b][1].z, gs[b][1].w};
+          const uint32_t uw[8] = {us[b][0].x, us[b][0].y, us[b][0].z, us[b][0].w,
+                                  us[b][1].x, us[b][1].y, us[b][1].z, us[b][1].w};
           uint32_t dgw[8], duw[8];
 #pragma unroll
           for (int t = 0; t < 8; ++t)
@@ -559,16 +567,15 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
               dR[(rl + 8 * (q >> 2) + (q & 3)) * DP + pcl] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
           }
         }
-        if (i + 2 < T::FM) load_gu(i + 2, i & 1);
       }
       __syncthreads();
       // four lanes per 64-column panel row, consecutive rows on consecutive lane quads
       constexpr int CPR = PCB / 16;
-      static_assert((T::TM * CPR) % T::NT == 0 && CPR % 4 == 0, "whole row-pass rounds");
+      static_assert((SR * CPR) % T::NT == 0 && CPR % 4 == 0, "whole row-pass rounds");
 #pragma unroll 2
-      for (int it = 0; it < T::TM * CPR / T::NT; ++it) {
+      for (int it = 0; it < SR * CPR / T::NT; ++it) {
         const int t = it * T::NT + tid;
-        const int r = (t >> 2) % T::TM, c = ((t >> 2) / T::TM) * 4 + (t & 3);
+        const int r = (t >> 2) % SR, c = ((t >> 2) / SR) * 4 + (t & 3);
         const uint4 a = *reinterpret_cast<const uint4*>(dR + r * DP + c * 16);
         const uint4 b = *reinterpret_cast<const uint4*>(dR + r * DP + c * 16 + 8);
         const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
@@ -585,7 +592,7 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
       // dhq_c [2F, mcap] in 64-token panels: a pass's RH consecutive block rows lie in one
       // panel (RH = 64) or half of one (RH = 32); G lanes cover a column's run of them,
       // consecutive columns on consecutive lane groups
-      constexpr int CPC = T::TM / 16;
+      constexpr int CPC = SR / 16;
       constexpr int G = RH >= 64 ? 4 : RH / 16;
       static_assert((PCB * CPC) % T::NT == 0 && RH % 16 == 0 && CPC % G == 0, "whole column-copy rounds");
 #pragma unroll 2
@@ -603,7 +610,7 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
         const int64_t rg = (m0 + brow(hh, gi * 32)) >> 5;
         p.s_c[(pc0 + pc) * p.sc_rs + (rg >> 2) * p.sc_kbs + (rg & 3)] = sT[pc * SG + gi];
       }
-      __syncthreads();  // the staging tiles are rewritten in the second pass
+      __syncthreads();  // the staging tiles are rewritten in the next pass
     }
     return;
   }
@@ -753,10 +760,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
 
 // ------------------------------------------------------------------ host launchers
 
-// Tile configurations (4 wavefronts): 256x256 (wavefront tile 128x128) when N is a multiple
-// of 256 and the rows allow 256-row tiles (M-grouped: pad_multiple 256; the dSwiGLU epilogue's
-// staging needs 256x128), 256x128 otherwise, 128x128 for pad_multiple 128. M-grouped row tiles
-// divide pad_multiple.
+// Tile configurations (4 wavefronts): 256x256 (wavefront tile 128x128) when the rows allow
+// 256-row tiles (M-grouped: pad_multiple 256) and N is a multiple of 256; 256x128 otherwise,
+// 128x128 for pad_multiple 128. M-grouped row tiles divide pad_multiple. dSwiGLU stays on
+// 256x128: with 256 accumulators per wavefront its epilogue has registers for one fragment of
+// g/u lookahead only, and the exposed h13 read latency made it slower than 256x128 (measured).
 template <int BM, int BN, int SCHED, int EPI>
 static hipError_t launch_cfg(const GemmParams& p, hipStream_t st) {
   // 1-D grids: the kernel maps block ids to tiles (see the schedulers)
