@@ -115,6 +115,17 @@ def test_ragged_and_empty_shapes(rows, cols, mode):
     run_and_compare(mx, _f2b(v).reshape(rows, cols), mode)
 
 
+@pytest.mark.parametrize("rows,cols,mode", [(2048, 4096, 3), (1984, 4096, 3), (2048, 4000, 1)])
+def test_macro_tile_order_every_code(rows, cols, mode):
+    """Shapes whose tile grid takes the 8x8 macro-tile block order (rows and column tiles in
+    multiples of 8, macro-tiles in a multiple of 8), with a partial last row band or column
+    tile: every code and scale byte against the oracle."""
+    mx = require_gpu()
+    rng = np.random.default_rng(rows + 3 * cols)
+    v = (rng.standard_normal((rows, cols)) * np.ldexp(1.0, rng.integers(-8, 8, size=(rows, 1)))).astype(np.float32)
+    run_and_compare(mx, _f2b(v).reshape(rows, cols), mode)
+
+
 def test_quant_workload_bit_exact_band_and_samples():
     mx = require_gpu()
     cfg = workloads.QUANT_CONFIG
