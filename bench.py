@@ -121,7 +121,7 @@ def main():
     ap.add_argument("--serial", action="store_true",
                     help="launch with MXF_SERIAL stated explicitly (the default order; profiler runs)")
     ap.add_argument("--quant-only", action="store_true",
-                    help="only measure the standalone quantizer (for a profiler run of that kernel alone)")
+                    help="only measure the standalone quantizer and dequantizer (for a profiler run of those kernels alone)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -147,7 +147,8 @@ def main():
         return
     if args.quant_only:
         mx.lib()
-        print(json.dumps({"quantize": bench_quantize(mx, torch, dev, args)}), flush=True)
+        print(json.dumps({"quantize": bench_quantize(mx, torch, dev, args),
+                          "dequantize": bench_dequantize(mx, torch, dev, args)}), flush=True)
         return
     mx.lib()
     cfg = workloads.MLP_CONFIGS[args.workload]

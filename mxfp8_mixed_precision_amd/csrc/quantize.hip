@@ -296,6 +296,14 @@ __device__ __forceinline__ float code_f32(uint32_t c) {
   else return e4m3_f32(c);
 }
 
+// Two codes (bytes 0-1, or 2-3 with HI) of a word -> their exact fp32 values, by the gfx950
+// hardware conversion of the OCP formats (the same values as code_f32; NaN codes give a NaN).
+template <int FMT, bool HI>
+__device__ __forceinline__ f32x2 code_pk_f32(uint32_t w) {
+  if constexpr (FMT == FMT_E5M2) return __builtin_amdgcn_cvt_pk_f32_bf8((int)w, HI);
+  else return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+}
+
 // E8M0 byte -> 2^(b - 127) as fp32: 0x00 is the subnormal 2^-127 (bits 0x00400000), 0xFF is NaN.
 __device__ __forceinline__ float e8m0_f32(uint32_t b) {
   return __uint_as_float(b == 0xFFu ? 0x7FC00000u : (b == 0u ? 0x00400000u : b << 23));
@@ -314,14 +322,25 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* q, const ui
   if ((cols & 15) == 0) {
     const int64_t cpr = cols >> 4;
     const int64_t total = rows * cpr;
-    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
-      const int64_t r = t / cpr, c16 = t - r * cpr;
-      const uint4 v = *reinterpret_cast<const uint4*>(q + r * cols + c16 * 16);
+    int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= total) return;
+    // (row, 16-code chunk) of t, stepped by the grid stride without a division per step
+    int64_t r = t / cpr, c16 = t - r * cpr;
+    const int64_t sr = stride / cpr, sc16 = stride - sr * cpr;
+    for (; t < total; t += stride) {
+      const uint4 v = load16_nt(q + r * cols + c16 * 16);  // the codes are read once
       const float sc = e8m0_f32(s[r * G + (c16 >> 1)]);
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
       float f[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) f[i] = code_f32<FMT>((w[i >> 2] >> (8 * (i & 3))) & 0xFFu) * sc;
+      for (int k = 0; k < 4; ++k) {
+        // the hardware OCP decode of bytes 0-1 and 2-3 of the word (exact in fp32)
+        const f32x2 lo = code_pk_f32<FMT, false>(w[k]), hi = code_pk_f32<FMT, true>(w[k]);
+        f[4 * k] = lo.x * sc;
+        f[4 * k + 1] = lo.y * sc;
+        f[4 * k + 2] = hi.x * sc;
+        f[4 * k + 3] = hi.y * sc;
+      }
       if (BF16) {
         uint32_t h[8];
 #pragma unroll
@@ -333,6 +352,12 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* q, const ui
         float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + r * cols + c16 * 16);
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = make_float4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]);
+      }
+      r += sr;
+      c16 += sc16;
+      if (c16 >= cpr) {
+        c16 -= cpr;
+        ++r;
       }
     }
   } else {
@@ -558,7 +583,9 @@ hipError_t mxf_launch_dequantize(const void* q, const void* s, int64_t rows, int
                                  void* out, hipStream_t st) {
   const int64_t units = (cols % 16 == 0) ? rows * (cols / 16) : rows * cols;
   if (units == 0) return hipSuccess;
-  const dim3 grid((unsigned)std::min<int64_t>((units + 255) / 256, 8192));
+  // one unit per thread up to 2^24 units; the grid-stride loop covers larger inputs (a grid capped
+  // at 8192 workgroups, each thread looping 3-4 times, measured 15% slower on [16384, 7168])
+  const dim3 grid((unsigned)std::min<int64_t>((units + 255) / 256, 65536));
   const uint8_t* qq = (const uint8_t*)q;
   const uint8_t* ss = (const uint8_t*)s;
   if (bf16 && !e5m2)

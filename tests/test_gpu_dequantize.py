@@ -75,6 +75,36 @@ def test_round_trip_of_the_quantizer_workload():
     assert n == 0, f"{n} mismatches: {ex}"
 
 
+@pytest.mark.parametrize("e5m2", [False, True])
+def test_inputs_past_one_grid_pass(e5m2):
+    """More 16-code units than one launch has threads (2^24): the kernel's grid-stride loop
+    steps (row, chunk) by the stride, wrapping past the row end. 86000 x 7184 codes (449 chunks
+    a row, 2.3 passes); the rows where the second and third passes start, the last rows and
+    random rows are checked in full against the oracle, in BF16 and FP32."""
+    mx = require_gpu()
+    rows, cols = 86000, 7184
+    gen = torch.Generator(device="cuda").manual_seed(11 + e5m2)
+    q = torch.randint(0, 256, (rows, cols), dtype=torch.uint8, device="cuda", generator=gen)
+    s = torch.randint(0, 256, (rows, cols // 32 + 1), dtype=torch.uint8, device="cuda", generator=gen)
+    fmt = "e5m2" if e5m2 else "e4m3"
+    pass_rows = [(k << 24) // (cols // 16) for k in (1, 2)]
+    pick = sorted(set([0, 1] + [r + d for r in pass_rows for d in range(-3, 4)] + list(range(rows - 4, rows))
+                      + np.random.default_rng(5).choice(rows, size=16, replace=False).tolist()))
+    qs, ss = q[pick].cpu().numpy(), s[pick].cpu().numpy()
+    for dtype, sign in ((torch.bfloat16, 0x7FFF), (torch.float32, 0x7FFFFFFF)):
+        out = mx.dequantize(q, s, out_dtype=dtype, e5m2=e5m2)
+        torch.cuda.synchronize()
+        if dtype == torch.bfloat16:
+            got = out[pick].view(torch.uint16).cpu().numpy()
+            want, inf = dequantize_to(qs, ss, "bf16", fmt), 0x7F80
+        else:
+            got = out[pick].cpu().numpy().view(np.uint32)
+            want, inf = dequantize_to(qs, ss, "f32", fmt).view(np.uint32), 0x7F800000
+        del out
+        n, ex = _mismatches(got, want, (got & sign) > inf, (want & sign) > inf)
+        assert n == 0, f"{dtype}: {n} mismatches, e.g. (sampled row, col), got, want: {ex}"
+
+
 def test_empty_is_a_noop():
     mx = require_gpu()
     mx.mxfp8_dequantize(0, 0, 0, 64, mx.DEQ_BF16, 0)
