@@ -376,7 +376,8 @@ def bench_dequantize(mx, torch, dev, args):
     return {"workload": f"E4M3 + E8M0 [{rows}, {cols}] row-wise -> BF16", "value": round(gbs, 1),
             "unit": "GB/s", "avg_us": round(avg_s * 1e6, 2),
             "roofline": {"bound": "hbm", "kernel": "dequantize", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": traffic_for("dequantize", "quant")}}
 
 
 def bench_dispatch(mx, torch, dev, args, quant_x_us):

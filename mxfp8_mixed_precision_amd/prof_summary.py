@@ -19,7 +19,8 @@ reports them while the sources are unchanged).
 
 Kernel dispatches are named by their position in a bench.py step: the MLP step enqueues, in
 order, quant_w13, quant_x, quant_w2, fc1_swiglu, fc2, quant_dy, fc2_wgrad, fc2_dgrad_dswiglu,
-fc1_wgrad, fc1_dgrad; a --quant-only run launches `quantize` only. Profile with
+fc1_wgrad, fc1_dgrad; a --quant-only run launches `quantize` (the dual quantizer) and then
+`dequantize` (row-wise codes to BF16). Profile with
 `bench.py --serial` so that every kernel runs alone (durations not stretched by overlap).
 """
 import argparse
@@ -37,8 +38,10 @@ MLP_SEQUENCE = ["quant_w13", "quant_x", "quant_w2", "fc1_swiglu", "fc2", "quant_
 EXPECT = {
     "quant_w13": "quant_dual_kernel<2,", "quant_w2": "quant_dual_kernel<0,", "quant_x": "quant_dual_kernel<1,",
     "quant_dy": "quant_dual_kernel<1,", "fc1_swiglu": ", 0, 1>", "fc2": ", 0, 0>", "fc2_dgrad_dswiglu": ", 0, 2>",
-    "fc2_wgrad": ", 1, 0>", "fc1_dgrad": ", 0, 0>", "fc1_wgrad": ", 1, 3>", "quantize": "quant_dual_kernel<0,",
+    "fc2_wgrad": ", 1, 0>", "fc1_dgrad": ", 0, 0>", "fc1_wgrad": ", 1, 3>", "quantize": "quant_dual_kernel<0,true,true,0>",
+    "dequantize": "dequant_kernel<true,0>",
 }
+QUANT_ONLY = ["quantize", "dequantize"]
 
 
 def code_only(text):
@@ -105,7 +108,7 @@ def label(dispatches, quant_only):
     dispatches (e.g. a trailing standalone-quantizer measurement) are left out."""
     out = []
     if quant_only:
-        return [(did, "quantize", r) for did, name, r in dispatches if _matches(name, "quantize")]
+        return [(did, k, r) for did, name, r in dispatches for k in QUANT_ONLY if _matches(name, k)]
     i, n = 0, len(MLP_SEQUENCE)
     while i + n <= len(dispatches):
         window = dispatches[i:i + n]
@@ -181,7 +184,7 @@ def main():
           "", "```", cmds, "```", ""] + lines
     md.append("| kernel | launches | avg us | median us | min us | max us | HBM read MB/launch | HBM write MB/launch |")
     md.append("|---|---|---|---|---|---|---|---|")
-    order = ["quantize"] if args.quant_only else MLP_SEQUENCE
+    order = QUANT_ONLY if args.quant_only else MLP_SEQUENCE
     for k in order:
         if k not in dur:
             continue
