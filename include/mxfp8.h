@@ -28,8 +28,15 @@
  * Conventions (torchtitan PR #2, section "Fail-loud contract"):
  *  - Every pointer argument is a DEVICE pointer unless marked "host".
  *  - The caller owns every buffer. The library never allocates or frees device
- *    memory, never synchronises (except mxf_read_status) and keeps no pointer
- *    after a call returns.
+ *    memory, never synchronises (except mxf_read_status and mxf_profile_end)
+ *    and keeps no pointer after a call returns.
+ *  - Library-owned state: besides the thread-local error string, the library
+ *    keeps, per host thread, (a) two helper streams and three events per device,
+ *    created on the first MLP call with MXF_CONCURRENT and kept until the
+ *    process ends, and (b) the timing events of mxf_profile_begin (kept and
+ *    reused until the thread ends), plus a per-device cache of the device's
+ *    architecture and compute-unit count. Without MXF_CONCURRENT and without
+ *    profiling no stream or event is created.
  *  - All arguments are validated on the host before anything is launched. On
  *    failure nothing is launched, a status code is returned and
  *    mxf_last_error() names the offending argument and value. There is no
@@ -53,6 +60,10 @@ extern "C" {
 
 #define MXF_ABI_VERSION 1
 
+/* Status codes. There is no dtype code: every argument's element type is fixed by the entry
+ * point (BF16 inputs, u8 codes and scales, int32 offsets; the output type is chosen by a flag),
+ * and no workspace-size code: workspace and saved sizes are derived from the descriptor by
+ * mxf_mlp_workspace_bytes / mxf_mlp_saved_bytes, not passed in. */
 typedef enum {
   MXF_OK = 0,
   MXF_E_NULL = 1,      /* a required pointer is NULL */
@@ -214,7 +225,8 @@ mxf_status mxf_mlp_tensor(const mxf_mlp_desc* desc /* host */, int which, int* r
  * x [m_capacity, D] BF16; w1, w3 [E, F, D] BF16; w2 [E, D, F] BF16;
  * y [m_capacity, D] BF16 (FP32 with MXF_OUT_F32).
  * saved: mxf_mlp_saved_bytes; keep it unchanged until grouped_mlp_bwd has run.
- * workspace: mxf_mlp_workspace_bytes. All pointers 16-byte aligned. */
+ * workspace: mxf_mlp_workspace_bytes. Tensor pointers 16-byte aligned; offs and counts
+ * 4-byte aligned. */
 mxf_status grouped_mlp_fwd(const mxf_mlp_desc* desc /* host */, const int32_t* offs,
                            const int32_t* counts, const void* x, const void* w1, const void* w3,
                            const void* w2, void* y, void* saved, void* workspace, void* stream);

@@ -64,6 +64,15 @@ mxf_status check_device() {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// The token offsets and counts are int32 arrays read by every kernel of an MLP call.
+mxf_status check_offs_ptrs(const int32_t* offs, const int32_t* counts) {
+  if (!offs) return fail(MXF_E_NULL, "offs is NULL");
+  if (!aligned4(offs)) return fail(MXF_E_ALIGN, "offs is not 4-byte aligned");
+  if (counts && !aligned4(counts)) return fail(MXF_E_ALIGN, "counts is not 4-byte aligned");
+  return MXF_OK;
+}
 
 // ------------------------------------------------------------------ kernel timing
 
@@ -330,7 +339,7 @@ mxf_status grouped_mlp_fwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   const void* ptrs[] = {w1, w3, w2, y, saved, workspace, x};
   const char* names[] = {"w1", "w3", "w2", "y", "saved", "workspace", "x"};
   if ((s = check_mlp_ptrs(ptrs, names, xq ? 6 : 7)) != MXF_OK) return s;
-  if (!offs) return fail(MXF_E_NULL, "offs is NULL");
+  if ((s = check_offs_ptrs(offs, counts)) != MXF_OK) return s;
   if ((s = check_device()) != MXF_OK) return s;
 
   Layout L;
@@ -419,7 +428,7 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   const void* ptrs[] = {dy, saved, dx, dw1, dw3, dw2, workspace};
   const char* names[] = {"dy", "saved", "dx", "dw1", "dw3", "dw2", "workspace"};
   if ((s = check_mlp_ptrs(ptrs, names, 7)) != MXF_OK) return s;
-  if (!offs) return fail(MXF_E_NULL, "offs is NULL");
+  if ((s = check_offs_ptrs(offs, counts)) != MXF_OK) return s;
   if ((s = check_device()) != MXF_OK) return s;
 
   Layout L;
@@ -527,8 +536,6 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
 
 // ------------------------------------------------------------------ dispatch
 
-static bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
-
 static mxf_status check_plan_sizes(int64_t tokens, int32_t topk, int32_t E) {
   if (tokens < 0) return fail(MXF_E_SHAPE, "tokens = %lld: negative", (long long)tokens);
   if (topk < 1 || topk > 64) return fail(MXF_E_SHAPE, "topk = %d: must be in [1, 64]", topk);
@@ -612,6 +619,7 @@ mxf_status mxfp8_dispatch_quantize(const mxf_mlp_desc* desc, const int32_t* offs
   mxf_status s = check_desc(desc);
   if (s != MXF_OK) return s;
   if ((s = check_dispatch(x_tokens, tokens, topk, offs, row_assign, desc->m_capacity)) != MXF_OK) return s;
+  if ((s = check_offs_ptrs(offs, counts)) != MXF_OK) return s;
   const void* ptrs[] = {saved, workspace};
   const char* names[] = {"saved", "workspace"};
   if ((s = check_mlp_ptrs(ptrs, names, 2)) != MXF_OK) return s;

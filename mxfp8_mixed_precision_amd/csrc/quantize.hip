@@ -226,7 +226,9 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
     const int64_t ng = (p.cols - col0) >> 5;  // valid groups in the block (>= 1)
     uint8_t* dst = p.s_r + e * p.sr_bs + r * p.sr_rs + (g0 >> 2) * p.sr_kbs;
     if (r < p.rows) {
-      if (ng >= 4 && (p.sr_rs & 3) == 0 && (p.sr_kbs & 3) == 0) {
+      // one word store only where the four bytes are a naturally aligned word (the scale
+      // array's base may sit at any byte)
+      if (ng >= 4 && ((uintptr_t)dst & 3) == 0 && (p.sr_rs & 3) == 0 && (p.sr_kbs & 3) == 0) {
         *reinterpret_cast<uint32_t*>(dst) = srow[tid];
       } else {
         for (int g = 0; g < 4 && g < ng; ++g) dst[g] = srow_b[tid * 4 + g];
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
       const int64_t g0 = row0 >> 5;
       const int64_t ng = (p.rows - row0) >> 5;
       uint8_t* dst = p.s_c + e * p.sc_bs + (col0 + tid) * p.sc_rs + (g0 >> 2) * p.sc_kbs;
-      if (ng >= 4 && (p.sc_rs & 3) == 0 && (p.sc_kbs & 3) == 0) {
+      if (ng >= 4 && ((uintptr_t)dst & 3) == 0 && (p.sc_rs & 3) == 0 && (p.sc_kbs & 3) == 0) {
         *reinterpret_cast<uint32_t*>(dst) = scol[tid];
       } else {
         for (int g = 0; g < 4 && g < ng; ++g) dst[g] = scol_b[tid * 4 + g];

@@ -121,7 +121,16 @@ def real_rows_mask(offs, counts, m):
 
 
 def check_offsets(offs, counts, pad_multiple, m_capacity):
-    """True when offs/counts satisfy the layout contract of the padded expert-major layout."""
+    """True when offs/counts describe a padded expert-major layout.
+
+    torchtitan PR #12, section "What it adds": every expert's token segment is
+    hard-aligned to pad_multiple. Written out: offs[0] = 0; offs never
+    decreases (a zero-token expert has an empty segment); every offs[e] is a
+    multiple of pad_multiple; the layout fits the allocation (offs[E] <=
+    m_capacity); and counts[e], when given, lies in [0, offs[e+1] - offs[e]]
+    (the real rows precede the pad rows of the segment). Both arrays are read
+    as signed integers.
+    """
     offs = np.asarray(offs, dtype=np.int64)
     if offs[0] != 0 or np.any(np.diff(offs) < 0) or offs[-1] > m_capacity:
         return False

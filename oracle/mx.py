@@ -190,12 +190,3 @@ def dequantize_to(q, s, dtype, fmt="e4m3"):
     with np.errstate(over="ignore", invalid="ignore"):
         return v.astype(np.float32)
 
-
-def quantize_bf16_rowwise(bits, fmt="e4m3"):
-    """Row-wise MXFP8 of a BF16 matrix given as uint16 bit patterns."""
-    return quantize_rowwise(bf16_bits_to_f64(bits), fmt)
-
-
-def quantize_bf16_colwise(bits, fmt="e4m3"):
-    """Column-wise MXFP8 of a BF16 matrix given as uint16 bit patterns."""
-    return quantize_colwise(bf16_bits_to_f64(bits), fmt)

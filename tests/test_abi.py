@@ -110,6 +110,23 @@ def test_mlp_pointer_rejections():
     assert ei.value.status == _abi.E_NULL and "dw1" in str(ei.value)
 
 
+def test_offsets_alignment_rejections():
+    """offs and counts are int32 arrays: a pointer that is not 4-byte aligned is rejected
+    before anything is launched, by the forward, the backward and the fused dispatch."""
+    d = _desc()
+    good = 1 << 20
+    for offs, counts, name in ((good + 2, None, "offs"), (good, good + 1, "counts")):
+        with pytest.raises(mx.MxfError) as ei:
+            mx.grouped_mlp_fwd(d, offs, counts, good, good, good, good, good, good, good, stream=0)
+        assert ei.value.status == _abi.E_ALIGN and name in str(ei.value)
+        with pytest.raises(mx.MxfError) as ei:
+            mx.grouped_mlp_bwd(d, offs, counts, good, good, good, good, good, good, good, stream=0)
+        assert ei.value.status == _abi.E_ALIGN and name in str(ei.value)
+        with pytest.raises(mx.MxfError) as ei:
+            mx.mxfp8_dispatch_quantize(d, offs, counts, good, good, 8, 2, good, good, stream=0)
+        assert ei.value.status == _abi.E_ALIGN and name in str(ei.value)
+
+
 @pytest.mark.parametrize("rows,cols,mode,code", [
     (64, 48, mx.ROW, _abi.E_SHAPE), (48, 64, mx.COL, _abi.E_SHAPE), (-1, 64, mx.ROW, _abi.E_SHAPE),
     (64, 64, 0, _abi.E_ARG), (64, 64, 4, _abi.E_ARG),

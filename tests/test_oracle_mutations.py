@@ -131,3 +131,21 @@ def test_e5m2_mutations_are_caught(monkeypatch):
     sb = mx.scale_byte
     monkeypatch.setattr(mx, "scale_byte", lambda a, emax=8: sb(a, 14 if emax == 15 else emax))   # E4M3-like emax slip
     assert _fails(te.test_closed_forms, 0)
+
+
+def test_offsets_check_mutations_are_caught(monkeypatch):
+    import test_oracle_offsets as to
+    good = mlp.check_offsets
+    muts = [
+        lambda o, c, p, m: good([x - x % p for x in o], c, p, m),                 # alignment ignored
+        lambda o, c, p, m: good(o, None, p, m),                                   # counts ignored
+        lambda o, c, p, m: good(o, c, p, m + p),                                  # capacity off by a segment
+        lambda o, c, p, m: good(sorted(o), c, p, m),                              # order ignored
+    ]
+    cases = [(2, 2, 6, range(-2, 9), range(-1, 6))]
+    for mut in muts:
+        monkeypatch.setattr(to, "check_offsets", mut)
+        caught = any(_fails(to.test_hand_cases, *h) for h in to.HAND) or \
+            any(_fails(to.test_accepts_exactly_the_constructed_layouts, *c) for c in cases)
+        assert caught
+    monkeypatch.undo()
