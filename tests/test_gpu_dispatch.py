@@ -168,7 +168,10 @@ def _dispatch_quant(mx, name=None, case=None):
 
 
 DQ_CASES = [("tiny", None), ("rand_D512", dict(seed=21, tokens=700, topk=4, E=8, D=512, pad=256, zero=(1, 6))),
-            ("rand_D384", dict(seed=22, tokens=96, topk=2, E=3, D=384, pad=128, zero=()))]
+            ("rand_D384", dict(seed=22, tokens=96, topk=2, E=3, D=384, pad=128, zero=())),
+            # E >= 64: the kernels' looping offsets check and binary-search expert lookup
+            ("E64", dict(seed=23, tokens=1500, topk=4, E=64, D=256, pad=128, zero=(0, 17, 63))),
+            ("E96_pad256", dict(seed=24, tokens=2000, topk=3, E=96, D=256, pad=256, zero=(5, 95)))]
 
 
 @pytest.mark.parametrize("name,case", DQ_CASES, ids=[c[0] for c in DQ_CASES])

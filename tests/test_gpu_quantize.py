@@ -171,3 +171,35 @@ def test_deterministic_and_stream_ordered():
     s.synchronize()
     for t1, t2 in zip(r1, r2):
         assert torch.equal(t1, t2)
+
+
+@pytest.mark.parametrize("offset", [1, 2, 3])
+def test_scale_arrays_at_any_byte_offset(offset):
+    """mxfp8_quantize documents its scale arrays as any alignment: with s_row and s_col starting
+    `offset` bytes past an aligned address (where whole-word scale stores would be misaligned)
+    the codes and scales still equal the oracle's, and the bytes around the arrays are
+    untouched."""
+    mx = require_gpu()
+    rows, cols = 256, 512
+    g = torch.Generator(device="cpu")
+    g.manual_seed(offset)
+    x = torch.randn((rows, cols), generator=g).to(torch.bfloat16)
+    xd = x.cuda()
+    q_r = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+    q_c = torch.empty((cols, rows), dtype=torch.uint8, device="cuda")
+    nsr, nsc = rows * cols // 32, cols * rows // 32
+    sr_buf = torch.full((nsr + 16,), 0xA5, dtype=torch.uint8, device="cuda")
+    sc_buf = torch.full((nsc + 16,), 0x5A, dtype=torch.uint8, device="cuda")
+    s_r = sr_buf[offset:offset + nsr]
+    s_c = sc_buf[offset:offset + nsc]
+    print(f"\nscale arrays at byte offset {offset}", flush=True)
+    mx.mxfp8_quantize(xd, rows, cols, 3, q_r, s_r, q_c, s_c)
+    torch.cuda.synchronize()
+    v = bf16_bits_to_f64(bits(x))
+    rq, rs = quantize_rowwise(v)
+    cq, cs = quantize_colwise(v)
+    assert np.array_equal(np_u8(q_r), rq) and np.array_equal(np_u8(s_r).reshape(rows, cols // 32), rs)
+    assert np.array_equal(np_u8(q_c), cq) and np.array_equal(np_u8(s_c).reshape(cols, rows // 32), cs)
+    srb, scb = np_u8(sr_buf), np_u8(sc_buf)
+    assert np.all(srb[:offset] == 0xA5) and np.all(srb[offset + nsr:] == 0xA5)
+    assert np.all(scb[:offset] == 0x5A) and np.all(scb[offset + nsc:] == 0x5A)
