@@ -271,6 +271,23 @@ mxf_status mxf_route_plan(const int32_t* expert_idx, int64_t tokens, int32_t top
                           int32_t* row_assign, int32_t* assign_row, int32_t* status, void* workspace,
                           void* stream);
 
+/* Allocation-free variant of mxf_route_plan, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same plan, with the same arguments and outputs minus `workspace`. Its per-workgroup
+ * histograms live in a static device array of MXF_ROUTE_NOALLOC_MAX_BYTES that the library
+ * holds on each GPU it runs on until the process ends (the address is looked up on the first
+ * call per device). The call allocates nothing. Limit: mxf_route_plan_workspace_bytes(tokens,
+ * topk, E) <= MXF_ROUTE_NOALLOC_MAX_BYTES (e.g. E = 16: up to 120M assignments; E = 1024: up to
+ * 2M), else MXF_E_SHAPE before any launch. Every call on one GPU shares that array: calls that
+ * overlap on one GPU (other streams, other host threads) race and give undefined results;
+ * calls ordered on one stream are safe (the array's contents on entry do not matter).
+ * Errors: as mxf_route_plan. */
+#define MXF_ROUTE_NOALLOC_MAX_BYTES (8u << 20)
+mxf_status mxf_route_plan_noalloc(const int32_t* expert_idx, int64_t tokens, int32_t topk, int32_t E,
+                                  int32_t pad_multiple, int64_t m_capacity, int32_t* offs,
+                                  int32_t* counts, int32_t* row_assign, int32_t* assign_row,
+                                  int32_t* status, void* stream);
+
 /* BF16 permute: x_out [m_capacity, D] row r (r < min(offs[E], m_capacity)) = x_tokens
  * [tokens, D] row row_assign[r] / topk, or zeros where row_assign[r] is -1 (or outside
  * [0, tokens * topk)). Rows at or past offs[E] are not written. offs and row_assign as

@@ -34,7 +34,8 @@ T = {name: i for i, name in enumerate(TENSORS)}
 EXPORTS = ["mxf_abi_version", "mxf_query_device", "mxf_last_error", "mxfp8_quantize", "mxfp8_dequantize",
            "mxf_mlp_saved_bytes", "mxf_mlp_workspace_bytes", "mxf_mlp_tensor", "grouped_mlp_fwd",
            "grouped_mlp_bwd", "mxf_read_status", "mxf_profile_begin", "mxf_profile_end",
-           "mxf_pack_w13", "mxf_unpack_w13", "mxf_route_plan_workspace_bytes", "mxf_route_plan", "mxf_dispatch_permute",
+           "mxf_pack_w13", "mxf_unpack_w13", "mxf_route_plan_workspace_bytes", "mxf_route_plan", "mxf_route_plan_noalloc",
+           "mxf_dispatch_permute",
            "mxfp8_dispatch_quantize"]
 
 
@@ -86,6 +87,7 @@ def lib():
             "mxf_unpack_w13": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp]),
             "mxf_route_plan_workspace_bytes": (sz, [i64, i32, i32]),
             "mxf_route_plan": (ctypes.c_int, [vp, i64, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, vp]),
+            "mxf_route_plan_noalloc": (ctypes.c_int, [vp, i64, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp]),
             "mxf_dispatch_permute": (ctypes.c_int, [vp, i64, i32, i64, i32, vp, vp, i64, vp, vp]),
             "mxfp8_dispatch_quantize": (ctypes.c_int, [pdesc, vp, vp, vp, vp, i64, i32, vp, vp, vp]),
         }
@@ -226,6 +228,17 @@ def mxf_route_plan(expert_idx, tokens, topk, E, pad_multiple, m_capacity, offs, 
     _check(lib().mxf_route_plan(_ptr(expert_idx), tokens, topk, E, pad_multiple, m_capacity, _ptr(offs),
                                 _ptr(counts), _ptr(row_assign), _ptr(assign_row), _ptr(status), _ptr(workspace),
                                 _stream(stream)))
+
+
+ROUTE_NOALLOC_MAX_BYTES = 8 << 20
+
+
+def mxf_route_plan_noalloc(expert_idx, tokens, topk, E, pad_multiple, m_capacity, offs, counts, row_assign,
+                           assign_row, status, stream=None):
+    """Raw call of the allocation-free routing plan (no workspace argument)."""
+    _check(lib().mxf_route_plan_noalloc(_ptr(expert_idx), tokens, topk, E, pad_multiple, m_capacity, _ptr(offs),
+                                        _ptr(counts), _ptr(row_assign), _ptr(assign_row), _ptr(status),
+                                        _stream(stream)))
 
 
 def route_plan(expert_idx, E, pad_multiple, m_capacity, stream=None):

@@ -550,10 +550,13 @@ size_t mxf_route_plan_workspace_bytes(int64_t tokens, int32_t topk, int32_t E) {
   return mxf_route_plan_workspace_bytes(tokens * topk, E);
 }
 
-mxf_status mxf_route_plan(const int32_t* expert_idx, int64_t tokens, int32_t topk, int32_t E, int32_t pad_multiple,
-                          int64_t m_capacity, int32_t* offs, int32_t* counts, int32_t* row_assign,
-                          int32_t* assign_row, int32_t* status, void* workspace, void* stream) {
-  g_err.clear();
+// Host-side checks shared by the two routing-plan entry points (workspace: the caller's buffer,
+// or the library's static scratch for the allocation-free variant, which passes a non-null
+// placeholder here and checks the size itself).
+static mxf_status check_route_plan(const int32_t* expert_idx, int64_t tokens, int32_t topk, int32_t E,
+                                   int32_t pad_multiple, int64_t m_capacity, const int32_t* offs,
+                                   const int32_t* counts, const int32_t* row_assign, const int32_t* assign_row,
+                                   const int32_t* status, const void* workspace) {
   mxf_status s = check_plan_sizes(tokens, topk, E);
   if (s != MXF_OK) return s;
   if (pad_multiple < 1 || pad_multiple > 4096)
@@ -569,10 +572,46 @@ mxf_status mxf_route_plan(const int32_t* expert_idx, int64_t tokens, int32_t top
   const char* an[] = {"expert_idx", "offs", "counts", "row_assign", "assign_row", "status", "workspace"};
   for (int i = 0; i < 7; ++i)
     if (!aligned4(al[i])) return fail(MXF_E_ALIGN, "%s is not 4-byte aligned", an[i]);
+  return MXF_OK;
+}
+
+mxf_status mxf_route_plan(const int32_t* expert_idx, int64_t tokens, int32_t topk, int32_t E, int32_t pad_multiple,
+                          int64_t m_capacity, int32_t* offs, int32_t* counts, int32_t* row_assign,
+                          int32_t* assign_row, int32_t* status, void* workspace, void* stream) {
+  g_err.clear();
+  mxf_status s = check_route_plan(expert_idx, tokens, topk, E, pad_multiple, m_capacity, offs, counts, row_assign,
+                                  assign_row, status, workspace);
+  if (s != MXF_OK) return s;
   if ((s = check_device()) != MXF_OK) return s;
   MXF_HIP(timed("route_plan", (hipStream_t)stream, [&] {
-            return mxf_launch_route_plan(expert_idx, (int32_t)n, E, pad_multiple, m_capacity, offs, counts,
-                                         row_assign, assign_row, status, workspace, (hipStream_t)stream);
+            return mxf_launch_route_plan(expert_idx, (int32_t)(tokens * topk), E, pad_multiple, m_capacity, offs,
+                                         counts, row_assign, assign_row, status, workspace, (hipStream_t)stream);
+          }), "route plan launch");
+  return MXF_OK;
+}
+
+mxf_status mxf_route_plan_noalloc(const int32_t* expert_idx, int64_t tokens, int32_t topk, int32_t E,
+                                  int32_t pad_multiple, int64_t m_capacity, int32_t* offs, int32_t* counts,
+                                  int32_t* row_assign, int32_t* assign_row, int32_t* status, void* stream) {
+  g_err.clear();
+  static const int32_t placeholder = 0;  // stands for the scratch array in the shared host checks
+  mxf_status s = check_route_plan(expert_idx, tokens, topk, E, pad_multiple, m_capacity, offs, counts, row_assign,
+                                  assign_row, status, &placeholder);
+  if (s != MXF_OK) return s;
+  const size_t need = mxf_route_plan_workspace_bytes(tokens * topk, E);
+  if (need > (size_t)MXF_ROUTE_NOALLOC_MAX_BYTES)
+    return fail(MXF_E_SHAPE,
+                "tokens * topk = %lld with E = %d needs %zu bytes of plan scratch; the allocation-free plan holds "
+                "at most %zu (use mxf_route_plan with a workspace)",
+                (long long)(tokens * topk), E, need, (size_t)MXF_ROUTE_NOALLOC_MAX_BYTES);
+  if ((s = check_device()) != MXF_OK) return s;
+  void* ws = nullptr;
+  size_t cap = 0;
+  MXF_HIP(mxf_route_scratch(&ws, &cap), "route plan scratch lookup");
+  if (need > cap) return fail(MXF_E_SHAPE, "plan scratch of %zu bytes exceeds the static %zu", need, cap);
+  MXF_HIP(timed("route_plan", (hipStream_t)stream, [&] {
+            return mxf_launch_route_plan(expert_idx, (int32_t)(tokens * topk), E, pad_multiple, m_capacity, offs,
+                                         counts, row_assign, assign_row, status, ws, (hipStream_t)stream);
           }), "route plan launch");
   return MXF_OK;
 }

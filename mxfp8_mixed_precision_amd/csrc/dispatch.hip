@@ -25,7 +25,17 @@
 //    loads and stores) or writes zeros for a pad row.
 // The fused gather + dual quantization (no BF16 copy) is a kind of the quantizer
 // (quantize.hip).
+#include <mutex>
+
 #include "kernels.h"
+#include "mxfp8.h"
+
+// Per-workgroup histograms of the allocation-free routing plan (mxf_route_plan_noalloc): a
+// file-scope device array instead of a caller workspace. Each GPU the library runs on holds
+// its own copy until the process ends. Host code never passes this name to a kernel (on the
+// host it is only a stand-in symbol): it looks the device address up once per device with
+// hipGetSymbolAddress and uses that.
+static __device__ __align__(256) int32_t scratch[MXF_ROUTE_NOALLOC_MAX_BYTES / sizeof(int32_t)];
 
 namespace mxf {
 
@@ -247,4 +257,29 @@ hipError_t mxf_launch_permute(const void* x, int64_t n_assign, int topk, int64_t
   hipLaunchKernelGGL(mxf::permute_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (const uint16_t*)x, n_assign,
                      topk, D, offs, E, row_assign, mcap, (uint16_t*)out);
   return hipGetLastError();
+}
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];  // device address of `scratch`, per device ordinal
+}  // namespace
+
+// Device address and size of the routing plan's static scratch array on the current device,
+// looked up on the first call per device (with that device current) and cached.
+hipError_t mxf_route_scratch(void** ptr, size_t* bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  *bytes = sizeof(scratch);
+  return hipSuccess;
 }

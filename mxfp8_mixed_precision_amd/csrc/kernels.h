@@ -68,6 +68,7 @@ hipError_t mxf_launch_pack13(const void* w1, const void* w3, void* w13, int64_t 
                              int64_t D, bool pack, hipStream_t st);
 // dispatch.hip
 size_t mxf_route_plan_workspace_bytes(int64_t n, int E);
+hipError_t mxf_route_scratch(void** ptr, size_t* bytes);
 hipError_t mxf_launch_route_plan(const int32_t* idx, int32_t n, int E, int pad, int64_t mcap, int32_t* offs,
                                  int32_t* counts, int32_t* row_assign, int32_t* assign_row, int32_t* status,
                                  void* workspace, hipStream_t st);
