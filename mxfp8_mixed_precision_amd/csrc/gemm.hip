@@ -23,7 +23,9 @@
 // K advances in 64-k stages through a ring of four LDS stages filled by direct global->LDS
 // loads (one 1 KB load per 16 rows; three stages in flight while one is consumed); the
 // fragments of the next stage are read into a second register set while the matrix
-// instructions of the current one run. LDS rows are 64 bytes; the 16-byte chunk index is
+// instructions of the current one run. The dSwiGLU GEMM instead runs two blocks per CU (a
+// three-stage ring in 80 KB, fragments read at the start of each stage, at most 256 registers),
+// so that each block's long epilogue runs beside the other block's matrix instructions. LDS rows are 64 bytes; the 16-byte chunk index is
 // XOR-swizzled with (row / 4) % 4 so that a 16-lane phase of ds_read_b128 over 16
 // consecutive rows hits 16 distinct bank groups.
 //
@@ -52,10 +54,14 @@ enum GemmEpi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2, EPI_UNPACK13 = 3 
 
 
 
-template <int BM, int BN, int WM, int WN>
+// OCC = blocks resident per CU. OCC 1: a four-stage ring in up to 160 KB of LDS, fragments
+// double-buffered in registers. OCC 2: a three-stage ring in at most 80 KB and at most 256
+// registers per lane, so a second block shares every SIMD and its matrix instructions run while
+// this block waits on loads or works through its epilogue.
+template <int BM, int BN, int WM, int WN, int OCC = 1>
 struct Tile {
   static constexpr int BK = 64;   // K per pipeline stage (one MFMA K step)
-  static constexpr int S = 4;     // stages in the LDS ring
+  static constexpr int S = OCC == 2 ? 3 : 4;  // stages in the LDS ring
   static constexpr int NT = WM * WN * 64;
   static constexpr int NW = WM * WN;
   static constexpr int TM = BM / WM;
@@ -72,7 +78,7 @@ struct Tile {
   static constexpr int NSC = 3;
   static constexpr int SC_OFF = S * STAGE;
   static constexpr int SC_SLOT = 2 * NW * 256;
-  static constexpr int LDS_BYTES = 160 * 1024;
+  static constexpr int LDS_BYTES = 160 * 1024 / OCC;
   static constexpr int IA = BM / 16 / NW;  // 1 KB direct-to-LDS loads (16 rows) of A, per wavefront
   static constexpr int IB = BN / 16 / NW;
   static constexpr int LO = IA + IB;       // loads per wavefront for an odd stage
@@ -82,8 +88,9 @@ struct Tile {
   static constexpr int EPI_ST = BM * (BN + 8) * 2;
   static constexpr int EPI_SW = BM * (BN / 2 + 8) * 2 + (BN / 2) * (BM + 8) + (BN / 2) * (BM / 32);
   // dSwiGLU passes: a wavefront's fragment rows in two halves (dSwiGLU runs on 64-column
-  // wavefront tiles, FN <= 2)
-  static constexpr int DSW_NP = 2;
+  // wavefront tiles, FN <= 2); under OCC 2 one fragment row per pass (the staging then fits
+  // the smaller LDS share)
+  static constexpr int DSW_NP = (OCC == 2 && FM >= 2) ? FM : 2;
   static constexpr int DSW_SR = WM * (TM / DSW_NP);  // staged rows per pass
   static constexpr int EPI_DSW = DSW_SR * (2 * BN + 8) * 2 + 2 * BN * (DSW_SR + 8) + 2 * BN * (DSW_SR / 32);
   static constexpr int LDS_MAIN = S * STAGE + NSC * SC_SLOT;
@@ -96,7 +103,8 @@ struct Tile {
   static_assert(BM <= 64 * NW && BN <= 64 * NW, "one scale-word load per wavefront and operand");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 fragments");
   static_assert(LDS_MAIN <= LDS_BYTES, "pipeline does not fit in LDS");
-  static_assert(S % 2 == 0 && (S / 2) * (L + LO) <= 63, "loads in flight exceed the vmcnt range");
+  static_assert(OCC == 2 ? (S == 3 && L + LO <= 63) : (S % 2 == 0 && (S / 2) * (L + LO) <= 63),
+                "loads in flight exceed the vmcnt range");
 };
 
 // LDS tile layout: 64-byte rows, 16-byte chunk c of row r stored at chunk c ^ ((r / 4) % 4). A
@@ -133,10 +141,10 @@ __device__ __forceinline__ void g2lds4(const void* sbase, uint32_t voff, uint32_
 
 // One output tile (rows [m0, m0 + BM), columns [n0, n0 + BN), contraction over [kbeg, kend)):
 // the pipelined main loop and the epilogue. smem holds Tile<BM, BN, WM, WN>::lds(EPI) bytes.
-template <int BM, int BN, int WM, int WN, int SCHED, int EPI>
+template <int BM, int BN, int WM, int WN, int SCHED, int EPI, int OCC>
 __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int e, int64_t m0, int64_t n0,
                                          int64_t kbeg, int64_t kend) {
-  using T = Tile<BM, BN, WM, WN>;
+  using T = Tile<BM, BN, WM, WN, OCC>;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
@@ -206,6 +214,74 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
     }
   };
 
+  constexpr int NMF = T::FM * T::FN;  // MFMAs per stage
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  if constexpr (OCC == 2) {
+    // Three-slot ring, one register set. Step kt: wait until stage kt has landed (stage kt+1's
+    // loads may still be in flight), pass the block barrier (every wavefront has consumed stage
+    // kt-1, whose slot is (kt+2) % 3), issue stage kt+2 into that slot, read stage kt's
+    // fragments and run its matrix instructions. The LDS read latency and the load waits are
+    // covered by the other block on the same SIMDs. Past the end a surplus copy of the last
+    // stage is loaded, so every step's loads and waits are the same.
+    v8i fa[T::FM], fb[T::FN];
+    uint32_t sa[T::FM], sb[T::FN];
+    auto read_stage = [&](int kt, auto par) {
+      constexpr int B = decltype(par)::value;  // kt % 2: which 32-k groups of the scale word
+      const uint8_t* base = smem + (kt % T::S) * T::STAGE;
+      const uint8_t* sbase = smem + T::SC_OFF + ((kt >> 1) % T::NSC) * T::SC_SLOT;
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i) sa[i] = sbase[(tr0 + i * 32 + r32) * 4 + 2 * B + g];
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) sb[j] = sbase[T::NW * 256 + (tc0 + j * 32 + r32) * 4 + 2 * B + g];
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi) {
+          const uint4 v = *reinterpret_cast<const uint4*>(base + T::B_OFF + swz(tc0 + j * 32 + r32, 2 * hi + g));
+          fb[j][4 * hi] = (int)v.x; fb[j][4 * hi + 1] = (int)v.y;
+          fb[j][4 * hi + 2] = (int)v.z; fb[j][4 * hi + 3] = (int)v.w;
+        }
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi) {
+          const uint4 v = *reinterpret_cast<const uint4*>(base + T::A_OFF + swz(tr0 + i * 32 + r32, 2 * hi + g));
+          fa[i][4 * hi] = (int)v.x; fa[i][4 * hi + 1] = (int)v.y;
+          fa[i][4 * hi + 2] = (int)v.z; fa[i][4 * hi + 3] = (int)v.w;
+        }
+    };
+    if (KT > 0) {  // stages 0 and 1 (KT is even, so stage 1 exists)
+#pragma unroll
+      for (int q = 0; q < T::L; ++q) issue_one(q, 0, 0);
+#pragma unroll
+      for (int q = 0; q < T::LO; ++q) issue_one(q, 1, 1);
+    }
+    auto step2 = [&](int kt, auto par) {
+      constexpr int P = decltype(par)::value;
+      wait_vmcnt<P ? T::L : T::LO>();  // stage kt landed; stage kt+1 (odd: LO loads) may be in flight
+      __syncthreads();
+      const int ks = kt + 2 < KT ? kt + 2 : KT - 1;
+#pragma unroll
+      for (int q = 0; q < (P ? T::LO : T::L); ++q) issue_one(q, ks, kt + 2);  // stage kt+2 has parity P
+      read_stage(kt, par);
+#pragma unroll
+      for (int m = 0; m < NMF; ++m) {
+        const int i = m / T::FN, j = m % T::FN;
+        if constexpr (TRACC)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 0, (int)sb[j], 0,
+                                                                      (int)sa[i]);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, (int)sa[i], 0,
+                                                                      (int)sb[j]);
+      }
+    };
+    for (int kt = 0; kt < KT; kt += 2) {
+      step2(kt, I0());
+      step2(kt + 1, I1());
+    }
+    if (KT > 0) wait_vmcnt<0>();  // no load may still target LDS when the epilogue reuses it
+  } else {
   // Fragments of one stage in registers: A/B operands and this lane's two E8M0 scale bytes
   // (its 32-k group of the stage: byte 2 * (kt % 2) + g of the row's scale word, read alone so
   // that the matrix instruction takes it with op_sel 0).
@@ -248,9 +324,6 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
   // stage (past the end: a surplus copy of the last stage), so the waits are the same
   // everywhere; steps are instantiated with compile-time flags so that each interleaved
   // sequence is one basic block.
-  constexpr int NMF = T::FM * T::FN;  // MFMAs per stage
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
   if (KT > 0) {
 #pragma unroll
     for (int st = 0; st < T::S; ++st) {
@@ -305,6 +378,7 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
   }
   if (KT > 0) {
     wait_vmcnt<0>();  // no load may still target LDS when the epilogue reuses it
+  }
   }
 
   // ------------------------------------------------------------------ epilogues
@@ -510,7 +584,7 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
     // (f = i FN + j): fragment f + GR - 1 is requested when fragment f is taken up
     constexpr int NF = T::FM * T::FN;
     static_assert(EPI != EPI_DSWIGLU || T::FN <= 2, "dSwiGLU runs on 64-column wavefront tiles");
-    constexpr int GR = 4;
+    constexpr int GR = OCC == 2 ? 3 : 4;
     uint4 gs[GR][2], us[GR][2];
     auto load_gu = [&](int f) {
       const int i = f / T::FN, j = f % T::FN, slot = f % GR;
@@ -629,14 +703,15 @@ struct TailCfg {
   static constexpr int BM4 = BM / 2, BN4 = BN / 2;      // Q = 4
 };
 
-template <int BM, int BN, int WM, int WN, int SCHED, int EPI>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
-  using T = Tile<BM, BN, WM, WN>;
+template <int BM, int BN, int WM, int WN, int SCHED, int EPI, int OCC>
+__global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_mx_kernel(GemmParams p) {
+  using T = Tile<BM, BN, WM, WN, OCC>;
   using TC = TailCfg<BM, BN>;
   constexpr bool SPLIT = SCHED == SCHED_MGROUP && TC::Q2;
-  constexpr int LDSZ = SPLIT ? T::imax(T::lds(EPI), T::imax(Tile<TC::BM2, TC::BN2, WM, WN>::lds(EPI),
-                                                           Tile<TC::BM4, TC::BN4, WM, WN>::lds(EPI)))
+  constexpr int LDSZ = SPLIT ? T::imax(T::lds(EPI), T::imax(Tile<TC::BM2, TC::BN2, WM, WN, OCC>::lds(EPI),
+                                                           Tile<TC::BM4, TC::BN4, WM, WN, OCC>::lds(EPI)))
                              : T::lds(EPI);
+  static_assert(LDSZ <= T::LDS_BYTES, "LDS of the kernel exceeds its share of the CU");
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDSZ];
 
   const int tid = threadIdx.x;
@@ -658,9 +733,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
     int64_t nfull = ntiles, rem = 0;
     int q = 1;
     if (SPLIT) {
-      rem = ntiles % p.ncu;
-      if (rem && TC::Q4 && 4 * rem <= p.ncu) q = 4;
-      else if (rem && 2 * rem <= p.ncu) q = 2;
+      const int64_t slots = (int64_t)p.ncu * OCC;  // blocks resident at once
+      rem = ntiles % slots;
+      if (rem && TC::Q4 && 4 * rem <= slots) q = 4;
+      else if (rem && 2 * rem <= slots) q = 2;
       if (q > 1) nfull = ntiles - rem;
       else rem = 0;
     }
@@ -695,7 +771,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
           m0 += (part >> 1) * TC::BM4;
           n0 += (part & 1) * TC::BN4;
           e = ofs.expert(m0);
-          tile_run<TC::BM4, TC::BN4, WM, WN, SCHED, EPI>(p, smem, e, m0, n0, kbeg, kend);
+          tile_run<TC::BM4, TC::BN4, WM, WN, SCHED, EPI, OCC>(p, smem, e, m0, n0, kbeg, kend);
           return;
         }
       }
@@ -703,7 +779,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
         if (TC::BM2 == BM) n0 += part * TC::BN2;
         else m0 += part * TC::BM2;
         e = ofs.expert(m0);
-        tile_run<TC::BM2, TC::BN2, WM, WN, SCHED, EPI>(p, smem, e, m0, n0, kbeg, kend);
+        tile_run<TC::BM2, TC::BN2, WM, WN, SCHED, EPI, OCC>(p, smem, e, m0, n0, kbeg, kend);
         return;
       }
     }
@@ -755,7 +831,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
     kend = kbeg + ksp[e];
     __syncthreads();  // the LDS scratch is reused by the main loop
   }
-  tile_run<BM, BN, WM, WN, SCHED, EPI>(p, smem, e, m0, n0, kbeg, kend);
+  tile_run<BM, BN, WM, WN, SCHED, EPI, OCC>(p, smem, e, m0, n0, kbeg, kend);
 }
 
 // ------------------------------------------------------------------ host launchers
@@ -765,26 +841,32 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmParams p) {
 // 128x128 for pad_multiple 128. M-grouped row tiles divide pad_multiple. dSwiGLU stays on
 // 256x128: with 256 accumulators per wavefront its epilogue has registers for one fragment of
 // g/u lookahead only, and the exposed h13 read latency made it slower than 256x128 (measured).
-template <int BM, int BN, int SCHED, int EPI>
+template <int BM, int BN, int SCHED, int EPI, int OCC = 1>
 static hipError_t launch_cfg(const GemmParams& p, hipStream_t st) {
   // 1-D grids: the kernel maps block ids to tiles (see the schedulers)
   int64_t nblk;
   if (SCHED == SCHED_MGROUP)
-    nblk = (p.mcap / BM) * (p.N / BN) + (TailCfg<BM, BN>::Q2 ? 3 * p.ncu : 0);  // + tail sub-tiles
+    nblk = (p.mcap / BM) * (p.N / BN) + (TailCfg<BM, BN>::Q2 ? 3 * p.ncu * OCC : 0);  // + tail sub-tiles
   else
     nblk = (p.M / BM) * (p.N / BN) * p.E;
   if (nblk == 0) return hipSuccess;
   if (nblk > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)nblk);
-  hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, 2, 2, SCHED, EPI>), grid, dim3(256), 0, st, p);
+  hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, 2, 2, SCHED, EPI, OCC>), grid, dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
 template <int SCHED, int EPI>
 static hipError_t launch(const GemmParams& p, bool big_m, hipStream_t st) {
-  if constexpr (EPI != EPI_DSWIGLU)
+  if constexpr (EPI == EPI_DSWIGLU) {
+    // two blocks per CU: one block's dSwiGLU epilogue (sigmoid, saved g/u reads, dual
+    // quantization) runs beside the other block's matrix instructions; measured 13% faster
+    // than one 256 x 128 block per CU on the DSv3 rank shape (FC2 dgrad: 141 against 165 us)
+    if (big_m) return launch_cfg<256, 128, SCHED, EPI, 2>(p, st);
+  } else {
     if (big_m && p.N % 256 == 0) return launch_cfg<256, 256, SCHED, EPI>(p, st);
-  if (big_m) return launch_cfg<256, 128, SCHED, EPI>(p, st);
+    if (big_m) return launch_cfg<256, 128, SCHED, EPI>(p, st);
+  }
   return launch_cfg<128, 128, SCHED, EPI>(p, st);
 }
 
