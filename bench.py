@@ -38,14 +38,14 @@ def gemm_flops(name, m_real, D, F):
 
 def quant_bytes(name, m_pad, m_real, E, D, F):
     """Algorithmic HBM bytes of one launch of each quantization kernel: BF16 read of the real
-    rows, codes in both directions (2 B/element) and scales (2/32 B/element) written."""
+    rows, codes in both directions (2 B/element) and scales (2/32 B/element) written.
+    quant_fwd quantizes W13 (packed), W2 and X in one launch."""
     out = 2 + 2.0 / 32
-    if name in ("quant_x", "quant_dy"):
-        return m_real * D * 2 + m_pad * D * out
-    if name == "quant_w13":
-        return E * 2 * F * D * (2 + out)
-    if name == "quant_w2":
-        return E * D * F * (2 + out)
+    x = m_real * D * 2 + m_pad * D * out
+    if name == "quant_dy":
+        return x
+    if name == "quant_fwd":
+        return E * 2 * F * D * (2 + out) + E * D * F * (2 + out) + x
     return None
 
 
@@ -265,7 +265,7 @@ def main():
     }
 
     if not args.no_plans:
-        out["dispatch"] = bench_dispatch(mx, torch, dev, args, kernels["quant_x"]["avg_us"])
+        out["dispatch"] = bench_dispatch(mx, torch, dev, args, kernels["quant_fwd"]["avg_us"], sets[0])
         out["plans"] = bench_plans(mx, torch, dev, args, sets, counts, E, D, F, y, dx, dw1, dw3, dw2)
     if not args.no_quant:
         out["quantize"] = bench_quantize(mx, torch, dev, args)
@@ -277,6 +277,8 @@ def main():
                 "w3_cpu": cpu_prob["w3"], "w2_cpu": cpu_prob["w2"], "counts": counts, "offs": offs,
                 "D": D, "F": F, "pad": pad}
         out["cpu_baseline"] = cpu_baseline(prob)
+        if "quantize" in out:
+            out["quantize"]["cpu_baseline"] = cpu_baseline_quantize()
     print(json.dumps(out), flush=True)
 
 
@@ -314,12 +316,42 @@ def bench_quantize(mx, torch, dev, args):
     gbs = nbytes / avg_s / 1e9
     # the E5M2 element variant of the same kernel, same workload
     avg5 = loop_seconds(torch, n, lambda i: mx.mxfp8_quantize(xs[i % 3], rows, cols, 3 | mx.E5M2, q_r, s_r, q_c, s_c))
+    # measured ceiling: a plain device copy reading the quantizer's input bytes and writing as
+    # many (torch's vectorised copy kernel), same rotation of 3 sources
+    dst = torch.empty_like(xs[0])
+    for i in range(3):
+        dst.copy_(xs[i])
+    cp_s = loop_seconds(torch, n, lambda i: dst.copy_(xs[i % 3]))
+    cp_gbs = 2 * xs[0].numel() * 2 / cp_s / 1e9
+    del dst
     return {"workload": f"quant: BF16 [{rows}, {cols}] dual (row-wise + column-wise) MXFP8", "value": round(gbs, 1),
             "unit": "GB/s", "avg_us": round(avg_s * 1e6, 2),
             "e5m2": {"value": round(nbytes / avg5 / 1e9, 1), "unit": "GB/s", "avg_us": round(avg5 * 1e6, 2)},
+            "copy_ceiling": {"value": round(cp_gbs, 1), "unit": "GB/s", "avg_us": round(cp_s * 1e6, 2),
+                             "kernel": f"device copy of BF16 [{rows}, {cols}] (read + write)",
+                             "frac_of_copy": round(gbs / cp_gbs, 4)},
             "roofline": {"bound": "hbm", "kernel": "quantize", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": traffic_for("quantize", "quant")}}
+
+
+def cpu_baseline_quantize(rows_sample=8192):
+    """The oracle's dual quantizer (numpy, one thread: no BLAS involved) on the first
+    rows_sample rows of the quantizer workload, reported on the same 4.0625 B/element."""
+    import numpy as np
+    import workloads
+    from oracle.formats import bf16_bits_to_f64
+    from oracle.mx import quantize_colwise, quantize_rowwise
+    cols = workloads.QUANT_CONFIG["cols"]
+    x = bf16_bits_to_f64(workloads.bf16_bits(workloads.quant_matrix(seed=42)[:rows_sample]))
+    t0 = time.perf_counter()
+    quantize_rowwise(x)
+    quantize_colwise(x)
+    dt = time.perf_counter() - t0
+    nel = rows_sample * cols
+    return {"value": round(nel * (2 + 2 + 2.0 / 32) / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"dual quantization of rows 0..{rows_sample - 1} of the [16384, {cols}] workload "
+                      f"({nel} elements) in {dt:.1f} s; numpy fp64 table search, one thread"}
 
 
 def bench_plans(mx, torch, dev, args, sets, counts, E, D, F, y, dx, dw1, dw3, dw2):
@@ -351,7 +383,7 @@ def bench_plans(mx, torch, dev, args, sets, counts, E, D, F, y, dx, dw1, dw3, dw
             ms = (time.perf_counter() - t0) * 1e3 / args.steps
             res[f"{plan}_pad{pad}"] = {"ms_per_step": round(ms, 4), "m_padded": mcap,
                                        "useful_tflops": round(18.0 * m_real * D * F / (ms / 1e3) / 1e12, 1),
-                                       "launches_fwd_bwd": "5 + 5" if plan == "fused" else "6 + 6"}
+                                       "launches_fwd_bwd": "3 + 5" if plan == "fused" else "4 + 6"}
             del ctx
     return res
 
@@ -379,10 +411,10 @@ def bench_dequantize(mx, torch, dev, args):
                          "traffic": traffic_for("dequantize", "quant")}}
 
 
-def bench_dispatch(mx, torch, dev, args, quant_x_us):
+def bench_dispatch(mx, torch, dev, args, quant_fwd_us, weights):
     """Dispatch of the workload's routed tokens into the padded layout: the routing plan, then
-    either the BF16 permute (followed by the forward's own Q_X, timed in the main pass) or the
-    fused gather + dual quantization of X."""
+    either the BF16 permute (followed by the forward's quantization of X: the forward quantizer's
+    time with X minus its time without X) or the fused gather + dual quantization of X."""
     import workloads
     tok, ids = workloads.routed_tokens(args.workload, device="cpu")
     cfg = workloads.MLP_CONFIGS[args.workload]
@@ -413,12 +445,22 @@ def bench_dispatch(mx, torch, dev, args, quant_x_us):
         one(i)
     torch.cuda.synchronize()
     assert int(status.item()) == mx.DEV_OK and ctx.status() == mx.DEV_OK
-    mx.profile_begin(3 * n)
+    y = torch.empty((mcap, D), dtype=torch.bfloat16, device=dev)
+
+    def fwd_xq(i):  # the forward with X's codes from the fused dispatch: W13 and W2 only
+        ctx.fwd(offs, cnt, None, weights["w1"], weights["w3"], weights["w2"], y)
+
+    for i in range(2):
+        fwd_xq(i)
+    torch.cuda.synchronize()
+    mx.profile_begin(6 * n)
     for i in range(n):
         one(i)
+        fwd_xq(i)
     torch.cuda.synchronize()
     prof = mx.profile_end()
-    us = {k: prof[k][1] / prof[k][0] * 1e3 for k in ("route_plan", "permute", "dispatch_quant_x")}
+    us = {k: prof[k][1] / prof[k][0] * 1e3 for k in ("route_plan", "permute", "dispatch_quant_x", "quant_fwd")}
+    quant_x_us = quant_fwd_us - us["quant_fwd"]
     # compulsory HBM bytes: each token row read once (its topk copies come from cache), every
     # padded row written, the row indices read
     rd = tokens * D * 2
@@ -431,9 +473,11 @@ def bench_dispatch(mx, torch, dev, args, quant_x_us):
             "permute_us": round(us["permute"], 2), "permute_gbs": gbs(perm_bytes, us["permute"]),
             "dispatch_quant_x_us": round(us["dispatch_quant_x"], 2),
             "dispatch_quant_x_gbs": gbs(dq_bytes, us["dispatch_quant_x"]),
+            "quant_x_us": round(quant_x_us, 2),
             "unfused_us": round(us["permute"] + quant_x_us, 2),
             "fused_us": round(us["dispatch_quant_x"], 2),
-            "note": "unfused = permute + the forward's quant_x (main serial pass); fused = dispatch_quant_x"}
+            "note": "unfused = permute + the forward quantizer's X share (its time with X, main serial pass, "
+                    "minus its time without X); fused = dispatch_quant_x"}
 
 
 if __name__ == "__main__":

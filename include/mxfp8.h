@@ -147,8 +147,8 @@ mxf_status mxfp8_dequantize(const void* q, const void* s, int64_t rows, int64_t 
 #define MXF_SERIAL 4u      /* launch every kernel on the caller's stream, one after another:
                               the default, stated explicitly (not with MXF_CONCURRENT) */
 #define MXF_CONCURRENT 32u /* run independent launches concurrently on two helper streams forked
-                              from and joined into the caller's stream (W2's quantization beside
-                              FC1; FC2 wgrad, FC1 wgrad and FC1 dgrad beside each other). Measured
+                              from and joined into the caller's stream (the backward's FC2 wgrad,
+                              FC1 wgrad and FC1 dgrad beside each other). Measured
                               on MI355X it is slower than the serial order for the DSv3 rank
                               shape (the GEMMs then share their L2 panels); kept for A/B runs */
 
@@ -213,7 +213,8 @@ mxf_status mxf_mlp_tensor(const mxf_mlp_desc* desc /* host */, int which, int* r
                           size_t* offset /* host */, size_t* bytes /* host */);
 
 /* Streams: fwd and bwd enqueue their kernels asynchronously on `stream`. With MXF_CONCURRENT
- * some of them run on two helper streams owned by the calling host thread (one pair per device);
+ * some backward kernels run on two helper streams owned by the calling host thread (one pair per
+ * device);
  * the helpers start after everything previously enqueued on `stream` and `stream` waits for them
  * before the call returns, so the call behaves as one ordered unit of work on `stream`.
  *
@@ -321,7 +322,8 @@ mxf_status mxf_read_status(const void* workspace, void* stream, int32_t* device_
  * created here, not in the timed calls). mxf_profile_end waits for the recorded events and
  * returns, per kernel name, the number of launches and their summed duration in ms; it
  * fills at most max_out entries and sets *n_out to the number filled, then stops recording.
- * Kernel names: quant_w13, quant_w2, quant_x, fc1_swiglu, fc2, quant_dy, fc2_dgrad_dswiglu,
+ * Kernel names: quant_fwd (W13, W2 and X quantized in one launch), fc1_swiglu, fc2, quant_dy,
+ * fc2_dgrad_dswiglu,
  * fc2_wgrad, fc1_dgrad, fc1_wgrad (MXF_UNFUSED: fc1, swiglu_quant, fc2_dgrad, dswiglu_quant),
  * quantize, dequantize, route_plan, permute, dispatch_quant_x.
  * Errors: MXF_E_ARG (capacity < 1 or > 1<<20, or end without begin), MXF_E_NULL, MXF_E_HIP. */

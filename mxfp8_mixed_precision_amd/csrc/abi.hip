@@ -351,32 +351,15 @@ mxf_status grouped_mlp_fwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   const int64_t M = desc->m_capacity, D = desc->D, F = desc->F, E = desc->E;
   const bool dbg = (desc->flags & MXF_DEBUG_F32) != 0;
 
-  MXF_HIP(timed("quant_w13", st, [&] {
-            return mxf_launch_quant_weights(w1, w3, true, E, 2 * F, D, T(MXF_T_W13Q_R), T(MXF_T_W13S_R),
-                                            T(MXF_T_W13Q_C), T(MXF_T_W13S_C), st);
-          }), "W13 quantize launch");
-  if (!xq) {
-    MXF_HIP(timed("quant_x", st, [&] {
-              return mxf_launch_quant_tokens(x, M, D, offs, counts, (int)E, desc->pad_multiple, T(MXF_T_XQ_R),
-                                             T(MXF_T_XS_R), T(MXF_T_XQ_C), T(MXF_T_XS_C),
-                                             (int32_t*)T(MXF_T_STATUS), true, st);
-            }), "X quantize launch");
-  }
-
-  // W2 is needed only by FC2: its (HBM-bound) quantization runs on a helper stream beside FC1,
-  // whose main loop is bound by L2 -> LDS traffic and leaves HBM bandwidth spare
-  Helpers* H = nullptr;
-  if ((s = get_helpers(&H, desc->flags, st)) != MXF_OK) return s;
-  const bool fork = H->s[0] != st;
-  if (fork) {
-    MXF_HIP(hipEventRecord(H->fork, st), "hipEventRecord");
-    MXF_HIP(hipStreamWaitEvent(H->s[0], H->fork, 0), "hipStreamWaitEvent");
-  }
-  MXF_HIP(timed("quant_w2", H->s[0], [&] {
-            return mxf_launch_quant_weights(w2, nullptr, false, E, D, F, T(MXF_T_W2Q_R), T(MXF_T_W2S_R),
-                                            T(MXF_T_W2Q_C), T(MXF_T_W2S_C), H->s[0]);
-          }), "W2 quantize launch");
-  if (fork) MXF_HIP(hipEventRecord(H->join[0], H->s[0]), "hipEventRecord");
+  // W13 (pack + dual), W2 (dual) and X (dual, unless the fused dispatch wrote its codes) in
+  // one launch
+  MXF_HIP(timed("quant_fwd", st, [&] {
+            return mxf_launch_quant_fwd(w1, w3, w2, E, D, F, T(MXF_T_W13Q_R), T(MXF_T_W13S_R), T(MXF_T_W13Q_C),
+                                        T(MXF_T_W13S_C), T(MXF_T_W2Q_R), T(MXF_T_W2S_R), T(MXF_T_W2Q_C),
+                                        T(MXF_T_W2S_C), xq ? nullptr : x, M, offs, counts, desc->pad_multiple,
+                                        T(MXF_T_XQ_R), T(MXF_T_XS_R), T(MXF_T_XQ_C), T(MXF_T_XS_C),
+                                        (int32_t*)T(MXF_T_STATUS), st);
+          }), "forward quantize launch");
 
   mxf::GemmParams p = {};
   p.offs = offs;
@@ -414,7 +397,6 @@ mxf_status grouped_mlp_fwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   p.N = D; p.K = F;
   p.C = y; p.ldc = D; p.out_f32 = (desc->flags & MXF_OUT_F32) ? 1 : 0;
   p.dbg = nullptr;
-  if (fork) MXF_HIP(hipStreamWaitEvent(st, H->join[0], 0), "hipStreamWaitEvent");
   MXF_HIP(timed("fc2", st, [&] { return mxf_launch_gemm_mgroup(0, p, st); }), "FC2 launch");
   return MXF_OK;
 }

@@ -52,6 +52,11 @@ hipError_t mxf_launch_quant_tokens(const void* x, int64_t mcap, int64_t D, const
 hipError_t mxf_launch_quant_weights(const void* w, const void* w3, bool pack13, int64_t E, int64_t rows,
                                     int64_t cols, void* q_r, void* s_r, void* q_c, void* s_c,
                                     hipStream_t st);
+hipError_t mxf_launch_quant_fwd(const void* w1, const void* w3, const void* w2, int64_t E, int64_t D, int64_t F,
+                                void* w13q_r, void* w13s_r, void* w13q_c, void* w13s_c, void* w2q_r, void* w2s_r,
+                                void* w2q_c, void* w2s_c, const void* x, int64_t mcap, const int32_t* offs,
+                                const int32_t* counts, int pad, void* xq_r, void* xs_r, void* xq_c, void* xs_c,
+                                int32_t* status, hipStream_t st);
 hipError_t mxf_launch_swiglu_quant(const void* h13, int64_t mcap, int64_t F, const int32_t* offs,
                                    const int32_t* counts, int E, int pad, void* q_r, void* s_r, void* q_c,
                                    void* s_c, hipStream_t st);

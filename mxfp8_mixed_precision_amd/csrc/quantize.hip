@@ -58,15 +58,24 @@ struct QuantParams {
 };
 
 
+// Column codes of a block, transposed [128 columns][QTP bytes], and its scale words (4 groups of
+// a row / of a column), staged in LDS so that every global store is a 16-byte (codes) or 4-byte
+// (scales) piece of a contiguous run.
+constexpr int QTP = 128 + 8;
+struct QuantLds {
+  uint8_t qT[128 * QTP];
+  uint32_t srow[128];
+  uint32_t scol[128];
+};
+
+// One 128 x 128 tile of one batch entry: (bx, by, bz) is the tile's position in the launch grid
+// of its kind (see grid_of), so the same body serves a kernel of one kind and the combined
+// forward kernel.
 template <int KIND, bool ROW, bool COL, int FMT = FMT_E4M3>
-__global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
-  // Column codes of the block, transposed [128 columns][QTP bytes], and the block's scale
-  // words (4 groups of a row / of a column), staged in LDS so that every global store is a
-  // 16-byte (codes) or 4-byte (scales) piece of a contiguous run.
-  constexpr int QTP = 128 + 8;
-  __shared__ __attribute__((aligned(16))) uint8_t qT[COL ? 128 * QTP : 16];
-  __shared__ uint32_t srow[128];
-  __shared__ uint32_t scol[128];
+__device__ __forceinline__ void quant_tile(const QuantParams& p, int64_t bx, int64_t by, int64_t bz, QuantLds& L) {
+  uint8_t* qT = L.qT;
+  uint32_t* srow = L.srow;
+  uint32_t* scol = L.scol;
   uint8_t* srow_b = reinterpret_cast<uint8_t*>(srow);
   uint8_t* scol_b = reinterpret_cast<uint8_t*>(scol);
   const int tid = threadIdx.x;
@@ -74,17 +83,17 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
   const int w = tid >> 6;
   const int s = lane >> 4;
   const int c = lane & 15;
-  const int64_t e = blockIdx.z;
+  const int64_t e = bz;
   // with col_fast, consecutive blocks take the column tiles of one 128-row band, so the blocks
   // resident at a time read and write a few contiguous bands
-  int64_t row0 = (int64_t)(p.col_fast ? blockIdx.y : blockIdx.x) * 128;
-  int64_t col0 = (int64_t)(p.col_fast ? blockIdx.x : blockIdx.y) * 128;
+  int64_t row0 = (p.col_fast ? by : bx) * 128;
+  int64_t col0 = (p.col_fast ? bx : by) * 128;
   if (p.macro8) {
     // Row-major scales of a single matrix: a row's 32-byte scale sector spans 8 column tiles
     // and a column's spans 8 row bands. Block L runs on XCD L % 8; each XCD takes whole
     // macro-tiles of 8 bands x 8 column tiles, so every sector is filled inside one XCD's L2
     // (split over XCDs, each L2 writes its few bytes back as a partial sector).
-    const int64_t L = blockIdx.x, x = L & 7, sq = L >> 3;
+    const int64_t L = bx, x = L & 7, sq = L >> 3;
     const int64_t m = x + 8 * (sq >> 6);         // macro-tile of the XCD's sq-th block
     const int64_t w = sq & 63;                   // tile within it, band-major
     const int64_t mcols = (p.cols + 1023) >> 10;  // macro-tiles across
@@ -102,7 +111,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
     // every wavefront reads the offsets (same answers everywhere); mend and the block's rows
     // are multiples of 128, so a block is either wholly before offs[E] or wholly past it
     const Offsets ofs = read_offsets(p.offs, p.counts, p.E, p.pad, p.rows);
-    if ((KIND == QK_MASKED || KIND == QK_GATHER) && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+    if ((KIND == QK_MASKED || KIND == QK_GATHER) && bx == 0 && by == 0 && threadIdx.x == 0)
       *p.status = ofs.ok ? 0 : 1;
     if (!ofs.ok) return;
     if (row0 >= ofs.mend) return;  // tail rows: never read or written
@@ -267,6 +276,69 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
   }
 }
 
+template <int KIND, bool ROW, bool COL, int FMT = FMT_E4M3>
+__global__ __launch_bounds__(256) void quant_dual_kernel(QuantParams p) {
+  __shared__ __attribute__((aligned(16))) QuantLds L;
+  quant_tile<KIND, ROW, COL, FMT>(p, blockIdx.x, blockIdx.y, blockIdx.z, L);
+}
+
+// Launch grid of one quantization (tiles of 128 x 128, batch entries along z); sets the
+// parameters' block-order fields. Shared by the single-kind launches and the combined forward
+// kernel.
+struct QGrid {
+  int64_t x, y, z;
+};
+static QGrid grid_of(int kind, QuantParams& p, int64_t batch) {
+  const int64_t rt = std::max<int64_t>((p.rows + 127) / 128, 1), ct = std::max<int64_t>((p.cols + 127) / 128, 1);
+  // Block order: column tiles fastest unless the matrix is much wider than tall or a batch of
+  // small matrices (measured on MI355X: 10-20% faster for tall operands such as [26112, 2048],
+  // slightly slower for [2048, 26112] and for the expert weight batches); grid y and z are
+  // limited to 65535.
+  p.col_fast = (batch == 1 && rt * 8 >= ct && rt <= 65535) || ct > 65535;
+  // a single matrix with row-major scales on both sides: macro-tile order (see the kernel)
+  p.macro8 = kind == QK_PLAIN && batch == 1 && !p.blk && rt % 8 == 0 && ct % 8 == 0 &&
+             ((rt / 8) * (ct / 8)) % 8 == 0 && rt * ct <= 0x7FFFFFFF;
+  if (p.macro8) return {rt * ct, 1, 1};
+  return {p.col_fast ? ct : rt, p.col_fast ? rt : ct, batch > 0 ? batch : 1};
+}
+
+// The forward's operand quantizations in one launch: W13 (pack + dual, a batch of experts), W2
+// (dual, a batch of experts) and, unless X's codes were written by the fused dispatch, X (dual
+// under the token layout; its first block writes the status word). One grid of n13 + n2 + nx
+// blocks, each section walking its own tile grid; one launch instead of three fills the
+// compute units through the last round of tiles.
+struct QuantFwd {
+  QuantParams w13, w2, x;
+  QGrid g13, g2, gx;
+  int64_t n13, n2, nx;
+};
+__global__ __launch_bounds__(256) void quant_fwd_kernel(QuantFwd f) {
+  __shared__ __attribute__((aligned(16))) QuantLds L;
+  int64_t b = blockIdx.x;
+  auto split = [](int64_t i, const QGrid& g, int64_t& bx, int64_t& by, int64_t& bz) {
+    bx = i % g.x;
+    by = (i / g.x) % g.y;
+    bz = i / (g.x * g.y);
+  };
+  int64_t bx, by, bz;
+  if (b < f.n13) {
+    split(b, f.g13, bx, by, bz);
+    quant_tile<QK_PACK13, true, true>(f.w13, bx, by, bz, L);
+    return;
+  }
+  b -= f.n13;
+  if (b < f.n2) {
+    split(b, f.g2, bx, by, bz);
+    quant_tile<QK_PLAIN, true, true>(f.w2, bx, by, bz, L);
+    return;
+  }
+  b -= f.n2;
+  if (b < f.nx) {
+    split(b, f.gx, bx, by, bz);
+    quant_tile<QK_MASKED, true, true>(f.x, bx, by, bz, L);
+  }
+}
+
 // ------------------------------------------------------------------ dequantization
 
 // E4M3 code -> its exact fp32 value, from the bit fields (OCP FP8): exponent field 0 is m * 2^-9,
@@ -406,18 +478,8 @@ static hipError_t launch_quant(int kind, uint32_t mode, const QuantParams& pin, 
   // the token-layout kind always runs (its first block writes the status word)
   if ((pin.rows == 0 || pin.cols == 0 || batch == 0) && kind != QK_MASKED && kind != QK_GATHER) return hipSuccess;
   QuantParams p = pin;
-  const int64_t rt = std::max<int64_t>((p.rows + 127) / 128, 1), ct = std::max<int64_t>((p.cols + 127) / 128, 1);
-  // Block order: column tiles fastest unless the matrix is much wider than tall or a batch of
-  // small matrices (measured on MI355X: 10-20% faster for tall operands such as [26112, 2048],
-  // slightly slower for [2048, 26112] and for the expert weight batches); grid y and z are
-  // limited to 65535.
-  p.col_fast = (batch == 1 && rt * 8 >= ct && rt <= 65535) || ct > 65535;
-  // a single matrix with row-major scales on both sides: macro-tile order (see the kernel)
-  p.macro8 = kind == QK_PLAIN && batch == 1 && !p.blk && rt % 8 == 0 && ct % 8 == 0 &&
-             ((rt / 8) * (ct / 8)) % 8 == 0 && rt * ct <= 0x7FFFFFFF;
-  const dim3 grid = p.macro8 ? dim3((unsigned)(rt * ct), 1, 1)
-                             : dim3((unsigned)(p.col_fast ? ct : rt), (unsigned)(p.col_fast ? rt : ct),
-                                    (unsigned)(batch > 0 ? batch : 1));
+  const QGrid g = grid_of(kind, p, batch);
+  const dim3 grid((unsigned)g.x, (unsigned)g.y, (unsigned)g.z);
   const dim3 block(256);
 #define MXF_QLAUNCH(K, R, C) hipLaunchKernelGGL((quant_dual_kernel<K, R, C>), grid, block, 0, st, p)
   if (kind == QK_PLAIN && e5m2) {
@@ -465,9 +527,9 @@ hipError_t mxf_launch_quantize(const void* x, int64_t rows, int64_t cols, uint32
 // Dual quantization of the activation-like operand x [mcap, D] under the token layout
 // (pad rows read as zero, rows >= offs[E] skipped); writes the status word. Scales in 128-k
 // planes (row-wise [D/128][mcap][4], column-wise [mcap/128][D][4]).
-hipError_t mxf_launch_quant_tokens(const void* x, int64_t mcap, int64_t D, const int32_t* offs,
-                                   const int32_t* counts, int E, int pad, void* q_r, void* s_r,
-                                   void* q_c, void* s_c, int32_t* status, bool saved_c, hipStream_t st) {
+static mxf::QuantParams token_params(const void* x, int64_t mcap, int64_t D, const int32_t* offs,
+                                     const int32_t* counts, int E, int pad, void* q_r, void* s_r, void* q_c,
+                                     void* s_c, int32_t* status, bool saved_c) {
   mxf::QuantParams p = {};
   p.blk = 1;  // GEMM operands: codes in 64-k panels
   p.nt_c = saved_c;
@@ -486,7 +548,14 @@ hipError_t mxf_launch_quant_tokens(const void* x, int64_t mcap, int64_t D, const
   p.E = E;
   p.pad = pad;
   p.status = status;
-  return mxf::launch_quant(mxf::QK_MASKED, 3, p, 1, st);
+  return p;
+}
+
+hipError_t mxf_launch_quant_tokens(const void* x, int64_t mcap, int64_t D, const int32_t* offs,
+                                   const int32_t* counts, int E, int pad, void* q_r, void* s_r,
+                                   void* q_c, void* s_c, int32_t* status, bool saved_c, hipStream_t st) {
+  return mxf::launch_quant(mxf::QK_MASKED, 3,
+                           token_params(x, mcap, D, offs, counts, E, pad, q_r, s_r, q_c, s_c, status, saved_c), 1, st);
 }
 
 // Fused dispatch: dual quantization of the padded token layout [mcap, D] gathered from the token
@@ -556,9 +625,8 @@ hipError_t mxf_launch_dswiglu_quant(const void* dh, const void* h13, int64_t mca
 // Dual quantization of a batch of E weight matrices [rows, cols], scales in 128-k planes per
 // matrix ([cols/128][rows][4] and [rows/128][cols][4]). pack13 = true reads w1/w3
 // [E, rows/2, cols] and quantizes their [E, rows, cols] 32-block interleave.
-hipError_t mxf_launch_quant_weights(const void* w, const void* w3, bool pack13, int64_t E, int64_t rows,
-                                    int64_t cols, void* q_r, void* s_r, void* q_c, void* s_c,
-                                    hipStream_t st) {
+static mxf::QuantParams weight_params(const void* w, const void* w3, bool pack13, int64_t rows, int64_t cols,
+                                      void* q_r, void* s_r, void* q_c, void* s_c) {
   mxf::QuantParams p = {};
   p.blk = 1;  // GEMM operands: codes in 64-k panels
   p.nt_c = 1;  // column codes are saved for the backward pass
@@ -578,7 +646,41 @@ hipError_t mxf_launch_quant_weights(const void* w, const void* w3, bool pack13, 
   p.ldc = rows;
   p.sr_rs = 4; p.sr_kbs = 4 * rows;  // 128-k planes per matrix
   p.sc_rs = 4; p.sc_kbs = 4 * cols;
-  return mxf::launch_quant(pack13 ? mxf::QK_PACK13 : mxf::QK_PLAIN, 3, p, E, st);
+  return p;
+}
+
+hipError_t mxf_launch_quant_weights(const void* w, const void* w3, bool pack13, int64_t E, int64_t rows,
+                                    int64_t cols, void* q_r, void* s_r, void* q_c, void* s_c,
+                                    hipStream_t st) {
+  return mxf::launch_quant(pack13 ? mxf::QK_PACK13 : mxf::QK_PLAIN, 3,
+                           weight_params(w, w3, pack13, rows, cols, q_r, s_r, q_c, s_c), E, st);
+}
+
+// The forward's three quantizations (W13 pack + dual, W2 dual, X dual under the token layout)
+// in one launch (quant_fwd_kernel); x == nullptr leaves X out (its codes were written by the
+// fused dispatch). Same outputs as mxf_launch_quant_weights (twice) and mxf_launch_quant_tokens.
+hipError_t mxf_launch_quant_fwd(const void* w1, const void* w3, const void* w2, int64_t E, int64_t D, int64_t F,
+                                void* w13q_r, void* w13s_r, void* w13q_c, void* w13s_c, void* w2q_r, void* w2s_r,
+                                void* w2q_c, void* w2s_c, const void* x, int64_t mcap, const int32_t* offs,
+                                const int32_t* counts, int pad, void* xq_r, void* xs_r, void* xq_c, void* xs_c,
+                                int32_t* status, hipStream_t st) {
+  mxf::QuantFwd f = {};
+  f.w13 = weight_params(w1, w3, true, 2 * F, D, w13q_r, w13s_r, w13q_c, w13s_c);
+  f.w2 = weight_params(w2, nullptr, false, D, F, w2q_r, w2s_r, w2q_c, w2s_c);
+  f.g13 = mxf::grid_of(mxf::QK_PACK13, f.w13, E);
+  f.g2 = mxf::grid_of(mxf::QK_PLAIN, f.w2, E);
+  f.n13 = f.g13.x * f.g13.y * f.g13.z;
+  f.n2 = f.g2.x * f.g2.y * f.g2.z;
+  if (x) {
+    f.x = token_params(x, mcap, D, offs, counts, (int)E, pad, xq_r, xs_r, xq_c, xs_c, status, true);
+    f.gx = mxf::grid_of(mxf::QK_MASKED, f.x, 1);
+    f.nx = f.gx.x * f.gx.y * f.gx.z;
+  }
+  const int64_t n = f.n13 + f.n2 + f.nx;
+  if (n == 0) return hipSuccess;
+  if (n > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mxf::quant_fwd_kernel, dim3((unsigned)n), dim3(256), 0, st, f);
+  return hipGetLastError();
 }
 
 hipError_t mxf_launch_dequantize(const void* q, const void* s, int64_t rows, int64_t cols, bool bf16, bool e5m2,

@@ -18,7 +18,7 @@ per launch, with the sha256 of the kernel sources they were measured on; bench.p
 reports them while the sources are unchanged).
 
 Kernel dispatches are named by their position in a bench.py step: the MLP step enqueues, in
-order, quant_w13, quant_x, quant_w2, fc1_swiglu, fc2, quant_dy, fc2_wgrad, fc2_dgrad_dswiglu,
+order, quant_fwd (W13, W2 and X in one launch), fc1_swiglu, fc2, quant_dy, fc2_wgrad, fc2_dgrad_dswiglu,
 fc1_wgrad, fc1_dgrad; a --quant-only run launches `quantize` (the dual quantizer) and then
 `dequantize` (row-wise codes to BF16). Profile with
 `bench.py --serial` so that every kernel runs alone (durations not stretched by overlap).
@@ -32,11 +32,11 @@ import os
 import re
 from collections import defaultdict
 
-MLP_SEQUENCE = ["quant_w13", "quant_x", "quant_w2", "fc1_swiglu", "fc2", "quant_dy", "fc2_wgrad",
+MLP_SEQUENCE = ["quant_fwd", "fc1_swiglu", "fc2", "quant_dy", "fc2_wgrad",
                 "fc2_dgrad_dswiglu", "fc1_wgrad", "fc1_dgrad"]
 # expected kernel template per logical name: (kernel family, SCHED/KIND, EPI/ROW,COL)
 EXPECT = {
-    "quant_w13": "quant_dual_kernel<2,", "quant_w2": "quant_dual_kernel<0,", "quant_x": "quant_dual_kernel<1,",
+    "quant_fwd": "quant_fwd_kernel",
     "quant_dy": "quant_dual_kernel<1,", "fc1_swiglu": ", 0, 1>", "fc2": ", 0, 0>", "fc2_dgrad_dswiglu": ", 0, 2>",
     "fc2_wgrad": ", 1, 0>", "fc1_dgrad": ", 0, 0>", "fc1_wgrad": ", 1, 3>", "quantize": "quant_dual_kernel<0,true,true,0>",
     "dequantize": "dequant_kernel<true,0>",
@@ -104,7 +104,7 @@ def _matches(name, logical):
 
 def label(dispatches, quant_only):
     """Attach logical kernel names (see the module docstring). For an MLP run, every window of
-    ten consecutive dispatches whose templates match the step sequence is one step; other
+    eight consecutive dispatches whose templates match the step sequence is one step; other
     dispatches (e.g. a trailing standalone-quantizer measurement) are left out."""
     out = []
     if quant_only:
