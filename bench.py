@@ -49,8 +49,9 @@ def quant_bytes(name, m_pad, m_real, E, D, F):
     return None
 
 
-def traffic_for(kernel, workload):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they match the sources."""
+def traffic_for(kernel, workload, key="kernels"):
+    """A per-launch figure from the committed rocprofv3 counter runs (key "kernels": HBM bytes;
+    "mfma_busy": the matrix-core busy fraction), if they were taken on the current sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -60,7 +61,7 @@ def traffic_for(kernel, workload):
             t = json.load(f)
         if t.get("source_sha256") != source_sha256(ROOT):
             return None
-        return t.get("kernels", {}).get(workload, {}).get(kernel)
+        return t.get(key, {}).get(workload, {}).get(kernel)
     except Exception:
         return None
 
@@ -238,7 +239,8 @@ def main():
         ach = fl / davg_s / 1e12
         roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_FP8_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_FP8_TFLOPS, 4),
-                "traffic": traffic_for(dom, args.workload)}
+                "traffic": traffic_for(dom, args.workload),
+                "mfma_busy": traffic_for(dom, args.workload, "mfma_busy")}
     else:
         by = quant_bytes(dom, m_pad, m_real, E, D, F)
         ach = by / davg_s / 1e9

@@ -11,6 +11,10 @@ Inputs:
   --fetch/write rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of the same command
   --copy-*      the same counters for `bench.py --calibrate-copy` (a 1 GiB device copy), which
                 give the factor from counter units to bytes
+  --compute     (optional) a rocprofv3 --pmc run of the same command with COMPUTE_COUNTERS:
+                per kernel, the matrix-core busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over the
+                kernel's active cycles times the SIMD count, rocprofv3's own MfmaUtil), the
+                FP8 matrix math the hardware counted, the L2 hit rate and the LDS activity
   --commands    text file holding the exact commands that produced the inputs
 
 Outputs (in OUTDIR): <kernel-group>_<workload>.md summaries and traffic.json (HBM bytes
@@ -34,14 +38,19 @@ from collections import defaultdict
 
 MLP_SEQUENCE = ["quant_fwd", "fc1_swiglu", "fc2", "quant_dy", "fc2_wgrad",
                 "fc2_dgrad_dswiglu", "fc1_wgrad", "fc1_dgrad"]
-# expected kernel template per logical name: (kernel family, SCHED/KIND, EPI/ROW,COL)
+# expected kernel template per logical name: a piece of the kernel's name (GEMMs: ", SCHED, EPI, "
+# of gemm_mx_kernel<BM, BN, WM, WN, SCHED, EPI, OCC>; quantizers: the kernel and its KIND)
 EXPECT = {
     "quant_fwd": "quant_fwd_kernel",
-    "quant_dy": "quant_dual_kernel<1,", "fc1_swiglu": ", 0, 1>", "fc2": ", 0, 0>", "fc2_dgrad_dswiglu": ", 0, 2>",
-    "fc2_wgrad": ", 1, 0>", "fc1_dgrad": ", 0, 0>", "fc1_wgrad": ", 1, 3>", "quantize": "quant_dual_kernel<0,true,true,0>",
+    "quant_dy": "quant_dual_kernel<1,", "fc1_swiglu": ", 0, 1, ", "fc2": ", 0, 0, ", "fc2_dgrad_dswiglu": ", 0, 2, ",
+    "fc2_wgrad": ", 1, 0, ", "fc1_dgrad": ", 0, 0, ", "fc1_wgrad": ", 1, 3, ", "quantize": "quant_dual_kernel<0,true,true,0>",
     "dequantize": "dequant_kernel<true,0>",
 }
 QUANT_ONLY = ["quantize", "dequantize"]
+COMPUTE_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_LDS_IDX_ACTIVE",
+                    "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "TCC_HIT_sum", "TCC_MISS_sum"]
+SIMDS = 1024   # 256 compute units x 4 SIMDs
+XCCS = 8       # GRBM_GUI_ACTIVE is reported per XCC; the CSV value is their sum
 
 
 def code_only(text):
@@ -138,6 +147,33 @@ def per_kernel_counter(pmc_dir, counter, quant_only):
     return vals
 
 
+def per_kernel_compute(pmc_dir, quant_only):
+    """Per logical kernel, the mean over launches of each COMPUTE_COUNTERS value."""
+    rows = list(csv.DictReader(open(_one(pmc_dir, "*counter_collection.csv"))))
+    out = {}
+    for counter in COMPUTE_COUNTERS:
+        sel = [r for r in rows if r["Counter_Name"] == counter]
+        disp = label(mxf_dispatches(sel), quant_only)
+        vals = defaultdict(list)
+        for _, logical, r in disp:
+            vals[logical].append(float(r["Counter_Value"]))
+        for k, v in vals.items():
+            out.setdefault(k, {})[counter] = sum(v) / len(v)
+    derived = {}
+    for k, c in out.items():
+        if not all(n in c for n in COMPUTE_COUNTERS):
+            continue
+        active = c["GRBM_GUI_ACTIVE"] / XCCS  # cycles the GPU was active during the dispatch
+        hits, miss = c["TCC_HIT_sum"], c["TCC_MISS_sum"]
+        derived[k] = {"mfma_busy": c["SQ_VALU_MFMA_BUSY_CYCLES"] / (active * SIMDS),
+                      "f8_flop": c["SQ_INSTS_VALU_MFMA_MOPS_F8"] * 512,
+                      "l2_hit": hits / (hits + miss) if hits + miss else None,
+                      "lds_active": c["SQ_LDS_IDX_ACTIVE"] / (active * SIMDS / 4),
+                      "lds_bank_conflict": c["SQ_LDS_BANK_CONFLICT"] / (active * SIMDS / 4),
+                      "active_cycles": active}
+    return derived
+
+
 def copy_factor(pmc_dir, counter, nbytes=1 << 30):
     rows = [r for r in csv.DictReader(open(_one(pmc_dir, "*counter_collection.csv"))) if r["Counter_Name"] == counter]
     vals = [float(r["Counter_Value"]) for r in rows if "copy" in r["Kernel_Name"].lower()]
@@ -155,6 +191,7 @@ def main():
     ap.add_argument("--write")
     ap.add_argument("--copy-fetch")
     ap.add_argument("--copy-write")
+    ap.add_argument("--compute")
     ap.add_argument("--quant-only", action="store_true")
     ap.add_argument("--commands", required=True)
     ap.add_argument("--out", required=True)
@@ -178,6 +215,7 @@ def main():
         lines.append(f"Counter calibration (1 GiB device copy): FETCH_SIZE reads {fraw:.0f} -> x{ff:.4f} bytes per unit; "
                      f"WRITE_SIZE reads {wraw:.0f} -> x{wf:.4f} bytes per unit.")
         lines.append("")
+    comp = per_kernel_compute(args.compute, args.quant_only) if args.compute else {}
     cmds = open(args.commands).read().strip()
     name = "quantize" if args.quant_only else "mlp_fwd_bwd"
     md = [f"# {name} kernels, workload `{args.workload}` (rocprofv3)", "", "Commands (run from the repository root):",
@@ -195,6 +233,23 @@ def main():
         med = sorted(v)[len(v) // 2]
         md.append(f"| {k} | {len(v)} | {sum(v) / len(v):.2f} | {med:.2f} | {min(v):.2f} | {max(v):.2f} | {rd} | {wr} |")
     md.append("")
+    if comp:
+        md.append("Compute counters (one rocprofv3 --pmc pass, " + ", ".join(COMPUTE_COUNTERS) + "): MFMA busy = "
+                  "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCC x 1024 SIMDs), as rocprofv3's MfmaUtil; "
+                  "F8 math = SQ_INSTS_VALU_MFMA_MOPS_F8 x 512 (executed, pad rows included); L2 hit = "
+                  "TCC_HIT / (TCC_HIT + TCC_MISS); LDS active and bank-conflict cycles per CU over the "
+                  "kernel's active cycles.")
+        md.append("")
+        md.append("| kernel | MFMA busy | F8 math TFLOP/launch | L2 hit | LDS active | LDS bank conflict | active cycles |")
+        md.append("|---|---|---|---|---|---|---|")
+        for k in order:
+            if k not in comp:
+                continue
+            c = comp[k]
+            hit = f"{c['l2_hit']:.3f}" if c["l2_hit"] is not None else "-"
+            md.append(f"| {k} | {c['mfma_busy']:.3f} | {c['f8_flop'] / 1e12:.4f} | {hit} | {c['lds_active']:.3f} | "
+                      f"{c['lds_bank_conflict']:.4f} | {c['active_cycles']:.0f} |")
+        md.append("")
     path = os.path.join(args.out, f"{name}_{args.workload}.md")
     with open(path, "w") as f:
         f.write("\n".join(md) + "\n")
@@ -207,6 +262,9 @@ def main():
     t.setdefault("detail", {})[args.workload] = traffic
     if ff:
         t["copy_calibration"] = {"fetch_factor": ff, "write_factor": wf}
+    if comp:
+        t.setdefault("mfma_busy", {})[args.workload] = {k: round(v["mfma_busy"], 4) for k, v in comp.items()}
+        t.setdefault("compute", {})[args.workload] = comp
     with open(tpath, "w") as f:
         json.dump(t, f, indent=1)
     print(open(path).read())
