@@ -467,6 +467,13 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
     uint16_t* hR = reinterpret_cast<uint16_t*>(smem);
     uint8_t* qT = smem + BM * HP * 2;
     uint8_t* sT = qT + HCB * QP;
+    // Row staging two columns at a time: word t of a lane holds rows R, R+1 of its column
+    // (slots 2t, 2t+1), lane l ^ 1 the same rows of the neighbouring column. After one lane
+    // swap, an even lane writes row R of columns (c, c+1), an odd lane row R+1 of (c-1, c):
+    // one 4-byte LDS write per word instead of two 2-byte writes.
+    const bool odd_lane = (lane & 1) != 0;
+    const uint32_t pr_sel = odd_lane ? 0x03020706u : 0x05040100u;  // {swapped, mine} byte picks
+    const int pr_off = odd_lane ? HP - 1 : 0;
     if (p.dbg) {
 #pragma unroll
       for (int i = 0; i < T::FM; ++i)
@@ -504,8 +511,9 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
           *reinterpret_cast<uint32_t*>(qT + hcl * QP + rl + 8 * k) = cvt4(hw[2 * k], hw[2 * k + 1], s);
         if (g == 0) sT[hcl * SG + (tr0 >> 5) + i] = (uint8_t)s.byte;
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
-          hR[(rl + 8 * (q >> 2) + (q & 3)) * HP + hcl] = (uint16_t)(hw[q >> 1] >> (16 * (q & 1)));
+        for (int t = 0; t < 8; ++t)
+          *reinterpret_cast<uint32_t*>(hR + (rl + 8 * (t >> 1) + 2 * (t & 1)) * HP + hcl + pr_off) =
+              __builtin_amdgcn_perm(dpp_xor1(hw[t]), hw[t], pr_sel);
       }
     }
     __syncthreads();
@@ -578,6 +586,10 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
     uint16_t* dR = reinterpret_cast<uint16_t*>(smem);
     uint8_t* qT = smem + SR * DP * 2;
     uint8_t* sT = qT + PCB * QP;
+    // row staging two columns at a time (as in the SwiGLU epilogue)
+    const bool odd_lane = (lane & 1) != 0;
+    const uint32_t pr_sel = odd_lane ? 0x03020706u : 0x05040100u;
+    const int pr_off = odd_lane ? DP - 1 : 0;
     // staged row lr of pass hh is block row (lr / RH) * TM + hh * RH + lr % RH
     auto brow = [&](int hh, int lr) { return (lr / RH) * T::TM + hh * RH + lr % RH; };
     // g, u of the fragments in flight, a ring of GR fragment slots in processing order
@@ -637,8 +649,9 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
               *reinterpret_cast<uint32_t*>(qT + pcl * QP + rl + 8 * k) = cvt4(w[2 * k], w[2 * k + 1], s);
             if (g == 0) sT[pcl * SG + wm * FH + ii] = (uint8_t)s.byte;
 #pragma unroll
-            for (int q = 0; q < 16; ++q)
-              dR[(rl + 8 * (q >> 2) + (q & 3)) * DP + pcl] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
+            for (int t = 0; t < 8; ++t)
+              *reinterpret_cast<uint32_t*>(dR + (rl + 8 * (t >> 1) + 2 * (t & 1)) * DP + pcl + pr_off) =
+                  __builtin_amdgcn_perm(dpp_xor1(w[t]), w[t], pr_sel);
           }
         }
       }
