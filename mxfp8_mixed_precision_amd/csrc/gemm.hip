@@ -70,12 +70,12 @@ struct Tile {
   static constexpr int FN = TN / 32;
   // one stage: A tile [BM][64 B], B tile [BN][64 B]. The scale words (four E8M0 bytes of
   // 128 k per row) of a 128-k block serve its two stages: the even stage loads them into a
-  // ring of three scale slots after the stage slots (one 256-byte piece per wavefront for A,
+  // ring of NSC scale slots after the stage slots (one 256-byte piece per wavefront for A,
   // then for B; rows beyond BM / BN land in unused bytes), the odd stage reads the same slot.
   static constexpr int A_OFF = 0;
   static constexpr int B_OFF = BM * BK;
   static constexpr int STAGE = (BM + BN) * BK;
-  static constexpr int NSC = 3;
+  static constexpr int NSC = OCC == 2 ? 3 : 4;  // scale slots (a power of two where LDS allows)
   static constexpr int SC_OFF = S * STAGE;
   static constexpr int SC_SLOT = 2 * NW * 256;
   static constexpr int LDS_BYTES = 160 * 1024 / OCC;
@@ -102,6 +102,7 @@ struct Tile {
   static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "tile/wavefront mismatch");
   static_assert(BM <= 64 * NW && BN <= 64 * NW, "one scale-word load per wavefront and operand");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 fragments");
+  static_assert(IA <= 4 && IB <= 4, "runs of at most four 1 KB loads per operand and wavefront");
   static_assert(LDS_MAIN <= LDS_BYTES, "pipeline does not fit in LDS");
   static_assert(OCC == 2 ? (S == 3 && L + LO <= 63) : (S % 2 == 0 && (S / 2) * (L + LO) <= 63),
                 "loads in flight exceed the vmcnt range");
@@ -132,12 +133,33 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_ptr)p;
 }
 // Address = wavefront-uniform 64-bit base (SGPRs) + per-lane 32-bit offset (one VGPR).
-__device__ __forceinline__ void g2lds16(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
-}
 __device__ __forceinline__ void g2lds4(const void* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
 }
+// Kilobyte q of a run of consecutive 1 KB loads that share one global base and one M0: the
+// instruction offset (1024 q) moves both the global and the LDS address, so a whole operand of
+// a stage needs one 64-bit base and one M0 value. q is a compile-time constant after unrolling.
+template <int OFF>
+__device__ __forceinline__ void g2lds16_off(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 offset:%3" ::"s"(lds), "v"(voff), "s"(sbase),
+               "i"(OFF) : "memory", "m0");
+}
+__device__ __forceinline__ void g2lds16_q(int q, const void* sbase, uint32_t voff, uint32_t lds) {
+  switch (q) {
+    case 0: g2lds16_off<0>(sbase, voff, lds); break;
+    case 1: g2lds16_off<1024>(sbase, voff, lds); break;
+    case 2: g2lds16_off<2048>(sbase, voff, lds); break;
+    default: g2lds16_off<3072>(sbase, voff, lds); break;
+  }
+}
+
+// LDS reads through a 32-bit LDS byte address; constant offsets added to the returned pointer
+// fold into the instruction's offset field.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const u32x4_t lds_u4;
+typedef __attribute__((address_space(3))) const uint8_t lds_u8;
+__device__ __forceinline__ lds_u4* lds16_at(uint32_t a) { return (lds_u4*)(uintptr_t)a; }
+__device__ __forceinline__ lds_u8* lds8_at(uint32_t a) { return (lds_u8*)(uintptr_t)a; }
 
 // One output tile (rows [m0, m0 + BM), columns [n0, n0 + BN), contraction over [kbeg, kend)):
 // the pipelined main loop and the epilogue. smem holds Tile<BM, BN, WM, WN>::lds(EPI) bytes.
@@ -198,19 +220,20 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
   // and waits the same): q < IA are A-tile loads, then IB B-tile loads, then (even stages
   // only) the A and B scale words of the 128-k block holding the stage, into scale slot
   // (kt / 2) % NSC. q is a compile-time constant.
+  // A wavefront's IA (IB) kilobytes of an operand are consecutive in HBM and in LDS, so they
+  // share one global base and one M0 value (g2lds16_q adds 1024 q to both).
   auto issue_one = [&](int q, int ks, int kt) {
-    const int64_t k0 = (int64_t)ks * T::BK;
+    const uint64_t ku = (uint32_t)ks;  // 0 <= ks < KT
     const uint32_t st = lds0 + (kt % T::S) * T::STAGE;
     const uint32_t sc = lds0 + T::SC_OFF + ((kt >> 1) % T::NSC) * T::SC_SLOT;
     if (q < T::IA) {
-      g2lds16(a_s + q * 1024 + ks * p.akp, a_v, st + T::A_OFF + (wid_u * T::IA + q) * 1024);
+      g2lds16_q(q, a_s + ku * (uint64_t)p.akp, a_v, st + T::A_OFF + wid_u * T::IA * 1024);
     } else if (q < T::IA + T::IB) {
-      const int i = q - T::IA;
-      g2lds16(b_s + i * 1024 + ks * p.bkp, b_v, st + T::B_OFF + (wid_u * T::IB + i) * 1024);
+      g2lds16_q(q - T::IA, b_s + ku * (uint64_t)p.bkp, b_v, st + T::B_OFF + wid_u * T::IB * 1024);
     } else if (q == T::IA + T::IB) {
-      g2lds4(Asg + (k0 >> 7) * p.kbsa, sa_v, sc + wid_u * 256);
+      g2lds4(Asg + (ku >> 1) * (uint64_t)p.kbsa, sa_v, sc + wid_u * 256);
     } else {
-      g2lds4(Bsg + (k0 >> 7) * p.kbsb, sb_v, sc + T::NW * 256 + wid_u * 256);
+      g2lds4(Bsg + (ku >> 1) * (uint64_t)p.kbsb, sb_v, sc + T::NW * 256 + wid_u * 256);
     }
   };
 
@@ -292,26 +315,38 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
   // r / 2, half r % 2 (k bytes [16g, 16g+16) or [32+16g, 32+16g+16)); then 2 FN B reads; then
   // FM + FN scale bytes.
   constexpr int NR = 2 * (T::FM + T::FN) + T::FM + T::FN;
-  auto read_one = [&](int r, int kt, auto par) {
+  // This lane's LDS byte addresses in ring slot 0 and scale slot 0: fragment rows tr0 + r32
+  // (A) and tc0 + r32 (B) in k half hi, and the row's scale word at byte g. Fragment i (j) is
+  // 2048 i bytes further (whole 32-row steps keep the swizzle) and its scale word 128 i further,
+  // so per stage only the slot offsets change and every read takes a constant offset.
+  const uint32_t rd_a0 = lds0 + T::A_OFF + swz(tr0 + r32, g), rd_a1 = lds0 + T::A_OFF + swz(tr0 + r32, 2 + g);
+  const uint32_t rd_b0 = lds0 + T::B_OFF + swz(tc0 + r32, g), rd_b1 = lds0 + T::B_OFF + swz(tc0 + r32, 2 + g);
+  const uint32_t rd_sa = lds0 + T::SC_OFF + (tr0 + r32) * 4 + g;
+  const uint32_t rd_sb = lds0 + T::SC_OFF + T::NW * 256 + (tc0 + r32) * 4 + g;
+  struct ReadBase { uint32_t a0, a1, b0, b1, sa, sb; };
+  auto read_base = [&](int kt) {  // addresses of stage kt's slots
+    const uint32_t so = (uint32_t)(kt % T::S) * T::STAGE;
+    const uint32_t sc = (uint32_t)((kt >> 1) % T::NSC) * T::SC_SLOT;
+    return ReadBase{rd_a0 + so, rd_a1 + so, rd_b0 + so, rd_b1 + so, rd_sa + sc, rd_sb + sc};
+  };
+  auto read_one = [&](int r, const ReadBase& rb, auto par) {
     constexpr int B = decltype(par)::value;  // kt % 2
-    const uint8_t* base = smem + (kt % T::S) * T::STAGE;
-    const uint8_t* sbase = smem + T::SC_OFF + ((kt >> 1) % T::NSC) * T::SC_SLOT;
     if (r < 2 * T::FM) {
       const int i = r >> 1, hi = r & 1;
-      const uint4 v = *reinterpret_cast<const uint4*>(base + T::A_OFF + swz(tr0 + i * 32 + r32, 2 * hi + g));
+      const u32x4_t v = lds16_at(hi ? rb.a1 : rb.a0)[i * 128];
       fa[B][i][4 * hi] = (int)v.x; fa[B][i][4 * hi + 1] = (int)v.y;
       fa[B][i][4 * hi + 2] = (int)v.z; fa[B][i][4 * hi + 3] = (int)v.w;
     } else if (r < 2 * (T::FM + T::FN)) {
       const int j = (r - 2 * T::FM) >> 1, hi = r & 1;
-      const uint4 v = *reinterpret_cast<const uint4*>(base + T::B_OFF + swz(tc0 + j * 32 + r32, 2 * hi + g));
+      const u32x4_t v = lds16_at(hi ? rb.b1 : rb.b0)[j * 128];
       fb[B][j][4 * hi] = (int)v.x; fb[B][j][4 * hi + 1] = (int)v.y;
       fb[B][j][4 * hi + 2] = (int)v.z; fb[B][j][4 * hi + 3] = (int)v.w;
     } else if (r < 2 * (T::FM + T::FN) + T::FM) {
       const int i = r - 2 * (T::FM + T::FN);
-      sa[B][i] = sbase[(tr0 + i * 32 + r32) * 4 + 2 * B + g];
+      sa[B][i] = lds8_at(rb.sa)[i * 128 + 2 * B];
     } else {
       const int j = r - 2 * (T::FM + T::FN) - T::FM;
-      sb[B][j] = sbase[T::NW * 256 + (tc0 + j * 32 + r32) * 4 + 2 * B + g];
+      sb[B][j] = lds8_at(rb.sb)[j * 128 + 2 * B];
     }
   };
 
@@ -332,8 +367,9 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
     }
     wait_vmcnt<2 * T::LO + T::L>();  // stage 0 landed; stages 1 - 3 may be in flight
     __syncthreads();
+    const ReadBase rb0 = read_base(0);
 #pragma unroll
-    for (int r = 0; r < NR; ++r) read_one(r, 0, I0());
+    for (int r = 0; r < NR; ++r) read_one(r, rb0, I0());
   }
   // step kt (P = kt % 2); MORE: stage kt+1 exists; LOAD: load stage kt+4 (clamped)
   auto step = [&](int kt, auto par, auto more, auto load) {
@@ -343,6 +379,7 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
     if (MORE) wait_vmcnt<T::L + T::LO>();  // stage kt+1 landed; kt+2 and kt+3 may be in flight
     __syncthreads();
     const int ks = kt + 4 < KT ? kt + 4 : KT - 1;
+    const ReadBase rb = read_base(kt + 1);
 #pragma unroll
     for (int m = 0; m < NMF; ++m) {
       const int i = m / T::FN, j = m % T::FN;
@@ -355,7 +392,7 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
       if (MORE) {
 #pragma unroll
         for (int r = m * NR / NMF; r < (m + 1) * NR / NMF; ++r)
-          read_one(r, kt + 1, std::integral_constant<int, 1 - P>());
+          read_one(r, rb, std::integral_constant<int, 1 - P>());
       }
       if (LOAD && m < LL) issue_one(m, ks, kt + 4);
       __builtin_amdgcn_sched_barrier(0);
@@ -509,7 +546,7 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           *reinterpret_cast<uint32_t*>(qT + hcl * QP + rl + 8 * k) = cvt4(hw[2 * k], hw[2 * k + 1], s);
-        if (g == 0) sT[hcl * SG + (tr0 >> 5) + i] = (uint8_t)s.byte;
+        sT[hcl * SG + (tr0 >> 5) + i] = (uint8_t)s.byte;  // lanes l and l ^ 32 write the same byte
 #pragma unroll
         for (int t = 0; t < 8; ++t)
           *reinterpret_cast<uint32_t*>(hR + (rl + 8 * (t >> 1) + 2 * (t & 1)) * HP + hcl + pr_off) =
@@ -538,7 +575,8 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
       *reinterpret_cast<uint4*>(p.q_r + (hcol >> 6) * 64 * M + row * 64 + (hcol & 63)) =
           make_uint4(cvt4(v[0], v[1], s), cvt4(v[2], v[3], s), cvt4(v[4], v[5], s), cvt4(v[6], v[7], s));
       const int64_t grp = hcol >> 5;
-      if (!(c & 1)) p.s_r[row * p.sr_rs + (grp >> 2) * p.sr_kbs + (grp & 3)] = (uint8_t)s.byte;
+      // lanes 2c and 2c + 1 hold the same group and write the same byte (no branch)
+      p.s_r[row * p.sr_rs + (grp >> 2) * p.sr_kbs + (grp & 3)] = (uint8_t)s.byte;
     }
     // column-wise codes (hq_c [F, mcap], 64-token panels): four lanes per column and panel,
     // consecutive columns on consecutive lane quads (contiguous kilobytes)
@@ -647,7 +685,7 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
 #pragma unroll
             for (int k = 0; k < 4; ++k)
               *reinterpret_cast<uint32_t*>(qT + pcl * QP + rl + 8 * k) = cvt4(w[2 * k], w[2 * k + 1], s);
-            if (g == 0) sT[pcl * SG + wm * FH + ii] = (uint8_t)s.byte;
+            sT[pcl * SG + wm * FH + ii] = (uint8_t)s.byte;  // lanes l and l ^ 32 write the same byte
 #pragma unroll
             for (int t = 0; t < 8; ++t)
               *reinterpret_cast<uint32_t*>(dR + (rl + 8 * (t >> 1) + 2 * (t & 1)) * DP + pcl + pr_off) =
@@ -674,7 +712,7 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
         *reinterpret_cast<uint4*>(p.q_r + (pcol >> 6) * 64 * p.mcap + row * 64 + (pcol & 63)) =
             make_uint4(cvt4(v[0], v[1], s), cvt4(v[2], v[3], s), cvt4(v[4], v[5], s), cvt4(v[6], v[7], s));
         const int64_t grp = pcol >> 5;
-        if (!(c & 1)) p.s_r[row * p.sr_rs + (grp >> 2) * p.sr_kbs + (grp & 3)] = (uint8_t)s.byte;
+        p.s_r[row * p.sr_rs + (grp >> 2) * p.sr_kbs + (grp & 3)] = (uint8_t)s.byte;  // as above: no branch
       }
       // dhq_c [2F, mcap] in 64-token panels: a pass's RH consecutive block rows lie in one
       // panel (RH = 64) or half of one (RH = 32); G lanes cover a column's run of them,
