@@ -190,12 +190,16 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
   // column-wise and keep the normal layout.
   constexpr bool TRACC = (EPI == EPI_STORE || EPI == EPI_UNPACK13);
   v16f acc[T::FM][T::FN];
+  // zeroed after the first loads are issued (a few hundred cycles that then overlap their latency)
+  auto zero_acc = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int i = 0; i < T::FM; ++i)
+    for (int i = 0; i < T::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < T::FN; ++j)
+      for (int j = 0; j < T::FN; ++j)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+  };
 
   // Direct global->LDS loads: a wavefront's 1 KB load covers 16 consecutive tile rows (starting
   // at a multiple of 16) of one 64-k panel -- one contiguous kilobyte of the operand -- and
@@ -280,6 +284,7 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
 #pragma unroll
       for (int q = 0; q < T::LO; ++q) issue_one(q, 1, 1);
     }
+    zero_acc();
     auto step2 = [&](int kt, auto par) {
       constexpr int P = decltype(par)::value;
       wait_vmcnt<P ? T::L : T::LO>();  // stage kt landed; stage kt+1 (odd: LO loads) may be in flight
@@ -365,6 +370,9 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
 #pragma unroll
       for (int q = 0; q < ((st & 1) ? T::LO : T::L); ++q) issue_one(q, st < KT ? st : KT - 1, st);
     }
+  }
+  zero_acc();
+  if (KT > 0) {
     wait_vmcnt<2 * T::LO + T::L>();  // stage 0 landed; stages 1 - 3 may be in flight
     __syncthreads();
     const ReadBase rb0 = read_base(0);
@@ -778,42 +786,46 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_mx_kernel(GemmParams p
     // XCDs (block b runs on XCD b % 8), so raster position t is taken from a contiguous per-XCD
     // range, and positions go in groups of GM row tiles x all column tiles: the ~32 blocks an
     // XCD runs at once share a few A row panels and B column panels in that XCD's L2.
-    constexpr int GM = 4;
-    const int64_t mtu = ofs.mend / BM;
-    const int64_t ntiles = mtu * ntn;
-    int64_t nfull = ntiles, rem = 0;
-    int q = 1;
+    // 32-bit arithmetic throughout (tile counts stay below 2^31, which the launcher checks):
+    // 64-bit divisions by run-time values cost about a microsecond per block
+    constexpr uint32_t GM = 4;
+    const uint32_t mtu = (uint32_t)(ofs.mend / BM);
+    const uint32_t ntiles = mtu * (uint32_t)ntn;
+    uint32_t nfull = ntiles, rem = 0;
+    uint32_t qs = 0;  // log2 of the sub-tiles per tail tile
     if (SPLIT) {
-      const int64_t slots = (int64_t)p.ncu * OCC;  // blocks resident at once
+      const uint32_t slots = (uint32_t)p.ncu * OCC;  // blocks resident at once
       rem = ntiles % slots;
-      if (rem && TC::Q4 && 4 * rem <= slots) q = 4;
-      else if (rem && 2 * rem <= slots) q = 2;
-      if (q > 1) nfull = ntiles - rem;
+      if (rem && TC::Q4 && 4 * rem <= slots) qs = 2;
+      else if (rem && 2 * rem <= slots) qs = 1;
+      if (qs) nfull = ntiles - rem;
       else rem = 0;
     }
+    const uint32_t q = 1u << qs;
     // The sub-tile blocks take the lowest block ids (padded to whole rounds of the 8 XCDs):
     // they finish early and their CUs move on to whole tiles out of phase with the rest, which
     // spreads the epilogues' store bursts over time.
-    const int64_t nsub = (rem * q + 7) / 8 * 8;
-    const int64_t b = blockIdx.x;
+    const uint32_t nsub = (rem * q + 7) / 8 * 8;
+    const uint32_t b = blockIdx.x;
     const bool tail = b < nsub;  // a sub-tile of one of the last rem tiles (raster order)
-    int64_t t, part = 0;
+    uint32_t t, part = 0;
     if (!tail) {
-      const int64_t f = b - nsub;  // whole tile f; f % 8 is still the block's XCD
+      const uint32_t f = b - nsub;  // whole tile f; f % 8 is still the block's XCD
       if (f >= nfull) return;
-      const int64_t q8 = nfull / 8, r8 = nfull % 8, x8 = f % 8, s8 = f / 8;
+      const uint32_t q8 = nfull / 8, r8 = nfull % 8, x8 = f % 8, s8 = f / 8;
       t = x8 < r8 ? x8 * (q8 + 1) + s8 : r8 * (q8 + 1) + (x8 - r8) * q8 + s8;
     } else {
       if (b >= rem * q) return;
-      t = nfull + b / q;
-      part = b % q;
+      t = nfull + (b >> qs);
+      part = b & (q - 1);
     }
-    const int64_t grp = t / (GM * ntn);
-    const int64_t first = grp * GM;
-    const int64_t gsz = min((int64_t)GM, mtu - first);
-    const int64_t within = t - grp * GM * ntn;
-    m0 = (first + within % gsz) * BM;
-    n0 = (within / gsz) * BN;
+    const uint32_t gstride = GM * (uint32_t)ntn;
+    const uint32_t grp = t / gstride;
+    const uint32_t first = grp * GM;
+    const uint32_t gsz = min(GM, mtu - first);
+    const uint32_t within = t - grp * gstride;
+    m0 = (int64_t)(first + within % gsz) * BM;
+    n0 = (int64_t)(within / gsz) * BN;
     kbeg = 0;
     kend = p.K;
     if constexpr (SPLIT) {
@@ -860,24 +872,25 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_mx_kernel(GemmParams p
       order[rank] = i;
     }
     __syncthreads();
-    const int mtn = (int)(p.M / BM);
-    const int64_t per = (int64_t)mtn * ntn;
-    const int64_t t = blockIdx.x;
+    // 32-bit arithmetic (as in the M-grouped order)
+    const uint32_t mtn = (uint32_t)(p.M / BM);
+    const uint32_t per = mtn * (uint32_t)ntn;
+    const uint32_t t = blockIdx.x;
     e = order[t / per];
-    const int64_t l = t % per;
-    const int64_t q8 = per / 8, r8 = per % 8, x8 = l % 8, s8 = l / 8;
-    const int64_t pos = (x8 < r8 ? x8 * (q8 + 1) : r8 * (q8 + 1) + (x8 - r8) * q8) + s8;
+    const uint32_t l = t % per;
+    const uint32_t q8 = per / 8, r8 = per % 8, x8 = l % 8, s8 = l / 8;
+    const uint32_t pos = (x8 < r8 ? x8 * (q8 + 1) : r8 * (q8 + 1) + (x8 - r8) * q8) + s8;
     // strips of width W across the smaller grid dimension; the longer one runs inside a strip
-    const bool mlong = mtn >= ntn;
-    const int64_t nlong = mlong ? mtn : ntn, nshort = mlong ? ntn : mtn;
-    constexpr int W = 4;
-    const int64_t nstrip = (nshort + W - 1) / W;
-    const int64_t strip = min(pos / (W * nlong), nstrip - 1);
-    const int64_t sw = min((int64_t)W, nshort - strip * W);  // width of this strip
-    const int64_t within = pos - strip * W * nlong;
-    const int64_t il = within / sw, is = strip * W + within % sw;
-    m0 = (mlong ? il : is) * BM;
-    n0 = (mlong ? is : il) * BN;
+    const bool mlong = mtn >= (uint32_t)ntn;
+    const uint32_t nlong = mlong ? mtn : ntn, nshort = mlong ? ntn : mtn;
+    constexpr uint32_t W = 4;
+    const uint32_t nstrip = (nshort + W - 1) / W;
+    const uint32_t strip = min(pos / (W * nlong), nstrip - 1);
+    const uint32_t sw = min(W, nshort - strip * W);  // width of this strip
+    const uint32_t within = pos - strip * W * nlong;
+    const uint32_t il = within / sw, is = strip * W + within % sw;
+    m0 = (int64_t)(mlong ? il : is) * BM;
+    n0 = (int64_t)(mlong ? is : il) * BN;
     kbeg = p.offs[e];
     kend = kbeg + ksp[e];
     __syncthreads();  // the LDS scratch is reused by the main loop
