@@ -35,7 +35,8 @@
 //     and multiplies by expert e's B. Tiles at or past offs[E] exit. BM divides
 //     pad_multiple, so no tile straddles two experts. Tiles are ordered per XCD for L2
 //     reuse, and the last (T mod #CU) tiles are split into sub-tiles (see TailCfg).
-//   K-grouped (both wgrads): one tile grid per expert, experts longest-K first; K runs over
+//   K-grouped (both wgrads): one tile grid per expert, experts longest-K first (index order
+//     from 64 experts on); K runs over
 //     the expert's token segment (the real rows rounded up to 128; pad rows are zero codes).
 //     A zero-token expert runs no K step and stores zeros.
 #include <atomic>
@@ -774,8 +775,51 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_mx_kernel(GemmParams p
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDSZ];
 
   const int tid = threadIdx.x;
-  const Offsets ofs = read_offsets(p.offs, p.counts, p.E, p.pad, p.mcap);
-  if (!ofs.ok) return;
+  // Token offsets (validated on the device; a violation leaves every output untouched). E < 64:
+  // one wavefront's lanes hold them (one round of loads; row lookups by ballot). E >= 64: the
+  // block copies offs and counts into LDS in one round of coalesced loads, checks them in
+  // parallel and looks rows up in LDS (the wavefront helpers would loop over E with a load per
+  // step and binary-search global memory). The copy sits after the K-grouped scratch (2E ints).
+  const bool big_e = p.E >= 64;
+  int32_t* olds = reinterpret_cast<int32_t*>(smem) + 2 * p.E;  // offs [0, E], counts [E + 1, 2E]
+  Offsets ofs = {};
+  int64_t mend;
+  if (!big_e) {
+    ofs = read_offsets(p.offs, p.counts, p.E, p.pad, p.mcap);
+    if (!ofs.ok) return;
+    mend = ofs.mend;
+  } else {
+    for (int i = tid; i <= p.E; i += T::NT) olds[i] = p.offs[i];
+    if (p.counts)
+      for (int i = tid; i < p.E; i += T::NT) olds[p.E + 1 + i] = p.counts[i];
+    __syncthreads();
+    bool bad = false;
+    for (int i = tid; i <= p.E; i += T::NT) {
+      const int32_t o = olds[i];
+      if (o % p.pad != 0 || o < 0 || (int64_t)o > p.mcap) bad = true;
+      if (i == 0 && o != 0) bad = true;
+      if (i > 0) {
+        const int32_t pr = olds[i - 1];
+        if (o < pr) bad = true;
+        if (p.counts) {
+          const int32_t c = olds[p.E + i];  // counts[i - 1]
+          if (c < 0 || c > o - pr) bad = true;
+        }
+      }
+    }
+    if (__syncthreads_or(bad)) return;
+    mend = olds[p.E];
+  }
+  // expert that owns row m (offs[e] <= m < offs[e + 1]; requires m < offs[E])
+  auto expert_of = [&](int64_t m) -> int {
+    if (!big_e) return ofs.expert(m);
+    int lo = 0, hi = p.E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if ((int64_t)olds[mid] <= m) lo = mid; else hi = mid;
+    }
+    return lo;
+  };
 
   int e;
   int64_t m0, n0, kbeg, kend;
@@ -789,7 +833,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_mx_kernel(GemmParams p
     // 32-bit arithmetic throughout (tile counts stay below 2^31, which the launcher checks):
     // 64-bit divisions by run-time values cost about a microsecond per block
     constexpr uint32_t GM = 4;
-    const uint32_t mtu = (uint32_t)(ofs.mend / BM);
+    const uint32_t mtu = (uint32_t)(mend / BM);
     const uint32_t ntiles = mtu * (uint32_t)ntn;
     uint32_t nfull = ntiles, rem = 0;
     uint32_t qs = 0;  // log2 of the sub-tiles per tail tile
@@ -833,7 +877,8 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_mx_kernel(GemmParams p
         if (tail && q == 4) {
           m0 += (part >> 1) * TC::BM4;
           n0 += (part & 1) * TC::BN4;
-          e = ofs.expert(m0);
+          e = expert_of(m0);
+          if (big_e) __syncthreads();  // the LDS copy of the offsets is reused by the main loop
           tile_run<TC::BM4, TC::BN4, WM, WN, SCHED, EPI, OCC>(p, smem, e, m0, n0, kbeg, kend);
           return;
         }
@@ -841,42 +886,58 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_mx_kernel(GemmParams p
       if (tail && q == 2) {
         if (TC::BM2 == BM) n0 += part * TC::BN2;
         else m0 += part * TC::BM2;
-        e = ofs.expert(m0);
+        e = expert_of(m0);
+        if (big_e) __syncthreads();
         tile_run<TC::BM2, TC::BN2, WM, WN, SCHED, EPI, OCC>(p, smem, e, m0, n0, kbeg, kend);
         return;
       }
     }
-    e = ofs.expert(m0);
+    e = expert_of(m0);
+    if (big_e) __syncthreads();
   } else {
-    // Experts are taken longest-K first (their tiles start earliest, which shortens the tail).
+    // Experts are taken longest-K first (their tiles start earliest, which shortens the tail;
+    // with 64 or more experts in index order, see below).
     // Within an expert every tile streams the whole K range, so what matters is how many A
     // row panels and B column panels each XCD's L2 must hold: block l of the expert runs on
     // XCD l % 8, each XCD takes a contiguous run of positions, and positions walk the tile
     // grid in strips 4 tiles wide across the smaller dimension, so a run covers a compact
     // patch (for 11 x 8 tiles: 60 panel streams in all instead of 96 for whole rows).
-    int* ksp = reinterpret_cast<int*>(smem);  // per-expert K span, then the order (LDS scratch)
-    int* order = ksp + p.E;
-    for (int i = tid; i < p.E; i += T::NT) {
-      const int seg = p.offs[i + 1] - p.offs[i];
-      const int real = p.counts ? p.counts[i] : seg;
-      ksp[i] = min(seg, (real + 127) / 128 * 128);
-    }
-    __syncthreads();
-    for (int i = tid; i < p.E; i += T::NT) {
-      const int ki = ksp[i];
-      int rank = 0;
-      for (int j = 0; j < p.E; ++j) {
-        const int kj = ksp[j];
-        rank += (kj > ki) || (kj == ki && j < i);
-      }
-      order[rank] = i;
-    }
-    __syncthreads();
     // 32-bit arithmetic (as in the M-grouped order)
     const uint32_t mtn = (uint32_t)(p.M / BM);
     const uint32_t per = mtn * (uint32_t)ntn;
     const uint32_t t = blockIdx.x;
-    e = order[t / per];
+    int ke;  // K span of expert e: its real rows rounded up to 128, within its segment
+    if (!big_e) {
+      int* ksp = reinterpret_cast<int*>(smem);  // per-expert K span, then the order (LDS scratch)
+      int* order = ksp + p.E;
+      for (int i = tid; i < p.E; i += T::NT) {
+        const int seg = p.offs[i + 1] - p.offs[i];
+        const int real = p.counts ? p.counts[i] : seg;
+        ksp[i] = min(seg, (real + 127) / 128 * 128);
+      }
+      __syncthreads();
+      for (int i = tid; i < p.E; i += T::NT) {
+        const int ki = ksp[i];
+        int rank = 0;
+        for (int j = 0; j < p.E; ++j) {
+          const int kj = ksp[j];
+          rank += (kj > ki) || (kj == ki && j < i);
+        }
+        order[rank] = i;
+      }
+      __syncthreads();
+      e = order[t / per];
+      ke = ksp[e];
+      kbeg = p.offs[e];
+    } else {
+      // many experts: index order (the rank sort costs O(E^2 / threads) per block, and the
+      // longest-first order matters less when each expert is a small share of the work)
+      e = (int)(t / per);
+      const int seg = olds[e + 1] - olds[e];
+      const int real = p.counts ? olds[p.E + 1 + e] : seg;
+      ke = min(seg, (real + 127) / 128 * 128);
+      kbeg = olds[e];
+    }
     const uint32_t l = t % per;
     const uint32_t q8 = per / 8, r8 = per % 8, x8 = l % 8, s8 = l / 8;
     const uint32_t pos = (x8 < r8 ? x8 * (q8 + 1) : r8 * (q8 + 1) + (x8 - r8) * q8) + s8;
@@ -891,8 +952,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_mx_kernel(GemmParams p
     const uint32_t il = within / sw, is = strip * W + within % sw;
     m0 = (int64_t)(mlong ? il : is) * BM;
     n0 = (int64_t)(mlong ? is : il) * BN;
-    kbeg = p.offs[e];
-    kend = kbeg + ksp[e];
+    kend = kbeg + ke;
     __syncthreads();  // the LDS scratch is reused by the main loop
   }
   tile_run<BM, BN, WM, WN, SCHED, EPI, OCC>(p, smem, e, m0, n0, kbeg, kend);
