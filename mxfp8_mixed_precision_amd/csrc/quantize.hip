@@ -93,12 +93,13 @@ __device__ __forceinline__ void quant_tile(const QuantParams& p, int64_t bx, int
     // and a column's spans 8 row bands. Block L runs on XCD L % 8; each XCD takes whole
     // macro-tiles of 8 bands x 8 column tiles, so every sector is filled inside one XCD's L2
     // (split over XCDs, each L2 writes its few bytes back as a partial sector).
-    const int64_t L = bx, x = L & 7, sq = L >> 3;
-    const int64_t m = x + 8 * (sq >> 6);         // macro-tile of the XCD's sq-th block
-    const int64_t w = sq & 63;                   // tile within it, band-major
-    const int64_t mcols = (p.cols + 1023) >> 10;  // macro-tiles across
-    row0 = ((m / mcols) * 8 + (w >> 3)) * 128;
-    col0 = ((m % mcols) * 8 + (w & 7)) * 128;
+    const uint32_t L = (uint32_t)bx, x = L & 7, sq = L >> 3;  // 32-bit: tiles < 2^31
+    const uint32_t m = x + 8 * (sq >> 6);                    // macro-tile of the XCD's sq-th block
+    const uint32_t w = sq & 63;                              // tile within it, band-major
+    const uint32_t mcols = (uint32_t)((p.cols + 1023) >> 10);  // macro-tiles across
+    const uint32_t mr = m / mcols;
+    row0 = (int64_t)(mr * 8 + (w >> 3)) * 128;
+    col0 = (int64_t)((m - mr * mcols) * 8 + (w & 7)) * 128;
   }
   const int64_t col = col0 + c * 8;
   const int64_t rw0 = row0 + w * 32;  // first row of this wavefront
@@ -314,11 +315,15 @@ struct QuantFwd {
 };
 __global__ __launch_bounds__(256) void quant_fwd_kernel(QuantFwd f) {
   __shared__ __attribute__((aligned(16))) QuantLds L;
-  int64_t b = blockIdx.x;
-  auto split = [](int64_t i, const QGrid& g, int64_t& bx, int64_t& by, int64_t& bz) {
-    bx = i % g.x;
-    by = (i / g.x) % g.y;
-    bz = i / (g.x * g.y);
+  uint32_t b = blockIdx.x;
+  // 32-bit arithmetic (block counts stay below 2^31; 64-bit divisions by run-time values are
+  // long scalar sequences)
+  auto split = [](uint32_t i, const QGrid& g, int64_t& bx, int64_t& by, int64_t& bz) {
+    const uint32_t gx = (uint32_t)g.x, gy = (uint32_t)g.y;
+    const uint32_t q = i / gx;
+    bx = i - q * gx;
+    by = q % gy;
+    bz = q / gy;
   };
   int64_t bx, by, bz;
   if (b < f.n13) {
