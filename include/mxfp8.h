@@ -168,9 +168,9 @@ typedef struct {
  * MXF_T_H13 (the BF16-rounded FC1 output g | u, kept for the backward pass) is row-major
  * [Mcap, 2F] in packed order under MXF_UNFUSED; otherwise it is stored fragment-tiled, in the order the matrix-core accumulators produce and consume it: records
  * of 2048 BF16 values, record R * (F/32) + J holding rows 32R .. 32R+31 and h columns
- * 32J .. 32J+31; inside a record, index ((s * 64) + c + 32 b) * 16 + 4 k + j (s = 0 gate,
- * 1 up; b < 2, c < 32, k < 4, j < 4) holds row 32R + 8k + 4b + j, column 32J + c of the
- * gate (s = 0) or up (s = 1) projection. Same size as [Mcap, 2F].
+ * 32J .. 32J+31; inside a record, index ((2 s + (k >> 1)) * 64 + c + 32 b) * 8 + 4 (k & 1) + j
+ * (s = 0 gate, 1 up; b < 2, c < 32, k < 4, j < 4) holds row 32R + 8k + 4b + j, column 32J + c
+ * of the gate (s = 0) or up (s = 1) projection. Same size as [Mcap, 2F].
  *
  * Every code tensor below (…Q_R, …Q_C; the shapes listed are [R, K], per expert for the
  * weights, K the axis the 32-groups run along) is stored in 64-k panels, the order the GEMM

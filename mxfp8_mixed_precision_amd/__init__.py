@@ -64,12 +64,12 @@ def h13_rowmajor(tiled, F):
 
     Stored order: 4096-byte records, record (R, J) = rows 32R..32R+31 x h columns
     32J..32J+31, at record index R * (F/32) + J; inside a record, element
-    (s, b, c, k, j) -- s = 0 gate / 1 up, lane c + 32b, slot 4k + j -- is row
-    32R + 8k + 4b + j, packed column 64J + 32s + c.
+    (s, kh, b, c, kl, j) -- s = 0 gate / 1 up, lane c + 32b, slot 4k + j with
+    k = 2 kh + kl -- is row 32R + 8k + 4b + j, packed column 64J + 32s + c.
     """
-    t = tiled.reshape(-1, F // 32, 2, 2, 32, 4, 4)     # R, J, s, b, c, k, j
+    t = tiled.reshape(-1, F // 32, 2, 2, 2, 32, 2, 4)     # R, J, s, kh, b, c, kl, j
     M = t.shape[0] * 32
-    return t.permute(0, 5, 3, 6, 1, 2, 4).reshape(M, 2 * F)  # R, k, b, j | J, s, c
+    return t.permute(0, 3, 6, 4, 7, 1, 2, 5).reshape(M, 2 * F)  # R, kh, kl, b, j | J, s, c
 
 
 class MlpContext:

@@ -498,7 +498,7 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
     // N = 2F (packed gate/up columns): fragment pair (2c, 2c+1) of a wavefront holds the gate
     // and up columns of the same 32 h columns, in the same accumulator slots. Per pair:
     //  * g, u are rounded to BF16 and saved (for the backward pass) as one 4 KB record in
-    //    accumulator order: two 2 KB coalesced stores, no staging;
+    //    accumulator order: four contiguous-kilobyte stores, no staging;
     //  * h = BF16(silu(g) * u); its column-wise groups (32 rows of one column: this lane's 16
     //    slots plus lane l^32's) are quantized in registers and the codes staged, transposed,
     //    in LDS; h itself is staged row-major for the row-wise groups.
@@ -542,12 +542,14 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
           hw[t] = swiglu_h2(gw[t], uw[t]);
         }
         const int64_t rec = ((wrow0 + i * 32) >> 5) * (F >> 5) + ((hc0 + tc0 / 2 + jp * 32) >> 5);
-        uint4* dg = reinterpret_cast<uint4*>(p.h13 + rec * 2048) + 2 * lane;
+        // record layout: four 1 KB runs (gate slots 0-7, gate 8-15, up 0-7, up 8-15), lane l's
+        // 16 bytes at 16 l in each, so every store is one contiguous kilobyte
+        uint4* dg = reinterpret_cast<uint4*>(p.h13 + rec * 2048) + lane;
         // saved for the backward pass: non-temporal (keeps the L2 for the GEMM operands)
         store16_nt(dg, make_uint4(gw[0], gw[1], gw[2], gw[3]));
-        store16_nt(dg + 1, make_uint4(gw[4], gw[5], gw[6], gw[7]));
+        store16_nt(dg + 64, make_uint4(gw[4], gw[5], gw[6], gw[7]));
         store16_nt(dg + 128, make_uint4(uw[0], uw[1], uw[2], uw[3]));
-        store16_nt(dg + 129, make_uint4(uw[4], uw[5], uw[6], uw[7]));
+        store16_nt(dg + 192, make_uint4(uw[4], uw[5], uw[6], uw[7]));
         uint32_t am = amax16(hw);
         am = max(am, (uint32_t)__shfl_xor((int)am, 32));
         const Scale s = scale_from_amax(am);
@@ -648,11 +650,11 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
     auto load_gu = [&](int f) {
       const int i = f / T::FN, j = f % T::FN, slot = f % GR;
       const int64_t rec = ((wrow0 + i * 32) >> 5) * (F >> 5) + ((wcol0 + j * 32) >> 5);
-      const uint4* src = reinterpret_cast<const uint4*>(p.h13 + rec * 2048) + 2 * lane;
+      const uint4* src = reinterpret_cast<const uint4*>(p.h13 + rec * 2048) + lane;  // as written
       gs[slot][0] = load16_nt(src);  // read once: non-temporal
-      gs[slot][1] = load16_nt(src + 1);
+      gs[slot][1] = load16_nt(src + 64);
       us[slot][0] = load16_nt(src + 128);
-      us[slot][1] = load16_nt(src + 129);
+      us[slot][1] = load16_nt(src + 192);
     };
 #pragma unroll
     for (int f = 0; f < GR - 1 && f < NF; ++f) load_gu(f);

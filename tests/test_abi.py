@@ -175,7 +175,8 @@ def test_h13_untile_matches_documented_order():
                             for j in range(4):
                                 row = 32 * R + 8 * k + 4 * b + j
                                 col = 64 * J + 32 * s + c
-                                tiled[base + (s * 64 + c + 32 * b) * 16 + 4 * k + j] = row * 100000 + col
+                                tiled[base + ((2 * s + (k >> 1)) * 64 + c + 32 * b) * 8 + 4 * (k & 1) + j] = \
+                                    row * 100000 + col
     rm = mx.h13_rowmajor(tiled, F)
     want = torch.arange(M)[:, None] * 100000 + torch.arange(2 * F)[None, :]
     assert torch.equal(rm, want)
