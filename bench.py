@@ -325,13 +325,31 @@ def bench_quantize(mx, torch, dev, args):
         dst.copy_(xs[i])
     cp_s = loop_seconds(torch, n, lambda i: dst.copy_(xs[i % 3]))
     cp_gbs = 2 * xs[0].numel() * 2 / cp_s / 1e9
-    del dst
+    # the library's HBM ceiling kernels on the same bytes: a pure read of the input, a pure
+    # write of as many bytes, and a copy (read + write) -- the fastest access patterns measured
+    # on this chip, against which the quantizer's read + write traffic is reported
+    nb = xs[0].numel() * 2
+    xor = torch.zeros(16, dtype=torch.uint8, device=dev)
+    ceil = {}
+    for name, mode, src, traffic in (("read", mx.HBM_READ, lambda i: xs[i % 3], nb),
+                                     ("write", mx.HBM_WRITE, lambda i: None, nb),
+                                     ("copy", mx.HBM_COPY, lambda i: xs[i % 3], 2 * nb)):
+        out = xor if mode == mx.HBM_READ else dst
+        for i in range(3):
+            mx.hbm_probe(mode, src(i), out, nb)
+        t = loop_seconds(torch, n, lambda i: mx.hbm_probe(mode, src(i), out, nb))
+        ceil[name] = {"value": round(traffic / t / 1e9, 1), "unit": "GB/s", "avg_us": round(t * 1e6, 2)}
+    del dst, xor
     return {"workload": f"quant: BF16 [{rows}, {cols}] dual (row-wise + column-wise) MXFP8", "value": round(gbs, 1),
             "unit": "GB/s", "avg_us": round(avg_s * 1e6, 2),
             "e5m2": {"value": round(nbytes / avg5 / 1e9, 1), "unit": "GB/s", "avg_us": round(avg5 * 1e6, 2)},
             "copy_ceiling": {"value": round(cp_gbs, 1), "unit": "GB/s", "avg_us": round(cp_s * 1e6, 2),
                              "kernel": f"device copy of BF16 [{rows}, {cols}] (read + write)",
                              "frac_of_copy": round(gbs / cp_gbs, 4)},
+            "hbm_ceilings": dict(ceil, kernel=f"library HBM probe kernels (mxf_hbm_probe) on {nb} bytes: read, "
+                                               "write, copy (read + write)",
+                                 frac_of_copy=round(gbs / ceil["copy"]["value"], 4),
+                                 copy_frac_of_peak=round(ceil["copy"]["value"] / PEAK_HBM_GBS, 4)),
             "roofline": {"bound": "hbm", "kernel": "quantize", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": traffic_for("quantize", "quant")}}

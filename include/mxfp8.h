@@ -325,7 +325,7 @@ mxf_status mxf_read_status(const void* workspace, void* stream, int32_t* device_
  * Kernel names: quant_fwd (W13, W2 and X quantized in one launch), fc1_swiglu, fc2, quant_dy,
  * fc2_dgrad_dswiglu,
  * fc2_wgrad, fc1_dgrad, fc1_wgrad (MXF_UNFUSED: fc1, swiglu_quant, fc2_dgrad, dswiglu_quant),
- * quantize, dequantize, route_plan, permute, dispatch_quant_x.
+ * quantize, dequantize, route_plan, permute, dispatch_quant_x, hbm_read, hbm_write, hbm_copy.
  * Errors: MXF_E_ARG (capacity < 1 or > 1<<20, or end without begin), MXF_E_NULL, MXF_E_HIP. */
 typedef struct {
   char name[32];
@@ -334,6 +334,19 @@ typedef struct {
 } mxf_kernel_time;
 mxf_status mxf_profile_begin(int32_t capacity);
 mxf_status mxf_profile_end(mxf_kernel_time* out /* host */, int32_t max_out, int32_t* n_out /* host */);
+
+/* HBM ceiling kernels (measurement): the read, write and copy rates the device sustains with
+ * the access pattern that reaches them (16-byte lanes, one contiguous kilobyte per wavefront
+ * instruction, grid-stride over the buffer). The HBM-bound kernels of the library are reported
+ * against these rates as well as against the data-sheet bandwidth. Device buffers, 16-byte
+ * aligned; bytes a positive multiple of 16 (at most 2^40).
+ *   mode 0 (read):  every 16-byte word of src is read once; dst[0..15] (caller-owned, 16
+ *                   bytes) is XORed with the XOR of all of them (zero it first).
+ *   mode 1 (write): 16-byte word i of dst becomes four copies of the low 32 bits of i; src unused.
+ *   mode 2 (copy):  dst = src (bytes each; the buffers must not overlap).
+ * Errors: MXF_E_ARG (mode), MXF_E_SHAPE (bytes), MXF_E_NULL, MXF_E_ALIGN, MXF_E_DEVICE,
+ * MXF_E_HIP. Timed under the profiling name hbm_read / hbm_write / hbm_copy. */
+mxf_status mxf_hbm_probe(int32_t mode, const void* src, void* dst, int64_t bytes, void* stream);
 
 /* Test helpers for the [E, 2F, D] 32-block packing: w13[e, 64j+i] = w1[e, 32j+i] and
  * w13[e, 64j+32+i] = w3[e, 32j+i] (i < 32), BF16, and its inverse. F % 32 == 0. */

@@ -717,6 +717,25 @@ static mxf_status pack_common(const void* a, const void* b, const void* c, int32
   return check_device();
 }
 
+mxf_status mxf_hbm_probe(int32_t mode, const void* src, void* dst, int64_t bytes, void* stream) {
+  g_err.clear();
+  if (mode < 0 || mode > 2) return fail(MXF_E_ARG, "mode = %d: must be 0 (read), 1 (write) or 2 (copy)", mode);
+  if (bytes <= 0 || bytes % 16 != 0 || bytes > ((int64_t)1 << 40))
+    return fail(MXF_E_SHAPE, "bytes = %lld: must be a positive multiple of 16, at most 2^40", (long long)bytes);
+  if ((mode != 1 && !src) || !dst) return fail(MXF_E_NULL, "src or dst is NULL");
+  if ((mode != 1 && !aligned16(src)) || !aligned16(dst)) return fail(MXF_E_ALIGN, "src or dst is not 16-byte aligned");
+  mxf_status st = check_device();
+  if (st != MXF_OK) return st;
+  int dev = 0, ncu = 0;
+  MXF_HIP(hipGetDevice(&dev), "hipGetDevice");
+  MXF_HIP(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev), "CU count");
+  static const char* const names[3] = {"hbm_read", "hbm_write", "hbm_copy"};
+  MXF_HIP(timed(names[mode], (hipStream_t)stream,
+                [&] { return mxf_launch_hbm_probe(mode, src, dst, bytes, ncu, (hipStream_t)stream); }),
+          "HBM probe launch");
+  return MXF_OK;
+}
+
 mxf_status mxf_pack_w13(const void* w1, const void* w3, void* w13, int32_t E, int32_t F, int32_t D, void* stream) {
   g_err.clear();
   mxf_status s = pack_common(w1, w3, w13, E, F, D);

@@ -82,3 +82,5 @@ hipError_t mxf_launch_permute(const void* x, int64_t n_assign, int topk, int64_t
 // gemm.hip
 hipError_t mxf_launch_gemm_mgroup(int epi, const mxf::GemmParams& p, hipStream_t st);
 hipError_t mxf_launch_gemm_kgroup(int epi, const mxf::GemmParams& p, hipStream_t st);
+// hbm.hip
+hipError_t mxf_launch_hbm_probe(int mode, const void* src, void* dst, int64_t bytes, int ncu, hipStream_t st);

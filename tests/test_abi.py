@@ -287,3 +287,20 @@ def test_code_panels_match_documented_order():
         want = ((torch.arange(n)[:, None, None] * 1000 + torch.arange(R)[None, :, None]) * 1000
                 + torch.arange(K)[None, None, :]).reshape(*lead, R, K)
         assert torch.equal(rm, want)
+
+
+def test_hbm_probe_rejections_before_any_launch():
+    """Argument errors of mxf_hbm_probe are reported without touching a device."""
+    def st(mode, src, dst, nbytes):
+        with pytest.raises(mx.MxfError) as ei:
+            mx.hbm_probe(mode, src, dst, nbytes, stream=0)
+        return ei.value.status
+    assert st(3, 16, 16, 1024) == _abi.E_ARG          # unknown mode
+    assert st(-1, 16, 16, 1024) == _abi.E_ARG
+    assert st(2, 16, 16, 0) == _abi.E_SHAPE           # empty
+    assert st(2, 16, 16, 1000) == _abi.E_SHAPE        # not a multiple of 16
+    assert st(0, 16, 16, 1 << 41) == _abi.E_SHAPE     # over 2^40 bytes
+    assert st(0, None, 16, 1024) == _abi.E_NULL       # read needs src
+    assert st(1, None, None, 1024) == _abi.E_NULL     # write needs dst
+    assert st(2, 24, 16, 1024) == _abi.E_ALIGN        # src not 16-byte aligned
+    assert st(1, None, 8, 1024) == _abi.E_ALIGN       # dst not 16-byte aligned
