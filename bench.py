@@ -227,9 +227,11 @@ def main():
         fl = gemm_flops(name, m_real, D, F)
         if fl is not None:
             k["tflops"] = round(fl / (avg / 1e3) / 1e12, 1)
+            k["frac_of_peak"] = round(k["tflops"] / PEAK_FP8_TFLOPS, 4)
         by = quant_bytes(name, m_pad, m_real, E, D, F)
         if by is not None:
             k["gbs"] = round(by / (avg / 1e3) / 1e9, 1)
+            k["frac_of_peak"] = round(k["gbs"] / PEAK_HBM_GBS, 4)
         kernels[name] = k
     dom = max(prof.items(), key=lambda kv: kv[1][1])[0]
     dn, dtot = prof[dom]

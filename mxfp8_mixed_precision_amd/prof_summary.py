@@ -23,7 +23,8 @@ reports them while the sources are unchanged).
 
 Kernel dispatches are named by their position in a bench.py step: the MLP step enqueues, in
 order, quant_fwd (W13, W2 and X in one launch), fc1_swiglu, fc2, quant_dy, fc2_wgrad, fc2_dgrad_dswiglu,
-fc1_wgrad, fc1_dgrad; a --quant-only run launches `quantize` (the dual quantizer) and then
+fc1_wgrad, fc1_dgrad; a --quant-only run launches `quantize` (the dual quantizer), the HBM
+ceiling kernels `hbm_read`, `hbm_write`, `hbm_copy` on the quantizer's input bytes, and then
 `dequantize` (row-wise codes to BF16). Profile with
 `bench.py --serial` so that every kernel runs alone (durations not stretched by overlap).
 """
@@ -45,8 +46,11 @@ EXPECT = {
     "quant_dy": "quant_dual_kernel<1,", "fc1_swiglu": ", 0, 1, ", "fc2": ", 0, 0, ", "fc2_dgrad_dswiglu": ", 0, 2, ",
     "fc2_wgrad": ", 1, 0, ", "fc1_dgrad": ", 0, 0, ", "fc1_wgrad": ", 1, 3, ", "quantize": "quant_dual_kernel<0,true,true,0>",
     "dequantize": "dequant_kernel<true,0>",
+    "hbm_read": "hbm_read_kernel", "hbm_write": "hbm_write_kernel", "hbm_copy": "hbm_copy_kernel",
 }
-QUANT_ONLY = ["quantize", "dequantize"]
+# a --quant-only run: the dual quantizer, the dequantizer, then the HBM ceiling kernels timed
+# beside the quantizer (read, write, copy of the quantizer's input bytes)
+QUANT_ONLY = ["quantize", "dequantize", "hbm_read", "hbm_write", "hbm_copy"]
 COMPUTE_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_LDS_IDX_ACTIVE",
                     "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "TCC_HIT_sum", "TCC_MISS_sum"]
 SIMDS = 1024   # 256 compute units x 4 SIMDs
