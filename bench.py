@@ -331,7 +331,7 @@ def bench_quantize(mx, torch, dev, args):
     # write of as many bytes, and a copy (read + write) -- the fastest access patterns measured
     # on this chip, against which the quantizer's read + write traffic is reported
     nb = xs[0].numel() * 2
-    xor = torch.zeros(16, dtype=torch.uint8, device=dev)
+    xor = torch.zeros(1024, dtype=torch.uint8, device=dev)
     ceil = {}
     for name, mode, src, traffic in (("read", mx.HBM_READ, lambda i: xs[i % 3], nb),
                                      ("write", mx.HBM_WRITE, lambda i: None, nb),

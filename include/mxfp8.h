@@ -340,8 +340,9 @@ mxf_status mxf_profile_end(mxf_kernel_time* out /* host */, int32_t max_out, int
  * instruction, grid-stride over the buffer). The HBM-bound kernels of the library are reported
  * against these rates as well as against the data-sheet bandwidth. Device buffers, 16-byte
  * aligned; bytes a positive multiple of 16 (at most 2^40).
- *   mode 0 (read):  every 16-byte word of src is read once; dst[0..15] (caller-owned, 16
- *                   bytes) is XORed with the XOR of all of them (zero it first).
+ *   mode 0 (read):  every 16-byte word of src is read once; dst (caller-owned, 1024 bytes:
+ *                   64 slots of 16 bytes, zero them first) receives partial XORs, and the
+ *                   XOR of its 64 slots is the XOR of all of src's 16-byte words.
  *   mode 1 (write): 16-byte word i of dst becomes four copies of the low 32 bits of i; src unused.
  *   mode 2 (copy):  dst = src (bytes each; the buffers must not overlap).
  * Errors: MXF_E_ARG (mode), MXF_E_SHAPE (bytes), MXF_E_NULL, MXF_E_ALIGN, MXF_E_DEVICE,

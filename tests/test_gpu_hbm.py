@@ -18,10 +18,11 @@ def test_read_xor(nbytes):
     g = torch.Generator().manual_seed(nbytes)
     host = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g)
     src = host.cuda()
-    dst = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    dst = torch.zeros(1024, dtype=torch.uint8, device="cuda")
     mx.hbm_probe(mx.HBM_READ, src, dst, nbytes)
     want = np.bitwise_xor.reduce(host.numpy().view(np.uint32).reshape(-1, 4), axis=0)
-    assert np.array_equal(dst.cpu().numpy().view(np.uint32), want)
+    got = np.bitwise_xor.reduce(dst.cpu().numpy().view(np.uint32).reshape(64, 4), axis=0)
+    assert np.array_equal(got, want)
 
 
 @pytest.mark.parametrize("nbytes", SIZES)
