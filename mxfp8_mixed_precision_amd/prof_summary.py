@@ -244,15 +244,19 @@ def main():
                   "TCC_HIT / (TCC_HIT + TCC_MISS); LDS active and bank-conflict cycles per CU over the "
                   "kernel's active cycles.")
         md.append("")
-        md.append("| kernel | MFMA busy | F8 math TFLOP/launch | L2 hit | LDS active | LDS bank conflict | active cycles |")
-        md.append("|---|---|---|---|---|---|---|")
+        md.append("Clock = active cycles over the kernel's mean duration in the trace run: the shader clock the "
+                  "kernel ran at (2.4 GHz is the maximum; the MXFP8 peak scales with it, 5.0 PF at 2.4 GHz).")
+        md.append("")
+        md.append("| kernel | MFMA busy | F8 math TFLOP/launch | L2 hit | LDS active | LDS bank conflict | active cycles | clock GHz |")
+        md.append("|---|---|---|---|---|---|---|---|")
         for k in order:
             if k not in comp:
                 continue
             c = comp[k]
             hit = f"{c['l2_hit']:.3f}" if c["l2_hit"] is not None else "-"
+            ghz = f"{c['active_cycles'] / (sum(dur[k]) / len(dur[k])) / 1e3:.2f}" if k in dur else "-"
             md.append(f"| {k} | {c['mfma_busy']:.3f} | {c['f8_flop'] / 1e12:.4f} | {hit} | {c['lds_active']:.3f} | "
-                      f"{c['lds_bank_conflict']:.4f} | {c['active_cycles']:.0f} |")
+                      f"{c['lds_bank_conflict']:.4f} | {c['active_cycles']:.0f} | {ghz} |")
         md.append("")
     path = os.path.join(args.out, f"{name}_{args.workload}.md")
     with open(path, "w") as f:
