@@ -12,8 +12,9 @@
 //   * lane l: row octet s = l / 16 (rows 8s .. 8s+7 of the wavefront), column octet
 //     c = l % 16 (cols 8c .. 8c+7). Each lane loads 8 rows x 16 bytes: a wavefront load
 //     instruction covers 4 rows x 256 contiguous bytes;
-//   * a row-wise group (32 cols) is 4 adjacent lanes: amax by two DPP quad swaps; the lane
-//     writes its 8 codes (8 bytes; 16 lanes write one full 128-byte line per row);
+//   * a row-wise group (32 cols) is 4 adjacent lanes: amax by two DPP quad swaps; lanes 2t and
+//     2t+1 swap halves of rows j and j+1 so that each writes 16 codes of one row (16 bytes: a
+//     wavefront store covers 8 rows x 128 bytes, 512 contiguous bytes of a 64-k panel);
 //   * a column-wise group (32 rows) is the 4 lanes l, l^16, l^32, l^48: amax by two
 //     cross-lane swaps; each lane writes 8 contiguous codes per column (the 4 lanes, and
 //     the 4 wavefronts of the block, complete 128 contiguous bytes of every column).
@@ -184,22 +185,35 @@ __device__ __forceinline__ void quant_tile(const QuantParams& p, int64_t bx, int
 
   if (ROW) {
     uint8_t* q_r = p.q_r + e * p.qr_bs;
+    // rows j and j+1 in pairs: lanes 2t and 2t+1 (column octets c, c+1 of one 16-column run)
+    // swap halves, so the even lane stores row j's 16 codes of the run and the odd lane row
+    // j+1's: one 16-byte store per lane and row pair instead of two 8-byte stores
+    const bool odd = (c & 1) != 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      uint32_t m = pk_max_u16(pk_max_u16(mag2(x[j][0]), mag2(x[j][1])),
-                              pk_max_u16(mag2(x[j][2]), mag2(x[j][3])));
-      m = max(m & 0xFFFFu, m >> 16);
-      m = max(m, dpp_xor1(m));
-      m = max(m, dpp_xor2(m));
-      const Scale sc = scale_from_amax<FMT>(m);
-      const uint32_t lo = cvt4<FMT>(x[j][0], x[j][1], sc);
-      const uint32_t hi = cvt4<FMT>(x[j][2], x[j][3], sc);
-      const int64_t r = r0 + j;
-      if (colok && r < p.rows) {
-        const int64_t o = p.blk ? (col >> 6) * 64 * p.rows + r * 64 + (col & 63) : r * p.cols + col;
-        *reinterpret_cast<uint2*>(q_r + o) = make_uint2(lo, hi);
+    for (int j = 0; j < 8; j += 2) {
+      uint32_t w[2][2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t m = pk_max_u16(pk_max_u16(mag2(x[j + h][0]), mag2(x[j + h][1])),
+                                pk_max_u16(mag2(x[j + h][2]), mag2(x[j + h][3])));
+        m = max(m & 0xFFFFu, m >> 16);
+        m = max(m, dpp_xor1(m));
+        m = max(m, dpp_xor2(m));
+        const Scale sc = scale_from_amax<FMT>(m);
+        w[h][0] = cvt4<FMT>(x[j + h][0], x[j + h][1], sc);
+        w[h][1] = cvt4<FMT>(x[j + h][2], x[j + h][3], sc);
+        if ((c & 3) == 0) srow_b[(r0 + j + h - row0) * 4 + (c >> 2)] = (uint8_t)sc.byte;
       }
-      if ((c & 3) == 0) srow_b[(r - row0) * 4 + (c >> 2)] = (uint8_t)sc.byte;
+      // even lane keeps row j and takes the odd neighbour's row j; odd lane keeps row j+1
+      const uint32_t s0 = odd ? w[0][0] : w[1][0], s1 = odd ? w[0][1] : w[1][1];
+      const uint32_t r0w = dpp_xor1(s0), r1w = dpp_xor1(s1);
+      const int64_t r = r0 + j + (odd ? 1 : 0);
+      const int64_t cc = col - (odd ? 8 : 0);  // first column of the 16-column run
+      const uint4 v = odd ? make_uint4(r0w, r1w, w[1][0], w[1][1]) : make_uint4(w[0][0], w[0][1], r0w, r1w);
+      if (cc < p.cols && r < p.rows) {
+        const int64_t o = p.blk ? (cc >> 6) * 64 * p.rows + r * 64 + (cc & 63) : r * p.cols + cc;
+        *reinterpret_cast<uint4*>(q_r + o) = v;
+      }
     }
   }
 
