@@ -93,7 +93,10 @@ struct Tile {
   // the smaller LDS share)
   static constexpr int DSW_NP = (OCC == 2 && FM >= 2) ? FM : 2;
   static constexpr int DSW_SR = WM * (TM / DSW_NP);  // staged rows per pass
-  static constexpr int EPI_DSW = DSW_SR * (2 * BN + 8) * 2 + 2 * BN * (DSW_SR + 8) + 2 * BN * (DSW_SR / 32);
+  // passes of 32 rows per wavefront keep two passes' column codes (whole 64-token panel rows)
+  static constexpr int DSW_PAIR = (TM / DSW_NP == 32 && DSW_NP % 2 == 0) ? 2 : 1;
+  static constexpr int EPI_DSW = DSW_SR * (2 * BN + 8) * 2 + 2 * BN * (DSW_PAIR * DSW_SR + 8) +
+                                 2 * BN * (DSW_PAIR * DSW_SR / 32);
   static constexpr int LDS_MAIN = S * STAGE + NSC * SC_SLOT;
   static constexpr int imax(int a, int b) { return a > b ? a : b; }
   // LDS of a kernel instance: the main loop's stages or its epilogue's staging
@@ -627,8 +630,13 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
     constexpr int SR = T::DSW_SR;     // staged rows per pass (WM * RH)
     constexpr int PCB = 2 * BN;       // packed columns of the block
     constexpr int DP = PCB + 8;       // row-major tile pitch (bf16)
-    constexpr int QP = SR + 8;        // transposed code tile pitch (bytes)
-    constexpr int SG = SR / 32;       // column groups staged per pass
+    // Column codes are staged for PAIR consecutive passes (PAIR = 2 when a pass holds 32 rows
+    // per wavefront), then copied out together: each wavefront's 2 x 32 rows of a pass pair are
+    // one whole 64-token panel row per column, so every 16-byte store is a quarter of a 64-byte
+    // run instead of half of a 32-byte one (half the store instructions and lines touched).
+    constexpr int PAIR = T::DSW_PAIR;
+    constexpr int QP = PAIR * SR + 8;  // transposed code tile pitch (bytes)
+    constexpr int SG = PAIR * SR / 32; // column groups staged per pass pair
     const int64_t F = p.N;
     const int64_t ld13 = 2 * F;
     const int64_t pc0 = 2 * n0;
@@ -686,6 +694,8 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
             dswiglu2(bf16x2_bits(acc[i][j][2 * t], acc[i][j][2 * t + 1]), gw[t], uw[t], dgw[t], duw[t]);
           const int pcg = 2 * (tc0 + j * 32) + r32;  // packed column of dG (dU: + 32)
           const int rl = wm * RH + ii * 32 + 4 * g;  // staged row of slot 0
+          // its row in the column-code staging: wavefront run wm, pass hh % PAIR within it
+          const int rq = wm * PAIR * RH + (hh % PAIR) * RH + ii * 32 + 4 * g;
 #pragma unroll
           for (int part = 0; part < 2; ++part) {
             const uint32_t* w = part ? duw : dgw;
@@ -695,8 +705,8 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
             const Scale s = scale_from_amax(am);
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-              *reinterpret_cast<uint32_t*>(qT + pcl * QP + rl + 8 * k) = cvt4(w[2 * k], w[2 * k + 1], s);
-            sT[pcl * SG + wm * FH + ii] = (uint8_t)s.byte;  // lanes l and l ^ 32 write the same byte
+              *reinterpret_cast<uint32_t*>(qT + pcl * QP + rq + 8 * k) = cvt4(w[2 * k], w[2 * k + 1], s);
+            sT[pcl * SG + wm * PAIR * FH + (hh % PAIR) * FH + ii] = (uint8_t)s.byte;  // lanes l and l ^ 32: same byte
 #pragma unroll
             for (int t = 0; t < 8; ++t)
               *reinterpret_cast<uint32_t*>(dR + (rl + 8 * (t >> 1) + 2 * (t & 1)) * DP + pcl + pr_off) =
@@ -725,28 +735,34 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
         const int64_t grp = pcol >> 5;
         p.s_r[row * p.sr_rs + (grp >> 2) * p.sr_kbs + (grp & 3)] = (uint8_t)s.byte;  // as above: no branch
       }
-      // dhq_c [2F, mcap] in 64-token panels: a pass's RH consecutive block rows lie in one
-      // panel (RH = 64) or half of one (RH = 32); G lanes cover a column's run of them,
-      // consecutive columns on consecutive lane groups
-      constexpr int CPC = SR / 16;
-      constexpr int G = RH >= 64 ? 4 : RH / 16;
-      static_assert((PCB * CPC) % T::NT == 0 && RH % 16 == 0 && CPC % G == 0, "whole column-copy rounds");
+      if (hh % PAIR == PAIR - 1) {
+        // dhq_c [2F, mcap] in 64-token panels: a wavefront run of the staged passes is PAIR * RH
+        // consecutive block rows, one panel row (64) or half of one (32); G lanes cover a
+        // column's run, consecutive columns on consecutive lane groups. Staged row cr of the
+        // pass group is block row (cr / (PAIR RH)) TM + h0 RH + cr % (PAIR RH), h0 its first pass.
+        constexpr int RUN = PAIR * RH;
+        constexpr int CPC = PAIR * SR / 16;
+        constexpr int G = RUN >= 64 ? 4 : RUN / 16;
+        static_assert((PCB * CPC) % T::NT == 0 && RH % 16 == 0 && CPC % G == 0, "whole column-copy rounds");
+        const int h0 = hh - (PAIR - 1);
+        auto crow = [&](int cr) { return (cr / RUN) * T::TM + h0 * RH + cr % RUN; };
 #pragma unroll 2
-      for (int it = 0; it < PCB * CPC / T::NT; ++it) {
-        const int t = it * T::NT + tid;
-        const int pc = (t / G) % PCB, c = ((t / G) / PCB) * G + (t % G);
-        const uint2 a = *reinterpret_cast<const uint2*>(qT + pc * QP + c * 16);
-        const uint2 b = *reinterpret_cast<const uint2*>(qT + pc * QP + c * 16 + 8);
-        const int64_t tok = m0 + brow(hh, c * 16);
-        *reinterpret_cast<uint4*>(p.q_c + (tok >> 6) * 64 * ld13 + (pc0 + pc) * 64 + (tok & 63)) =
-            make_uint4(a.x, a.y, b.x, b.y);
+        for (int it = 0; it < PCB * CPC / T::NT; ++it) {
+          const int t = it * T::NT + tid;
+          const int pc = (t / G) % PCB, c = ((t / G) / PCB) * G + (t % G);
+          const uint2 a = *reinterpret_cast<const uint2*>(qT + pc * QP + c * 16);
+          const uint2 b = *reinterpret_cast<const uint2*>(qT + pc * QP + c * 16 + 8);
+          const int64_t tok = m0 + crow(c * 16);
+          *reinterpret_cast<uint4*>(p.q_c + (tok >> 6) * 64 * ld13 + (pc0 + pc) * 64 + (tok & 63)) =
+              make_uint4(a.x, a.y, b.x, b.y);
+        }
+        for (int t = tid; t < PCB * SG; t += T::NT) {
+          const int pc = t / SG, gi = t % SG;
+          const int64_t rg = (m0 + crow(gi * 32)) >> 5;
+          p.s_c[(pc0 + pc) * p.sc_rs + (rg >> 2) * p.sc_kbs + (rg & 3)] = sT[pc * SG + gi];
+        }
       }
-      for (int t = tid; t < PCB * SG; t += T::NT) {
-        const int pc = t / SG, gi = t % SG;
-        const int64_t rg = (m0 + brow(hh, gi * 32)) >> 5;
-        p.s_c[(pc0 + pc) * p.sc_rs + (rg >> 2) * p.sc_kbs + (rg & 3)] = sT[pc * SG + gi];
-      }
-      __syncthreads();  // the staging tiles are rewritten in the next pass
+      __syncthreads();  // the row staging is rewritten in the next pass (the code staging after PAIR)
     }
     return;
   }
