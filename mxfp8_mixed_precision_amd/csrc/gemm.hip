@@ -571,26 +571,39 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
     // row-wise groups: one task = 16 columns of a row, four tasks (four lanes) per 64-column
     // panel row, consecutive rows on consecutive lane quads, so a wavefront stores a contiguous
     // kilobyte of a panel; lanes 2c and 2c+1 hold one group
+    // A quad handles one row in each of the NPAN panels of the tile (the panel loop is inner),
+    // so its first lane gathers the row's 2 NPAN scale bytes (group 2P+1 from lane 2 of the
+    // quad) and stores them as one word (NPAN = 2) or halfword (NPAN = 1) of the 128-k plane.
     constexpr int CPR = HCB / 16;
-    static_assert((BM * CPR) % T::NT == 0 && CPR % 4 == 0, "whole row-pass rounds");
+    constexpr int NPAN = CPR / 4;  // 64-column panels of the tile's h columns (1 or 2)
+    static_assert(BM % 64 == 0 && T::NT == 256 && CPR % 4 == 0 && (NPAN == 1 || NPAN == 2),
+                  "row pass: 64 rows per round, one or two panels");
     const int64_t M = p.mcap;
-#pragma unroll 2
-    for (int it = 0; it < BM * CPR / T::NT; ++it) {
-      const int t = it * T::NT + tid;
-      const int r = (t >> 2) % BM, c = ((t >> 2) / BM) * 4 + (t & 3);
-      const uint4 a = *reinterpret_cast<const uint4*>(hR + r * HP + c * 16);
-      const uint4 b = *reinterpret_cast<const uint4*>(hR + r * HP + c * 16 + 8);
-      const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-      uint32_t am = amax16(v);
-      am = max(am, dpp_xor1(am));
-      const Scale s = scale_from_amax(am);
+    const int64_t g0 = hc0 >> 5;  // first 32-column group of the tile (a multiple of 2 NPAN)
+#pragma unroll 1
+    for (int rg = 0; rg < BM / 64; ++rg) {
+      const int r = rg * 64 + (tid >> 2);
       const int64_t row = m0 + r;
-      const int64_t hcol = hc0 + c * 16;
-      *reinterpret_cast<uint4*>(p.q_r + (hcol >> 6) * 64 * M + row * 64 + (hcol & 63)) =
-          make_uint4(cvt4(v[0], v[1], s), cvt4(v[2], v[3], s), cvt4(v[4], v[5], s), cvt4(v[6], v[7], s));
-      const int64_t grp = hcol >> 5;
-      // lanes 2c and 2c + 1 hold the same group and write the same byte (no branch)
-      p.s_r[row * p.sr_rs + (grp >> 2) * p.sr_kbs + (grp & 3)] = (uint8_t)s.byte;
+      uint32_t wsc = 0;
+#pragma unroll
+      for (int P = 0; P < NPAN; ++P) {
+        const int c = P * 4 + (tid & 3);
+        const uint4 a = *reinterpret_cast<const uint4*>(hR + r * HP + c * 16);
+        const uint4 b = *reinterpret_cast<const uint4*>(hR + r * HP + c * 16 + 8);
+        const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        uint32_t am = amax16(v);
+        am = max(am, dpp_xor1(am));
+        const Scale s = scale_from_amax(am);
+        const int64_t hcol = hc0 + c * 16;
+        *reinterpret_cast<uint4*>(p.q_r + (hcol >> 6) * 64 * M + row * 64 + (hcol & 63)) =
+            make_uint4(cvt4(v[0], v[1], s), cvt4(v[2], v[3], s), cvt4(v[4], v[5], s), cvt4(v[6], v[7], s));
+        wsc |= (s.byte | (dpp_xor2(s.byte) << 8)) << (16 * P);  // lane 0 of the quad: groups 2P, 2P+1
+      }
+      if ((tid & 3) == 0) {
+        uint8_t* d = p.s_r + row * p.sr_rs + (g0 >> 2) * p.sr_kbs + (g0 & 3);
+        if constexpr (NPAN == 2) *reinterpret_cast<uint32_t*>(d) = wsc;
+        else *reinterpret_cast<uint16_t*>(d) = (uint16_t)wsc;
+      }
     }
     // column-wise codes (hq_c [F, mcap], 64-token panels): four lanes per column and panel,
     // consecutive columns on consecutive lane quads (contiguous kilobytes)
@@ -715,25 +728,37 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, uint8_t* smem, int
         }
       }
       __syncthreads();
-      // four lanes per 64-column panel row, consecutive rows on consecutive lane quads
+      // four lanes per 64-column panel row, consecutive rows on consecutive lane quads; a quad
+      // takes one row through all NPAN panels (inner loop), its first lane gathering the row's
+      // scale bytes and storing each 128-k plane word (two panels) whole
       constexpr int CPR = PCB / 16;
-      static_assert((SR * CPR) % T::NT == 0 && CPR % 4 == 0, "whole row-pass rounds");
+      constexpr int NPAN = CPR / 4;  // 64-column panels of the packed columns (an even number)
+      static_assert(SR % 64 == 0 && T::NT == 256 && CPR % 4 == 0 && NPAN % 2 == 0,
+                    "row pass: 64 rows per round, whole 128-column scale words");
 #pragma unroll 2
-      for (int it = 0; it < SR * CPR / T::NT; ++it) {
-        const int t = it * T::NT + tid;
-        const int r = (t >> 2) % SR, c = ((t >> 2) / SR) * 4 + (t & 3);
-        const uint4 a = *reinterpret_cast<const uint4*>(dR + r * DP + c * 16);
-        const uint4 b = *reinterpret_cast<const uint4*>(dR + r * DP + c * 16 + 8);
-        const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        uint32_t am = amax16(v);
-        am = max(am, dpp_xor1(am));
-        const Scale s = scale_from_amax(am);
+      for (int rg = 0; rg < SR / 64; ++rg) {
+        const int r = rg * 64 + (tid >> 2);
         const int64_t row = m0 + brow(hh, r);
-        const int64_t pcol = pc0 + c * 16;
-        *reinterpret_cast<uint4*>(p.q_r + (pcol >> 6) * 64 * p.mcap + row * 64 + (pcol & 63)) =
-            make_uint4(cvt4(v[0], v[1], s), cvt4(v[2], v[3], s), cvt4(v[4], v[5], s), cvt4(v[6], v[7], s));
-        const int64_t grp = pcol >> 5;
-        p.s_r[row * p.sr_rs + (grp >> 2) * p.sr_kbs + (grp & 3)] = (uint8_t)s.byte;  // as above: no branch
+        uint32_t wsc = 0;
+#pragma unroll
+        for (int P = 0; P < NPAN; ++P) {
+          const int c = P * 4 + (tid & 3);
+          const uint4 a = *reinterpret_cast<const uint4*>(dR + r * DP + c * 16);
+          const uint4 b = *reinterpret_cast<const uint4*>(dR + r * DP + c * 16 + 8);
+          const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+          uint32_t am = amax16(v);
+          am = max(am, dpp_xor1(am));
+          const Scale s = scale_from_amax(am);
+          const int64_t pcol = pc0 + c * 16;
+          *reinterpret_cast<uint4*>(p.q_r + (pcol >> 6) * 64 * p.mcap + row * 64 + (pcol & 63)) =
+              make_uint4(cvt4(v[0], v[1], s), cvt4(v[2], v[3], s), cvt4(v[4], v[5], s), cvt4(v[6], v[7], s));
+          wsc |= (s.byte | (dpp_xor2(s.byte) << 8)) << (16 * (P & 1));  // groups 2P, 2P+1
+          if ((P & 1) && (tid & 3) == 0) {
+            const int64_t grp = (pc0 >> 5) + 2 * (P - 1);  // first group of the word (a multiple of 4)
+            *reinterpret_cast<uint32_t*>(p.s_r + row * p.sr_rs + (grp >> 2) * p.sr_kbs) = wsc;
+          }
+          if (P & 1) wsc = 0;
+        }
       }
       if (hh % PAIR == PAIR - 1) {
         // dhq_c [2F, mcap] in 64-token panels: a wavefront run of the staged passes is PAIR * RH
@@ -1043,6 +1068,8 @@ hipError_t mxf_launch_gemm_mgroup(int epi, const mxf::GemmParams& pin, hipStream
   const hipError_t ce = device_cus(&p.ncu);
   if (ce != hipSuccess) return ce;
   const bool big = (p.pad % 256 == 0) && (p.mcap % 256 == 0);
+  // the fused epilogues store whole scale words of 128-k planes
+  if ((epi == EPI_SWIGLU || epi == EPI_DSWIGLU) && (p.sr_rs != 4 || p.sc_rs != 4)) return hipErrorInvalidValue;
   switch (epi) {
     case EPI_STORE: return launch<SCHED_MGROUP, EPI_STORE>(p, big, st);
     case EPI_SWIGLU: return launch<SCHED_MGROUP, EPI_SWIGLU>(p, big, st);
