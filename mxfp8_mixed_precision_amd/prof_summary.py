@@ -244,8 +244,10 @@ def main():
                   "TCC_HIT / (TCC_HIT + TCC_MISS); LDS active and bank-conflict cycles per CU over the "
                   "kernel's active cycles.")
         md.append("")
-        md.append("Clock = active cycles over the kernel's mean duration in the trace run: the shader clock the "
-                  "kernel ran at (2.4 GHz is the maximum; the MXFP8 peak scales with it, 5.0 PF at 2.4 GHz).")
+        md.append("Clock = active cycles (counter pass) over the kernel's mean duration (trace pass): an estimate "
+                  "of the shader clock the kernel ran at (2.4 GHz is the maximum; the MXFP8 peak scales with it, "
+                  "5.0 PF at 2.4 GHz). The counter pass's window around a dispatch is a few microseconds longer "
+                  "than the kernel, so short kernels read high (above 2.4 GHz for the 40 us dY quantizer).")
         md.append("")
         md.append("| kernel | MFMA busy | F8 math TFLOP/launch | L2 hit | LDS active | LDS bank conflict | active cycles | clock GHz |")
         md.append("|---|---|---|---|---|---|---|---|")
