@@ -32,7 +32,8 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 def gemm_flops(name, m_real, D, F):
     """Useful FLOPs of one launch of each GEMM kernel (2 per multiply-add, real rows only)."""
     per = {"fc1_swiglu": 2 * 2 * F * D, "fc2": 2 * D * F, "fc2_dgrad_dswiglu": 2 * F * D,
-           "fc2_wgrad": 2 * D * F, "fc1_dgrad": 2 * D * 2 * F, "fc1_wgrad": 2 * 2 * F * D}
+           "fc2_wgrad": 2 * D * F, "fc1_dgrad": 2 * D * 2 * F, "fc1_wgrad": 2 * 2 * F * D,
+           "bwd_gemms": 2 * D * F + 2 * D * 2 * F + 2 * 2 * F * D}  # FC2 wgrad + FC1 dgrad + FC1 wgrad
     return per[name] * m_real if name in per else None
 
 
@@ -405,7 +406,11 @@ def bench_plans(mx, torch, dev, args, sets, counts, E, D, F, y, dx, dw1, dw3, dw
             ms = (time.perf_counter() - t0) * 1e3 / args.steps
             res[f"{plan}_pad{pad}"] = {"ms_per_step": round(ms, 4), "m_padded": mcap,
                                        "useful_tflops": round(18.0 * m_real * D * F / (ms / 1e3) / 1e12, 1),
-                                       "launches_fwd_bwd": "3 + 5" if plan == "fused" else "4 + 6"}
+                                       # pad 256 (256-row tiles): FC1 wgrad, FC2 wgrad and FC1
+                                       # dgrad share one launch
+                                       "launches_fwd_bwd": ("3 + " if plan == "fused" else "4 + ") +
+                                                           (("3" if plan == "fused" else "4") if pad == 256
+                                                            else ("5" if plan == "fused" else "6"))}
             del ctx
     return res
 

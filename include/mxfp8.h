@@ -145,10 +145,13 @@ mxf_status mxfp8_dequantize(const void* q, const void* s, int64_t rows, int64_t 
                               workspace by mxfp8_dispatch_quantize (same desc, offs, counts);
                               x is not read and may be NULL */
 #define MXF_SERIAL 4u      /* launch every kernel on the caller's stream, one after another:
-                              the default, stated explicitly (not with MXF_CONCURRENT) */
+                              the default, stated explicitly (not with MXF_CONCURRENT). The
+                              backward's FC1 wgrad, FC2 wgrad and FC1 dgrad then share one launch
+                              where all three run on 256-row tiles (pad_multiple 256, D and 2F
+                              multiples of 256) */
 #define MXF_CONCURRENT 32u /* run independent launches concurrently on two helper streams forked
                               from and joined into the caller's stream (the backward's FC2 wgrad,
-                              FC1 wgrad and FC1 dgrad beside each other). Measured
+                              FC1 wgrad and FC1 dgrad as three launches beside each other). Measured
                               on MI355X it is slower than the serial order for the DSv3 rank
                               shape (the GEMMs then share their L2 panels); kept for A/B runs */
 
@@ -323,8 +326,9 @@ mxf_status mxf_read_status(const void* workspace, void* stream, int32_t* device_
  * returns, per kernel name, the number of launches and their summed duration in ms; it
  * fills at most max_out entries and sets *n_out to the number filled, then stops recording.
  * Kernel names: quant_fwd (W13, W2 and X quantized in one launch), fc1_swiglu, fc2, quant_dy,
- * fc2_dgrad_dswiglu,
- * fc2_wgrad, fc1_dgrad, fc1_wgrad (MXF_UNFUSED: fc1, swiglu_quant, fc2_dgrad, dswiglu_quant),
+ * fc2_dgrad_dswiglu, bwd_gemms (FC1 wgrad, FC2 wgrad and FC1 dgrad in one launch, on 256-row
+ * tiles: pad_multiple 256, D and 2F multiples of 256, not with MXF_CONCURRENT; otherwise
+ * fc2_wgrad, fc1_wgrad, fc1_dgrad) (MXF_UNFUSED: fc1, swiglu_quant, fc2_dgrad, dswiglu_quant),
  * quantize, dequantize, route_plan, permute, dispatch_quant_x, hbm_read, hbm_write, hbm_copy.
  * Errors: MXF_E_ARG (capacity < 1 or > 1<<20, or end without begin), MXF_E_NULL, MXF_E_HIP. */
 typedef struct {

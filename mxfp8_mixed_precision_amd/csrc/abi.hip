@@ -436,27 +436,27 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
   base.mcap = M;
   base.out_f32 = of32;
   // After dY's quantization the backward is a small graph: FC2 wgrad needs only dY and the
-  // saved h, so it runs on a helper stream beside FC2 dgrad; FC1 dgrad (caller's stream) and
-  // FC1 wgrad (second helper) both need dH13 from FC2 dgrad and run beside each other. Each
-  // kernel's last partial round of tiles then overlaps another kernel's work.
+  // saved h; FC1 wgrad and FC1 dgrad need dH13 from FC2 dgrad. Serial launches (the default):
+  // FC2 dgrad, then the three others in one launch where all run on 256-row tiles (one kernel
+  // boundary instead of three; CUs done with one GEMM's tiles start the next GEMM's), else one
+  // after another. MXF_CONCURRENT: FC2 wgrad on a helper stream beside FC2 dgrad, then FC1
+  // wgrad (second helper) beside FC1 dgrad (caller's stream).
   Helpers* H = nullptr;
   if ((s = get_helpers(&H, desc->flags, st)) != MXF_OK) return s;
   const bool fork = H->s[0] != st;
   // FC2 wgrad: dW2[e] = dY^T h over the expert's tokens
-  {
-    mxf::GemmParams p = base;
-    // every scale tensor is in 128-k planes: row stride 4, plane stride 4 x rows
-    p.A = T(MXF_T_DYQ_C); p.As = T(MXF_T_DYS_C); p.akp = 64 * D; p.ldas = 4; p.kbsa = 4 * D;
-    p.B = T(MXF_T_HQ_C); p.Bs = T(MXF_T_HS_C); p.bkp = 64 * F; p.ldbs = 4; p.kbsb = 4 * F;
-    p.M = D; p.N = F; p.K = M;
-    p.C = dw2; p.ldc = F; p.c_es = D * F;
-    if (fork) {
-      MXF_HIP(hipEventRecord(H->fork, st), "hipEventRecord");
-      MXF_HIP(hipStreamWaitEvent(H->s[0], H->fork, 0), "hipStreamWaitEvent");
-    }
-    MXF_HIP(timed("fc2_wgrad", H->s[0], [&] { return mxf_launch_gemm_kgroup(0, p, H->s[0]); }),
+  mxf::GemmParams pw2 = base;
+  // every scale tensor is in 128-k planes: row stride 4, plane stride 4 x rows
+  pw2.A = T(MXF_T_DYQ_C); pw2.As = T(MXF_T_DYS_C); pw2.akp = 64 * D; pw2.ldas = 4; pw2.kbsa = 4 * D;
+  pw2.B = T(MXF_T_HQ_C); pw2.Bs = T(MXF_T_HS_C); pw2.bkp = 64 * F; pw2.ldbs = 4; pw2.kbsb = 4 * F;
+  pw2.M = D; pw2.N = F; pw2.K = M;
+  pw2.C = dw2; pw2.ldc = F; pw2.c_es = D * F;
+  if (fork) {
+    MXF_HIP(hipEventRecord(H->fork, st), "hipEventRecord");
+    MXF_HIP(hipStreamWaitEvent(H->s[0], H->fork, 0), "hipStreamWaitEvent");
+    MXF_HIP(timed("fc2_wgrad", H->s[0], [&] { return mxf_launch_gemm_kgroup(0, pw2, H->s[0]); }),
             "FC2 wgrad launch");
-    if (fork) MXF_HIP(hipEventRecord(H->join[0], H->s[0]), "hipEventRecord");
+    MXF_HIP(hipEventRecord(H->join[0], H->s[0]), "hipEventRecord");
   }
   // FC2 dgrad + dSwiGLU + dual quantization of dH13
   {
@@ -484,30 +484,34 @@ mxf_status grouped_mlp_bwd(const mxf_mlp_desc* desc, const int32_t* offs, const 
     }
   }
   // FC1 wgrad: dW13[e] = dH13^T X over the expert's tokens, unpacked into dW1 / dW3
-  {
-    mxf::GemmParams p = base;
-    p.A = T(MXF_T_DHQ_C); p.As = T(MXF_T_DHS_C); p.akp = 64 * 2 * F; p.ldas = 4; p.kbsa = 4 * 2 * F;
-    p.B = T(MXF_T_XQ_C); p.Bs = T(MXF_T_XS_C); p.bkp = 64 * D; p.ldbs = 4; p.kbsb = 4 * D;
-    p.M = 2 * F; p.N = D; p.K = M;
-    p.C = dw1; p.C2 = dw3; p.ldc = D; p.c_es = F * D;
+  mxf::GemmParams pw1 = base;
+  pw1.A = T(MXF_T_DHQ_C); pw1.As = T(MXF_T_DHS_C); pw1.akp = 64 * 2 * F; pw1.ldas = 4; pw1.kbsa = 4 * 2 * F;
+  pw1.B = T(MXF_T_XQ_C); pw1.Bs = T(MXF_T_XS_C); pw1.bkp = 64 * D; pw1.ldbs = 4; pw1.kbsb = 4 * D;
+  pw1.M = 2 * F; pw1.N = D; pw1.K = M;
+  pw1.C = dw1; pw1.C2 = dw3; pw1.ldc = D; pw1.c_es = F * D;
+  // FC1 dgrad: dX = dH13 W13
+  mxf::GemmParams pd1 = base;
+  pd1.M = M;
+  pd1.A = T(MXF_T_DHQ_R); pd1.As = T(MXF_T_DHS_R); pd1.akp = 64 * M; pd1.ldas = 4; pd1.kbsa = 4 * M;
+  pd1.B = T(MXF_T_W13Q_C); pd1.Bs = T(MXF_T_W13S_C); pd1.bkp = 64 * D; pd1.ldbs = 4; pd1.kbsb = 4 * D;
+  pd1.b_es = D * 2 * F; pd1.bs_es = D * 2 * F / 32;
+  pd1.N = D; pd1.K = 2 * F;
+  pd1.C = dx; pd1.ldc = D;
+  if (!fork && mxf_gemm_bwd3_fits(pw1, pw2, pd1)) {
+    // serial launches: the three GEMMs in one launch
+    MXF_HIP(timed("bwd_gemms", st, [&] { return mxf_launch_gemm_bwd3(pw1, pw2, pd1, st); }),
+            "FC1 wgrad + FC2 wgrad + FC1 dgrad launch");
+  } else {
+    if (!fork)
+      MXF_HIP(timed("fc2_wgrad", st, [&] { return mxf_launch_gemm_kgroup(0, pw2, st); }), "FC2 wgrad launch");
     if (fork) {
       MXF_HIP(hipEventRecord(H->fork, st), "hipEventRecord");
       MXF_HIP(hipStreamWaitEvent(H->s[1], H->fork, 0), "hipStreamWaitEvent");
     }
-    MXF_HIP(timed("fc1_wgrad", H->s[1], [&] { return mxf_launch_gemm_kgroup(3, p, H->s[1]); }),
+    MXF_HIP(timed("fc1_wgrad", H->s[1], [&] { return mxf_launch_gemm_kgroup(3, pw1, H->s[1]); }),
             "FC1 wgrad launch");
     if (fork) MXF_HIP(hipEventRecord(H->join[1], H->s[1]), "hipEventRecord");
-  }
-  // FC1 dgrad: dX = dH13 W13
-  {
-    mxf::GemmParams p = base;
-    p.M = M;
-    p.A = T(MXF_T_DHQ_R); p.As = T(MXF_T_DHS_R); p.akp = 64 * M; p.ldas = 4; p.kbsa = 4 * M;
-    p.B = T(MXF_T_W13Q_C); p.Bs = T(MXF_T_W13S_C); p.bkp = 64 * D; p.ldbs = 4; p.kbsb = 4 * D;
-    p.b_es = D * 2 * F; p.bs_es = D * 2 * F / 32;
-    p.N = D; p.K = 2 * F;
-    p.C = dx; p.ldc = D;
-    MXF_HIP(timed("fc1_dgrad", st, [&] { return mxf_launch_gemm_mgroup(0, p, st); }), "FC1 dgrad launch");
+    MXF_HIP(timed("fc1_dgrad", st, [&] { return mxf_launch_gemm_mgroup(0, pd1, st); }), "FC1 dgrad launch");
   }
   if (fork) {
     MXF_HIP(hipStreamWaitEvent(st, H->join[0], 0), "hipStreamWaitEvent");

@@ -806,16 +806,26 @@ struct TailCfg {
   static constexpr int BM4 = BM / 2, BN4 = BN / 2;      // Q = 4
 };
 
+// LDS of one GEMM's blocks: its tile's main loop or epilogue staging, and those of its tail
+// sub-tiles (M-grouped).
 template <int BM, int BN, int WM, int WN, int SCHED, int EPI, int OCC>
-__global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_mx_kernel(GemmParams p) {
+constexpr int gemm_lds() {
+  using T = Tile<BM, BN, WM, WN, OCC>;
+  using TC = TailCfg<BM, BN>;
+  return (SCHED == SCHED_MGROUP && TC::Q2)
+             ? T::imax(T::lds(EPI), T::imax(Tile<TC::BM2, TC::BN2, WM, WN, OCC>::lds(EPI),
+                                            Tile<TC::BM4, TC::BN4, WM, WN, OCC>::lds(EPI)))
+             : T::lds(EPI);
+}
+
+// One block of a grouped GEMM: bid is the block's index within the GEMM's own grid (block bid
+// runs on XCD bid % 8, which the tile orders assume: a GEMM sharing a launch starts at a
+// multiple of 8).
+template <int BM, int BN, int WM, int WN, int SCHED, int EPI, int OCC>
+__device__ __forceinline__ void gemm_block(const GemmParams& p, uint32_t bid, uint8_t* smem) {
   using T = Tile<BM, BN, WM, WN, OCC>;
   using TC = TailCfg<BM, BN>;
   constexpr bool SPLIT = SCHED == SCHED_MGROUP && TC::Q2;
-  constexpr int LDSZ = SPLIT ? T::imax(T::lds(EPI), T::imax(Tile<TC::BM2, TC::BN2, WM, WN, OCC>::lds(EPI),
-                                                           Tile<TC::BM4, TC::BN4, WM, WN, OCC>::lds(EPI)))
-                             : T::lds(EPI);
-  static_assert(LDSZ <= T::LDS_BYTES, "LDS of the kernel exceeds its share of the CU");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[LDSZ];
 
   const int tid = threadIdx.x;
   // Token offsets (validated on the device; a violation leaves every output untouched). E < 64:
@@ -893,7 +903,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_mx_kernel(GemmParams p
     // they finish early and their CUs move on to whole tiles out of phase with the rest, which
     // spreads the epilogues' store bursts over time.
     const uint32_t nsub = (rem * q + 7) / 8 * 8;
-    const uint32_t b = blockIdx.x;
+    const uint32_t b = bid;
     const bool tail = b < nsub;  // a sub-tile of one of the last rem tiles (raster order)
     uint32_t t, part = 0;
     if (!tail) {
@@ -948,7 +958,8 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_mx_kernel(GemmParams p
     // 32-bit arithmetic (as in the M-grouped order)
     const uint32_t mtn = (uint32_t)(p.M / BM);
     const uint32_t per = mtn * (uint32_t)ntn;
-    const uint32_t t = blockIdx.x;
+    const uint32_t t = bid;
+    if (t >= per * (uint32_t)p.E) return;  // blocks that round a shared launch's section up
     int ke;  // K span of expert e: its real rows rounded up to 128, within its segment
     if (!big_e) {
       int* ksp = reinterpret_cast<int*>(smem);  // per-expert K span, then the order (LDS scratch)
@@ -999,6 +1010,49 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_mx_kernel(GemmParams p
     __syncthreads();  // the LDS scratch is reused by the main loop
   }
   tile_run<BM, BN, WM, WN, SCHED, EPI, OCC>(p, smem, e, m0, n0, kbeg, kend);
+}
+
+template <int BM, int BN, int WM, int WN, int SCHED, int EPI, int OCC>
+__global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_mx_kernel(GemmParams p) {
+  constexpr int LDSZ = gemm_lds<BM, BN, WM, WN, SCHED, EPI, OCC>();
+  static_assert(LDSZ <= Tile<BM, BN, WM, WN, OCC>::LDS_BYTES, "LDS of the kernel exceeds its share of the CU");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDSZ];
+  gemm_block<BM, BN, WM, WN, SCHED, EPI, OCC>(p, blockIdx.x, smem);
+}
+
+// The three GEMMs of the backward pass that follow FC2 dgrad -- FC1 wgrad (with the W13 row
+// unpack), FC2 wgrad and FC1 dgrad -- read only operands that exist once dH13 does and write
+// disjoint outputs, so they share one launch: three sections of one 1-D grid, each block
+// running one block of its section's GEMM. One kernel boundary replaces three, and the CUs
+// that finish one section's last tiles start the next section's at once instead of waiting
+// for the slowest tile. Sections follow the longest-first order of the weight gradients (FC1
+// wgrad's tiles are the largest), and FC1 dgrad, whose tile order splits its last tiles into
+// sub-tiles, comes last. Section sizes are rounded up to multiples of 8 (surplus blocks exit)
+// so that every section keeps the XCD mapping its tile order assumes.
+struct GemmTrio {
+  GemmParams w1, w2, d1;
+  uint32_t n1, n2;  // blocks of the first two sections
+};
+template <int BN2>
+__global__ __launch_bounds__(256, 1) void gemm_bwd3_kernel(GemmTrio g) {
+  constexpr int L1 = gemm_lds<256, 256, 2, 2, SCHED_KGROUP, EPI_UNPACK13, 1>();
+  constexpr int L2 = gemm_lds<256, BN2, 2, 2, SCHED_KGROUP, EPI_STORE, 1>();
+  constexpr int L3 = gemm_lds<256, 256, 2, 2, SCHED_MGROUP, EPI_STORE, 1>();
+  constexpr int LDSZ = L1 > L2 ? (L1 > L3 ? L1 : L3) : (L2 > L3 ? L2 : L3);
+  static_assert(LDSZ <= 160 * 1024, "LDS of the kernel exceeds the CU");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDSZ];
+  uint32_t b = blockIdx.x;
+  if (b < g.n1) {
+    gemm_block<256, 256, 2, 2, SCHED_KGROUP, EPI_UNPACK13, 1>(g.w1, b, smem);
+    return;
+  }
+  b -= g.n1;
+  if (b < g.n2) {
+    gemm_block<256, BN2, 2, 2, SCHED_KGROUP, EPI_STORE, 1>(g.w2, b, smem);
+    return;
+  }
+  b -= g.n2;
+  gemm_block<256, 256, 2, 2, SCHED_MGROUP, EPI_STORE, 1>(g.d1, b, smem);
 }
 
 // ------------------------------------------------------------------ host launchers
@@ -1089,4 +1143,38 @@ hipError_t mxf_launch_gemm_kgroup(int epi, const mxf::GemmParams& p, hipStream_t
     case EPI_UNPACK13: return launch<SCHED_KGROUP, EPI_UNPACK13>(p, big, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+bool mxf_gemm_bwd3_fits(const mxf::GemmParams& w1, const mxf::GemmParams& w2, const mxf::GemmParams& d1) {
+  return w1.M % 256 == 0 && w1.N % 256 == 0 && w2.M % 256 == 0 && d1.pad % 256 == 0 && d1.mcap % 256 == 0 &&
+         d1.N % 256 == 0;
+}
+
+hipError_t mxf_launch_gemm_bwd3(const mxf::GemmParams& w1, const mxf::GemmParams& w2, const mxf::GemmParams& d1,
+                                hipStream_t st) {
+  using namespace mxf;
+  // the single launches' shape checks
+  if (w1.M % 128 || w1.N % 128 || w1.ldc % 8 || w2.M % 128 || w2.N % 128 || w2.ldc % 8) return hipErrorInvalidValue;
+  if (d1.mcap % 128 || d1.N % 128 || d1.K % 128 || d1.ldc % 8) return hipErrorInvalidValue;
+  // the tiles the single launches would choose: 256 x 256 for FC1 wgrad and FC1 dgrad, 256 x 256
+  // or 256 x 128 for FC2 wgrad
+  if (!mxf_gemm_bwd3_fits(w1, w2, d1)) return hipErrorInvalidValue;
+  GemmTrio g;
+  g.w1 = w1;
+  g.w2 = w2;
+  g.d1 = d1;
+  const hipError_t ce = device_cus(&g.d1.ncu);
+  if (ce != hipSuccess) return ce;
+  const bool wide2 = w2.N % 256 == 0;
+  const int64_t n1 = (w1.M / 256) * (w1.N / 256) * w1.E;
+  const int64_t n2 = (w2.M / 256) * (w2.N / (wide2 ? 256 : 128)) * w2.E;
+  const int64_t n3 = (d1.mcap / 256) * (d1.N / 256) + 3 * (int64_t)g.d1.ncu;  // + tail sub-tiles
+  const int64_t r1 = (n1 + 7) / 8 * 8, r2 = (n2 + 7) / 8 * 8;
+  if (r1 + r2 + n3 > 0x7FFFFFFF) return hipErrorInvalidValue;
+  g.n1 = (uint32_t)r1;
+  g.n2 = (uint32_t)r2;
+  const dim3 grid((unsigned)(r1 + r2 + n3));
+  if (wide2) hipLaunchKernelGGL(gemm_bwd3_kernel<256>, grid, dim3(256), 0, st, g);
+  else hipLaunchKernelGGL(gemm_bwd3_kernel<128>, grid, dim3(256), 0, st, g);
+  return hipGetLastError();
 }

@@ -82,5 +82,12 @@ hipError_t mxf_launch_permute(const void* x, int64_t n_assign, int topk, int64_t
 // gemm.hip
 hipError_t mxf_launch_gemm_mgroup(int epi, const mxf::GemmParams& p, hipStream_t st);
 hipError_t mxf_launch_gemm_kgroup(int epi, const mxf::GemmParams& p, hipStream_t st);
+// FC1 wgrad (K-grouped, W13 unpack), FC2 wgrad (K-grouped, plain store) and FC1 dgrad
+// (M-grouped, plain store) in one launch, where each of them runs on 256-row tiles
+// (mxf_gemm_bwd3_fits; otherwise the launcher returns hipErrorInvalidValue and the caller
+// launches them one by one).
+bool mxf_gemm_bwd3_fits(const mxf::GemmParams& w1, const mxf::GemmParams& w2, const mxf::GemmParams& d1);
+hipError_t mxf_launch_gemm_bwd3(const mxf::GemmParams& w1, const mxf::GemmParams& w2, const mxf::GemmParams& d1,
+                                hipStream_t st);
 // hbm.hip
 hipError_t mxf_launch_hbm_probe(int mode, const void* src, void* dst, int64_t bytes, int ncu, hipStream_t st);

@@ -22,8 +22,8 @@ per launch, with the sha256 of the kernel sources they were measured on; bench.p
 reports them while the sources are unchanged).
 
 Kernel dispatches are named by their position in a bench.py step: the MLP step enqueues, in
-order, quant_fwd (W13, W2 and X in one launch), fc1_swiglu, fc2, quant_dy, fc2_wgrad, fc2_dgrad_dswiglu,
-fc1_wgrad, fc1_dgrad; a --quant-only run launches `quantize` (the dual quantizer), the HBM
+order, quant_fwd (W13, W2 and X in one launch), fc1_swiglu, fc2, quant_dy, fc2_dgrad_dswiglu,
+bwd_gemms (FC1 wgrad, FC2 wgrad and FC1 dgrad in one launch); a --quant-only run launches `quantize` (the dual quantizer), the HBM
 ceiling kernels `hbm_read`, `hbm_write`, `hbm_copy` on the quantizer's input bytes, and then
 `dequantize` (row-wise codes to BF16). Profile with
 `bench.py --serial` so that every kernel runs alone (durations not stretched by overlap).
@@ -37,14 +37,13 @@ import os
 import re
 from collections import defaultdict
 
-MLP_SEQUENCE = ["quant_fwd", "fc1_swiglu", "fc2", "quant_dy", "fc2_wgrad",
-                "fc2_dgrad_dswiglu", "fc1_wgrad", "fc1_dgrad"]
+MLP_SEQUENCE = ["quant_fwd", "fc1_swiglu", "fc2", "quant_dy", "fc2_dgrad_dswiglu", "bwd_gemms"]
 # expected kernel template per logical name: a piece of the kernel's name (GEMMs: ", SCHED, EPI, "
 # of gemm_mx_kernel<BM, BN, WM, WN, SCHED, EPI, OCC>; quantizers: the kernel and its KIND)
 EXPECT = {
     "quant_fwd": "quant_fwd_kernel",
     "quant_dy": "quant_dual_kernel<1,", "fc1_swiglu": ", 0, 1, ", "fc2": ", 0, 0, ", "fc2_dgrad_dswiglu": ", 0, 2, ",
-    "fc2_wgrad": ", 1, 0, ", "fc1_dgrad": ", 0, 0, ", "fc1_wgrad": ", 1, 3, ", "quantize": "quant_dual_kernel<0,true,true,0>",
+    "bwd_gemms": "gemm_bwd3_kernel", "quantize": "quant_dual_kernel<0,true,true,0>",
     "dequantize": "dequant_kernel<true,0>",
     "hbm_read": "hbm_read_kernel", "hbm_write": "hbm_write_kernel", "hbm_copy": "hbm_copy_kernel",
 }

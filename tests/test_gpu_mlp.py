@@ -240,6 +240,39 @@ def test_deterministic(tiny):
         assert torch.equal(r[k][:, :w], r2[k][:, :w]), k
 
 
+# A shape on 256-row tiles (pad 256, D and 2F multiples of 256): the backward's FC1 wgrad,
+# FC2 wgrad and FC1 dgrad share one launch there.
+MERGED_BWD = dict(counts=[0, 200, 0, 57], E=4, D=256, F=384, pad=256)
+
+
+def _merged_problem(case, seed=5):
+    return workloads.mlp_problem(None, seed=seed, counts=case["counts"], E=case["E"], D=case["D"], F=case["F"],
+                                 pad=case["pad"],
+                                 m_capacity=workloads.padded_offsets(case["counts"], case["pad"])[-1] + case["pad"])
+
+
+@pytest.mark.parametrize("case", [
+    MERGED_BWD,                                                       # FC2 wgrad on 256 x 128
+    dict(counts=[2300, 2250], E=2, D=256, F=2048, pad=256),          # 256 x 256; FC1 dgrad tail tiles
+    dict(counts=[512], E=1, D=512, F=640, pad=256),                  # dense (E = 1)
+])
+def test_merged_backward_gemms_match_separate_launches(case):
+    """On 256-row tiles the serial backward runs FC1 wgrad, FC2 wgrad and FC1 dgrad in one
+    launch; MXF_CONCURRENT launches them separately on helper streams. Outputs and weight
+    gradients are bit-identical (each output element is the same reduction in the same order
+    either way)."""
+    mx = require_gpu()
+    print(f"\nmerged backward case E={case['E']} D={case['D']} F={case['F']} pad={case['pad']}", flush=True)
+    prob = _merged_problem(case, seed=21)
+    r1 = run_mlp(mx, prob, mx.OUT_F32)
+    r2 = run_mlp(mx, prob, mx.OUT_F32 | mx.CONCURRENT)
+    m = prob["offs"][-1]
+    for k in ("dw1", "dw3", "dw2"):
+        assert torch.equal(r1[k], r2[k]), k
+    for k in ("y", "dx"):
+        assert torch.equal(r1[k][:m], r2[k][:m]), k
+
+
 def test_serial_launches_match_concurrent(tiny):
     """The default serial launches and MXF_CONCURRENT's helper-stream fork/join give
     bit-identical outputs and saved tensors."""
@@ -534,23 +567,25 @@ def _graph_kernel_nodes(mx, prob, flags, direction):
     return types
 
 
+@pytest.mark.parametrize("shape", ["tiny", "pad256"])
 @pytest.mark.parametrize("plan", ["fused", "unfused"])
-def test_launch_counts(plan):
+def test_launch_counts(plan, shape):
     """Launch-count contract (torchtitan PR #2 "Summary": the fused plan removes the standalone
-    activation casts; "Numerics and tests": profiler op-count contracts). Here: 3 forward + 5
-    backward kernels for the fused plan (one launch quantizing W13, W2 and X; FC1 + SwiGLU +
-    dual quantization; FC2 | dY quantizer, FC2 dgrad + dSwiGLU + dual quantization, both wgrads,
-    FC1 dgrad) and 4 + 6 for the unfused plan (plus the standalone SwiGLU / dSwiGLU quantizers,
-    after plain FC1 / FC2 dgrad GEMMs). Counted
-    twice: by the library's per-launch events and as kernel nodes of a captured HIP graph
-    (which must hold nothing but kernels: no memset or copy nodes)."""
+    activation casts; "Numerics and tests": profiler op-count contracts). Forward: 3 kernels
+    for the fused plan (one launch quantizing W13, W2 and X; FC1 + SwiGLU + dual quantization;
+    FC2), 4 for the unfused plan (plain FC1, then the standalone SwiGLU quantizer). Backward,
+    fused: the dY quantizer, FC2 dgrad + dSwiGLU + dual quantization, then FC1 wgrad, FC2 wgrad
+    and FC1 dgrad -- one launch on 256-row tiles (pad 256), three otherwise (pad 128): 3 or 5;
+    unfused: plain FC2 dgrad and the standalone dSwiGLU quantizer in place of the fused GEMM,
+    4 or 6. Counted twice: by the library's per-launch events and as kernel nodes of a
+    captured HIP graph (which must hold nothing but kernels: no memset or copy nodes)."""
     mx = require_gpu()
-    prob = workloads.mlp_problem("tiny", m_capacity=1536)
+    prob = workloads.mlp_problem("tiny", m_capacity=1536) if shape == "tiny" else _merged_problem(MERGED_BWD)
     flags = mx.UNFUSED if plan == "unfused" else 0
-    want = {"fused": ({"quant_fwd", "fc1_swiglu", "fc2"},
-                      {"quant_dy", "fc2_wgrad", "fc2_dgrad_dswiglu", "fc1_wgrad", "fc1_dgrad"}),
+    tail = {"fc2_wgrad", "fc1_wgrad", "fc1_dgrad"} if shape == "tiny" else {"bwd_gemms"}
+    want = {"fused": ({"quant_fwd", "fc1_swiglu", "fc2"}, {"quant_dy", "fc2_dgrad_dswiglu"} | tail),
             "unfused": ({"quant_fwd", "fc1", "swiglu_quant", "fc2"},
-                        {"quant_dy", "fc2_wgrad", "fc2_dgrad", "dswiglu_quant", "fc1_wgrad", "fc1_dgrad"})}[plan]
+                        {"quant_dy", "fc2_dgrad", "dswiglu_quant"} | tail)}[plan]
     E, D, F, pad, mcap = prob["E"], prob["D"], prob["F"], prob["pad"], prob["m_capacity"]
     ctx = mx.MlpContext(E, D, F, pad, mcap, flags=flags)
     offs = torch.tensor(prob["offs"], dtype=torch.int32, device="cuda")
