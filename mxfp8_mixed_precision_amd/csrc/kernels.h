@@ -26,7 +26,7 @@ struct GemmParams {
   const int32_t* counts;
   int E, pad;
   int64_t mcap;
-  int ncu;           // compute units of the device (set by the launcher; tail sub-tiling)
+  int ncu;           // compute units of the device (set by the launcher; tail sub-tiling; 0: none)
   // epilogue
   void* C;           // STORE: [M, N] (+ e * c_es for K-grouped); UNPACK13: dW1
   void* C2;          // UNPACK13: dW3
@@ -82,8 +82,8 @@ hipError_t mxf_launch_permute(const void* x, int64_t n_assign, int topk, int64_t
 // gemm.hip
 hipError_t mxf_launch_gemm_mgroup(int epi, const mxf::GemmParams& p, hipStream_t st);
 hipError_t mxf_launch_gemm_kgroup(int epi, const mxf::GemmParams& p, hipStream_t st);
-// FC1 wgrad (K-grouped, W13 unpack), FC2 wgrad (K-grouped, plain store) and FC1 dgrad
-// (M-grouped, plain store) in one launch, where each of them runs on 256-row tiles
+// FC1 dgrad (M-grouped, plain store), FC1 wgrad (K-grouped, W13 unpack) and FC2 wgrad
+// (K-grouped, plain store) in one launch, where each of them runs on 256-row tiles
 // (mxf_gemm_bwd3_fits; otherwise the launcher returns hipErrorInvalidValue and the caller
 // launches them one by one).
 bool mxf_gemm_bwd3_fits(const mxf::GemmParams& w1, const mxf::GemmParams& w2, const mxf::GemmParams& d1);
