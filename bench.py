@@ -124,6 +124,8 @@ def main():
                     help="launch with MXF_SERIAL stated explicitly (the default order; profiler runs)")
     ap.add_argument("--quant-only", action="store_true",
                     help="only measure the standalone quantizer and dequantizer (for a profiler run of those kernels alone)")
+    ap.add_argument("--mfma-only", action="store_true",
+                    help="only run the matrix-core ceiling kernels (for a profiler run of those kernels alone)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -146,6 +148,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 3}), flush=True)
+        return
+    if args.mfma_only:
+        mx.lib()
+        print(json.dumps({"mfma_ceilings": bench_mfma_ceilings(mx, torch, dev, args)}), flush=True)
         return
     if args.quant_only:
         mx.lib()
@@ -270,6 +276,9 @@ def main():
     }
 
     if not args.no_plans:
+        out["mfma_ceilings"] = bench_mfma_ceilings(mx, torch, dev, args)
+        if roof["bound"] == "mfma":
+            roof["frac_of_matrix_ceiling"] = round(roof["achieved"] / out["mfma_ceilings"]["matrix_only"]["value"], 4)
         out["dispatch"] = bench_dispatch(mx, torch, dev, args, kernels["quant_fwd"]["avg_us"], sets[0])
         out["plans"] = bench_plans(mx, torch, dev, args, sets, counts, E, D, F, y, dx, dw1, dw3, dw2)
     if not args.no_quant:
@@ -356,6 +365,37 @@ def bench_quantize(mx, torch, dev, args):
             "roofline": {"bound": "hbm", "kernel": "quantize", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": traffic_for("quantize", "quant")}}
+
+
+def bench_mfma_ceilings(mx, torch, dev, args):
+    """The library's matrix-core ceiling kernels (mxf_mfma_probe), one block per CU on a 256 x 256
+    tile per block: the matrix instructions alone, and the GEMM main loop's whole stage (direct
+    global->LDS loads, LDS fragment reads, matrix instructions, a barrier per stage) over a 2 MB
+    window of codes (held in each XCD's L2) and a 64 MB window (streamed from beyond the L2s).
+    The codes are N(0, 64^2) samples cast to E4M3 (real operand bits; the scales are 1)."""
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    g = torch.Generator(device=dev).manual_seed(7)
+    nb_big = 64 << 20
+    codes = (torch.randn(nb_big, generator=g, device=dev) * 64).clamp_(-448, 448).to(torch.float8_e4m3fn)
+    codes = codes.view(torch.uint8)
+    out = torch.empty(ncu * 256, dtype=torch.float32, device=dev)
+    stages = 2000
+    flop = ncu * stages * 256 * 256 * 64 * 2
+    n = 5
+    res = {}
+    for name, mode, nbytes in (("matrix_only", mx.MFMA_MATRIX, 2 << 20), ("stage_l2", mx.MFMA_STAGE, 2 << 20),
+                               ("stage_streamed", mx.MFMA_STAGE, nb_big)):
+        for _ in range(2):
+            mx.mfma_probe(mode, codes, nbytes, stages, ncu, out)
+        t = loop_seconds(torch, n, lambda i: mx.mfma_probe(mode, codes, nbytes, stages, ncu, out))
+        tf = flop / t / 1e12
+        res[name] = {"value": round(tf, 1), "unit": "TFLOP/s", "avg_us": round(t * 1e6, 1),
+                     "us_per_stage": round(t * 1e6 / stages, 4), "frac_of_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+    del codes, out
+    res["kernel"] = (f"library matrix-core probe kernels (mxf_mfma_probe): {ncu} blocks x {stages} stages of a "
+                     "256 x 256 x 64 block tile; matrix_only = the matrix instructions alone, stage_l2 / "
+                     "stage_streamed = the GEMM main-loop stage over a 2 MB / 64 MB window of E4M3 codes")
+    return res
 
 
 def cpu_baseline_quantize(rows_sample=8192):

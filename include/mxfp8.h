@@ -353,6 +353,27 @@ mxf_status mxf_profile_end(mxf_kernel_time* out /* host */, int32_t max_out, int
  * MXF_E_HIP. Timed under the profiling name hbm_read / hbm_write / hbm_copy. */
 mxf_status mxf_hbm_probe(int32_t mode, const void* src, void* dst, int64_t bytes, void* stream);
 
+/* Matrix-core ceiling kernels (measurement): the MXFP8 contraction rate the device sustains
+ * with the grouped GEMM's instruction mix, so the GEMMs can be reported against a measured rate
+ * as well as against the data-sheet peak. One 256-thread block per CU is the intended launch
+ * (blocks = the CU count); each block works a 256 x 256 tile in 64-k stages with
+ * v_mfma_scale_f32_32x32x64_f8f6f4 (8,388,608 FLOP per block and stage).
+ *   mode 0 (matrix only):  operands read once into registers; the loop is the matrix
+ *                          instructions alone.
+ *   mode 1 (whole stage):  the GEMM main loop's stage: direct global->LDS operand and scale
+ *                          loads into a four-stage ring, LDS fragment reads beside the matrix
+ *                          instructions, one barrier per stage. Stage s of block b reads the
+ *                          32 KB chunk (37 b + s) mod (bytes / 32768) of src.
+ * src: device buffer of bytes E4M3 codes (16-byte aligned; bytes a multiple of 32768, at least
+ * 131072, at most 2^40); its first 128 KB also seed the LDS ring. Scales are 127 (a factor of 1).
+ * out: device, blocks * 256 floats (16-byte aligned); thread t of block b writes out[256 b + t],
+ * the sum of the first accumulator of its 16 fragments -- with every code 0x38 (E4M3 1.0)
+ * exactly 1024 * stages. stages: even, in [2, 2^24]; blocks in [1, 65535].
+ * Errors: MXF_E_ARG (mode), MXF_E_SHAPE (bytes, stages, blocks), MXF_E_NULL, MXF_E_ALIGN,
+ * MXF_E_DEVICE, MXF_E_HIP. Timed under the profiling name mfma_matrix / mfma_stage. */
+mxf_status mxf_mfma_probe(int32_t mode, const void* src, int64_t bytes, int32_t stages, int32_t blocks,
+                          float* out, void* stream);
+
 /* Test helpers for the [E, 2F, D] 32-block packing: w13[e, 64j+i] = w1[e, 32j+i] and
  * w13[e, 64j+32+i] = w3[e, 32j+i] (i < 32), BF16, and its inverse. F % 32 == 0. */
 mxf_status mxf_pack_w13(const void* w1, const void* w3, void* w13, int32_t E, int32_t F,

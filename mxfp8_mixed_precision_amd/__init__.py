@@ -11,7 +11,8 @@ from ._abi import (CAP_GFX950, COL, DEBUG_F32, DEQ_BF16, DEQ_E5M2, DEQ_F32, E5M2
                    ROW, T, TENSORS, MlpDesc, MxfError, abi_version, grouped_mlp_bwd, grouped_mlp_fwd,
                    last_error, lib, make_desc, mlp_saved_bytes, mlp_tensor, mlp_workspace_bytes,
                    mxfp8_quantize, pack_w13, profile_begin, profile_end, quantize, query_device,
-                   read_status, unpack_w13, hbm_probe, HBM_READ, HBM_WRITE, HBM_COPY)
+                   read_status, unpack_w13, hbm_probe, HBM_READ, HBM_WRITE, HBM_COPY,
+                   mfma_probe, MFMA_MATRIX, MFMA_STAGE)
 
 # shapes of the documented tensors, as functions of (E, D, F, m_capacity)
 _SHAPES = {

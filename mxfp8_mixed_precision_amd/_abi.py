@@ -36,7 +36,7 @@ EXPORTS = ["mxf_abi_version", "mxf_query_device", "mxf_last_error", "mxfp8_quant
            "grouped_mlp_bwd", "mxf_read_status", "mxf_profile_begin", "mxf_profile_end",
            "mxf_pack_w13", "mxf_unpack_w13", "mxf_route_plan_workspace_bytes", "mxf_route_plan", "mxf_route_plan_noalloc",
            "mxf_dispatch_permute",
-           "mxfp8_dispatch_quantize", "mxf_hbm_probe"]
+           "mxfp8_dispatch_quantize", "mxf_hbm_probe", "mxf_mfma_probe"]
 
 
 class MxfError(RuntimeError):
@@ -91,6 +91,7 @@ def lib():
             "mxf_dispatch_permute": (ctypes.c_int, [vp, i64, i32, i64, i32, vp, vp, i64, vp, vp]),
             "mxfp8_dispatch_quantize": (ctypes.c_int, [pdesc, vp, vp, vp, vp, i64, i32, vp, vp, vp]),
             "mxf_hbm_probe": (ctypes.c_int, [i32, vp, vp, i64, vp]),
+            "mxf_mfma_probe": (ctypes.c_int, [i32, vp, i64, i32, i32, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -295,6 +296,14 @@ HBM_READ, HBM_WRITE, HBM_COPY = 0, 1, 2
 def hbm_probe(mode, src, dst, nbytes, stream=None):
     """HBM ceiling kernel (see mxf_hbm_probe): mode HBM_READ, HBM_WRITE or HBM_COPY."""
     _check(lib().mxf_hbm_probe(mode, _ptr(src) if src is not None else None, _ptr(dst), nbytes, _stream(stream)))
+
+
+MFMA_MATRIX, MFMA_STAGE = 0, 1
+
+
+def mfma_probe(mode, src, nbytes, stages, blocks, out, stream=None):
+    """Matrix-core ceiling kernel (see mxf_mfma_probe): mode MFMA_MATRIX or MFMA_STAGE."""
+    _check(lib().mxf_mfma_probe(mode, _ptr(src), nbytes, stages, blocks, _ptr(out), _stream(stream)))
 
 
 def profile_begin(capacity=4096):

@@ -740,6 +740,27 @@ mxf_status mxf_hbm_probe(int32_t mode, const void* src, void* dst, int64_t bytes
   return MXF_OK;
 }
 
+mxf_status mxf_mfma_probe(int32_t mode, const void* src, int64_t bytes, int32_t stages, int32_t blocks, float* out,
+                          void* stream) {
+  g_err.clear();
+  if (mode < 0 || mode > 1) return fail(MXF_E_ARG, "mode = %d: must be 0 (matrix only) or 1 (whole stage)", mode);
+  if (bytes < 131072 || bytes % 32768 != 0 || bytes > ((int64_t)1 << 40))
+    return fail(MXF_E_SHAPE, "bytes = %lld: must be a multiple of 32768, at least 131072, at most 2^40",
+                (long long)bytes);
+  if (stages <= 0 || stages % 2 != 0 || stages > (1 << 24))
+    return fail(MXF_E_SHAPE, "stages = %d: must be even, positive and at most 2^24", stages);
+  if (blocks <= 0 || blocks > 65535) return fail(MXF_E_SHAPE, "blocks = %d: must be in [1, 65535]", blocks);
+  if (!src || !out) return fail(MXF_E_NULL, "src or out is NULL");
+  if (!aligned16(src) || !aligned16(out)) return fail(MXF_E_ALIGN, "src or out is not 16-byte aligned");
+  mxf_status st = check_device();
+  if (st != MXF_OK) return st;
+  static const char* const names[2] = {"mfma_matrix", "mfma_stage"};
+  MXF_HIP(timed(names[mode], (hipStream_t)stream,
+                [&] { return mxf_launch_mfma_probe(mode, src, bytes, stages, blocks, out, (hipStream_t)stream); }),
+          "matrix-core probe launch");
+  return MXF_OK;
+}
+
 mxf_status mxf_pack_w13(const void* w1, const void* w3, void* w13, int32_t E, int32_t F, int32_t D, void* stream) {
   g_err.clear();
   mxf_status s = pack_common(w1, w3, w13, E, F, D);

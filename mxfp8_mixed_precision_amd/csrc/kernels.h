@@ -91,3 +91,6 @@ hipError_t mxf_launch_gemm_bwd3(const mxf::GemmParams& w1, const mxf::GemmParams
                                 hipStream_t st);
 // hbm.hip
 hipError_t mxf_launch_hbm_probe(int mode, const void* src, void* dst, int64_t bytes, int ncu, hipStream_t st);
+// mfma_probe.hip
+hipError_t mxf_launch_mfma_probe(int mode, const void* src, int64_t bytes, int stages, int blocks, float* out,
+                                 hipStream_t st);

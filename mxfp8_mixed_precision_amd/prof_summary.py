@@ -25,7 +25,8 @@ Kernel dispatches are named by their position in a bench.py step: the MLP step e
 order, quant_fwd (W13, W2 and X in one launch), fc1_swiglu, fc2, quant_dy, fc2_dgrad_dswiglu,
 bwd_gemms (FC1 wgrad, FC2 wgrad and FC1 dgrad in one launch); a --quant-only run launches `quantize` (the dual quantizer), the HBM
 ceiling kernels `hbm_read`, `hbm_write`, `hbm_copy` on the quantizer's input bytes, and then
-`dequantize` (row-wise codes to BF16). Profile with
+`dequantize` (row-wise codes to BF16); a --mfma-only run launches the matrix-core ceiling kernels
+(`mfma_matrix`, then `mfma_stage` over a 2 MB and then a 64 MB window of codes). Profile with
 `bench.py --serial` so that every kernel runs alone (durations not stretched by overlap).
 """
 import argparse
@@ -46,10 +47,14 @@ EXPECT = {
     "bwd_gemms": "gemm_bwd3_kernel", "quantize": "quant_dual_kernel<0,true,true,0>",
     "dequantize": "dequant_kernel<true,0>",
     "hbm_read": "hbm_read_kernel", "hbm_write": "hbm_write_kernel", "hbm_copy": "hbm_copy_kernel",
+    "mfma_matrix": "mfma_probe_kernel<0>", "mfma_stage": "mfma_probe_kernel<1>",
 }
 # a --quant-only run: the dual quantizer, the dequantizer, then the HBM ceiling kernels timed
 # beside the quantizer (read, write, copy of the quantizer's input bytes)
 QUANT_ONLY = ["quantize", "dequantize", "hbm_read", "hbm_write", "hbm_copy"]
+# a --mfma-only run: the matrix-core ceiling kernels, the matrix instructions alone, then the
+# whole GEMM stage over a 2 MB window (L2-resident) and, with as many launches, a 64 MB window
+MFMA_ONLY = ["mfma_matrix", "mfma_stage_l2", "mfma_stage_streamed"]
 COMPUTE_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_LDS_IDX_ACTIVE",
                     "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "TCC_HIT_sum", "TCC_MISS_sum"]
 SIMDS = 1024   # 256 compute units x 4 SIMDs
@@ -114,13 +119,19 @@ def _matches(name, logical):
     return re.sub(r"\s+", "", EXPECT[logical]) in re.sub(r"\s+", "", name)
 
 
-def label(dispatches, quant_only):
+def label(dispatches, group):
     """Attach logical kernel names (see the module docstring). For an MLP run, every window of
-    eight consecutive dispatches whose templates match the step sequence is one step; other
+    consecutive dispatches whose templates match the step sequence is one step; other
     dispatches (e.g. a trailing standalone-quantizer measurement) are left out."""
     out = []
-    if quant_only:
+    if group == "quant":
         return [(did, k, r) for did, name, r in dispatches for k in QUANT_ONLY if _matches(name, k)]
+    if group == "mfma":
+        mat = [(did, "mfma_matrix", r) for did, name, r in dispatches if _matches(name, "mfma_matrix")]
+        st = [(did, r) for did, name, r in dispatches if _matches(name, "mfma_stage")]
+        half = len(st) // 2  # the same launch count on each window, 2 MB first
+        return mat + [(did, "mfma_stage_l2" if i < half else "mfma_stage_streamed", r)
+                      for i, (did, r) in enumerate(st)]
     i, n = 0, len(MLP_SEQUENCE)
     while i + n <= len(dispatches):
         window = dispatches[i:i + n]
@@ -132,31 +143,31 @@ def label(dispatches, quant_only):
     return out
 
 
-def per_kernel_durations(trace_dir, quant_only):
+def per_kernel_durations(trace_dir, group):
     rows = list(csv.DictReader(open(_one(trace_dir, "*kernel_trace.csv"))))
-    disp = label(mxf_dispatches(rows), quant_only)
+    disp = label(mxf_dispatches(rows), group)
     dur = defaultdict(list)
     for _, logical, r in disp:
         dur[logical].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     return dur
 
 
-def per_kernel_counter(pmc_dir, counter, quant_only):
+def per_kernel_counter(pmc_dir, counter, group):
     rows = [r for r in csv.DictReader(open(_one(pmc_dir, "*counter_collection.csv"))) if r["Counter_Name"] == counter]
-    disp = label(mxf_dispatches(rows), quant_only)
+    disp = label(mxf_dispatches(rows), group)
     vals = defaultdict(list)
     for _, logical, r in disp:
         vals[logical].append(float(r["Counter_Value"]))
     return vals
 
 
-def per_kernel_compute(pmc_dir, quant_only):
+def per_kernel_compute(pmc_dir, group):
     """Per logical kernel, the mean over launches of each COMPUTE_COUNTERS value."""
     rows = list(csv.DictReader(open(_one(pmc_dir, "*counter_collection.csv"))))
     out = {}
     for counter in COMPUTE_COUNTERS:
         sel = [r for r in rows if r["Counter_Name"] == counter]
-        disp = label(mxf_dispatches(sel), quant_only)
+        disp = label(mxf_dispatches(sel), group)
         vals = defaultdict(list)
         for _, logical, r in disp:
             vals[logical].append(float(r["Counter_Value"]))
@@ -196,20 +207,22 @@ def main():
     ap.add_argument("--copy-write")
     ap.add_argument("--compute")
     ap.add_argument("--quant-only", action="store_true")
+    ap.add_argument("--mfma-only", action="store_true")
     ap.add_argument("--commands", required=True)
     ap.add_argument("--out", required=True)
     args = ap.parse_args()
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     os.makedirs(args.out, exist_ok=True)
-    dur = per_kernel_durations(args.trace, args.quant_only)
+    group = "quant" if args.quant_only else "mfma" if args.mfma_only else "mlp"
+    dur = per_kernel_durations(args.trace, group)
     traffic = {}
     lines = []
     ff = wf = None
     if args.fetch and args.write and args.copy_fetch and args.copy_write:
         ff, fraw = copy_factor(args.copy_fetch, "FETCH_SIZE")
         wf, wraw = copy_factor(args.copy_write, "WRITE_SIZE")
-        fetch = per_kernel_counter(args.fetch, "FETCH_SIZE", args.quant_only)
-        write = per_kernel_counter(args.write, "WRITE_SIZE", args.quant_only)
+        fetch = per_kernel_counter(args.fetch, "FETCH_SIZE", group)
+        write = per_kernel_counter(args.write, "WRITE_SIZE", group)
         for k in dur:
             if k in fetch and k in write:
                 fb = sum(fetch[k]) / len(fetch[k]) * ff
@@ -218,14 +231,14 @@ def main():
         lines.append(f"Counter calibration (1 GiB device copy): FETCH_SIZE reads {fraw:.0f} -> x{ff:.4f} bytes per unit; "
                      f"WRITE_SIZE reads {wraw:.0f} -> x{wf:.4f} bytes per unit.")
         lines.append("")
-    comp = per_kernel_compute(args.compute, args.quant_only) if args.compute else {}
+    comp = per_kernel_compute(args.compute, group) if args.compute else {}
     cmds = open(args.commands).read().strip()
-    name = "quantize" if args.quant_only else "mlp_fwd_bwd"
+    name = {"quant": "quantize", "mfma": "mfma_ceilings", "mlp": "mlp_fwd_bwd"}[group]
     md = [f"# {name} kernels, workload `{args.workload}` (rocprofv3)", "", "Commands (run from the repository root):",
           "", "```", cmds, "```", ""] + lines
     md.append("| kernel | launches | avg us | median us | min us | max us | HBM read MB/launch | HBM write MB/launch |")
     md.append("|---|---|---|---|---|---|---|---|")
-    order = QUANT_ONLY if args.quant_only else MLP_SEQUENCE
+    order = {"quant": QUANT_ONLY, "mfma": MFMA_ONLY, "mlp": MLP_SEQUENCE}[group]
     for k in order:
         if k not in dur:
             continue
@@ -262,6 +275,9 @@ def main():
     path = os.path.join(args.out, f"{name}_{args.workload}.md")
     with open(path, "w") as f:
         f.write("\n".join(md) + "\n")
+    if not traffic and not comp:  # a trace alone: no counters to store beside the source hash
+        print(open(path).read())
+        return
     tpath = os.path.join(args.out, "traffic.json")
     t = {"kernels": {}}
     if os.path.exists(tpath):

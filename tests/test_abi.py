@@ -304,3 +304,26 @@ def test_hbm_probe_rejections_before_any_launch():
     assert st(1, None, None, 1024) == _abi.E_NULL     # write needs dst
     assert st(2, 24, 16, 1024) == _abi.E_ALIGN        # src not 16-byte aligned
     assert st(1, None, 8, 1024) == _abi.E_ALIGN       # dst not 16-byte aligned
+
+
+def test_mfma_probe_rejections_before_any_launch():
+    """Argument errors of mxf_mfma_probe are reported without touching a device."""
+    def st(mode, src, nbytes, stages, blocks, out):
+        with pytest.raises(mx.MxfError) as ei:
+            mx.mfma_probe(mode, src, nbytes, stages, blocks, out, stream=0)
+        return ei.value.status
+    ok = dict(mode=1, src=16, nbytes=1 << 21, stages=64, blocks=256, out=16)
+    assert st(**ok | dict(mode=2)) == _abi.E_ARG                 # unknown mode
+    assert st(**ok | dict(mode=-1)) == _abi.E_ARG
+    assert st(**ok | dict(nbytes=65536)) == _abi.E_SHAPE         # below the 128 KB ring seed
+    assert st(**ok | dict(nbytes=(1 << 21) + 16)) == _abi.E_SHAPE  # not whole 32 KB chunks
+    assert st(**ok | dict(nbytes=1 << 41)) == _abi.E_SHAPE       # over 2^40 bytes
+    assert st(**ok | dict(stages=0)) == _abi.E_SHAPE
+    assert st(**ok | dict(stages=63)) == _abi.E_SHAPE            # odd
+    assert st(**ok | dict(stages=(1 << 24) + 2)) == _abi.E_SHAPE
+    assert st(**ok | dict(blocks=0)) == _abi.E_SHAPE
+    assert st(**ok | dict(blocks=65536)) == _abi.E_SHAPE
+    assert st(**ok | dict(src=None)) == _abi.E_NULL
+    assert st(**ok | dict(out=None)) == _abi.E_NULL
+    assert st(**ok | dict(src=24)) == _abi.E_ALIGN
+    assert st(**ok | dict(out=8)) == _abi.E_ALIGN

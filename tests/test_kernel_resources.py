@@ -16,7 +16,7 @@ import pytest
 
 from mxfp8_mixed_precision_amd import build
 
-SOURCES = ["gemm.hip", "quantize.hip", "dispatch.hip", "hbm.hip"]
+SOURCES = ["gemm.hip", "quantize.hip", "dispatch.hip", "hbm.hip", "mfma_probe.hip"]
 LDS_LIMIT = 160 * 1024
 
 
