@@ -96,6 +96,35 @@ def test_nonfinite_block_reading():
     assert s == 255 and np.all((q & 0x7F) == 0x7F)
 
 
+def test_scale_bytes_and_nonfinite_blocks_against_torch_e8m0():
+    """The scale byte against torch's own E8M0 encoder (float8_e8m0fnu, an implementation
+    independent of the oracle's): for finite blocks the byte is the encoding of the power of two
+    2^(floor(log2 amax) - 8), clamped below at 2^-127 (byte 0); amax NaN or +Inf encodes as
+    0xFF, the E8M0 NaN. In a non-finite block every code is an E4M3 NaN (magnitude bits 0x7F,
+    which is what torch's float8_e4m3fn cast gives for an element divided by the NaN scale);
+    the sign bit follows the element (a reading: IEEE division by NaN leaves it unspecified)."""
+    rng = np.random.default_rng(3)
+    exps = rng.integers(-140, 20, size=4000)
+    v = rng.standard_normal((4000, 32)) * np.exp2(exps)[:, None]
+    v[::7, 5] = 0.0
+    v[::11] = 0.0  # all-zero blocks: byte 0 as well
+    _, s = quantize_blocks(v)
+    amax = np.max(np.abs(v), axis=1)
+    e = np.frexp(amax)[1] - 1  # floor(log2 amax), exact
+    # an all-zero block: torch encodes 0.0 as byte 0 as well
+    pw = torch.tensor(np.where(amax > 0, np.exp2((e - 8).astype(np.float64)), 0.0), dtype=torch.float64)
+    want = pw.to(torch.float32).to(torch.float8_e8m0fnu).view(torch.uint8).numpy()
+    assert np.array_equal(s, want)
+    bad = np.array([block([1.0, np.nan, -2.0]), block([np.inf, 1.0]), block([-3.0, -np.inf]),
+                    block([np.nan], fill=-1.0)])
+    q, s = quantize_blocks(bad)
+    amax_t = torch.tensor([np.nan, np.inf, np.inf, np.nan], dtype=torch.float32)
+    assert np.array_equal(s, amax_t.to(torch.float8_e8m0fnu).view(torch.uint8).numpy())
+    nan_div = (torch.tensor(bad, dtype=torch.float32) / torch.tensor(float("nan"))).to(torch.float8_e4m3fn)
+    assert np.array_equal(q & 0x7F, nan_div.view(torch.uint8).numpy() & 0x7F)
+    assert np.array_equal(q >> 7, np.signbit(bad).astype(np.uint8))
+
+
 # ----------------------------------------------------------------------------- brute force
 
 def _int_rne_e4m3(bits, byte):
