@@ -108,7 +108,7 @@ def cpu_baseline(prob):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     # 50 untimed steps (about 45 ms): after 5 the step still runs about 5% slower than after 60
     # or 200 (0.947 against 0.896 ms on one box) while the GPU's clocks settle under load
     ap.add_argument("--warmup", type=int, default=50)
