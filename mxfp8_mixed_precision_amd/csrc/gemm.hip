@@ -884,8 +884,10 @@ __device__ __forceinline__ void gemm_block(const GemmParams& p, uint32_t bid, ui
     // range, and positions go in groups of GM row tiles x all column tiles: the ~32 blocks an
     // XCD runs at once share a few A row panels and B column panels in that XCD's L2.
     // 32-bit arithmetic throughout (tile counts stay below 2^31, which the launcher checks):
-    // 64-bit divisions by run-time values cost about a microsecond per block
-    constexpr uint32_t GM = 4;
+    // 64-bit divisions by run-time values cost about a microsecond per block.
+    // GM measured per epilogue (settled clocks, GM 2, 3, 4, 8): 4 for FC1 + SwiGLU (164 against
+    // 166-168 us), 2 for the others (FC2 dgrad + dSwiGLU 131 against 133, FC2 78.3 against 78.7)
+    constexpr uint32_t GM = EPI == EPI_SWIGLU ? 4 : 2;
     const uint32_t mtu = (uint32_t)(mend / BM);
     const uint32_t ntiles = mtu * (uint32_t)ntn;
     uint32_t nfull = ntiles, rem = 0;
