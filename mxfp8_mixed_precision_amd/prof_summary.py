@@ -88,12 +88,16 @@ def code_only(text):
 
 
 def source_sha256(root):
-    """sha256 over the kernel sources (file names and code without comments)."""
+    """sha256 over the kernel sources (file names and code without comments) and the compiler
+    flags they are built with."""
+    from mxfp8_mixed_precision_amd import build
     h = hashlib.sha256()
     csrc = os.path.join(root, "mxfp8_mixed_precision_amd", "csrc")
     for n in sorted(os.listdir(csrc)):
         with open(os.path.join(csrc, n), encoding="utf-8") as f:
             h.update(n.encode() + b"\0" + code_only(f.read()).encode())
+        h.update(" ".join(build.SOURCE_FLAGS.get(n, [])).encode() + b"\0")
+    h.update(" ".join(f for f in build.HIPCC_FLAGS if not f.startswith("-I")).encode())
     return h.hexdigest()
 
 

@@ -3,7 +3,7 @@
 Every kernel of the library must run without scratch memory: a register spill turns into
 per-lane private-segment traffic through HBM (a spilled accumulator fragment in the GEMM store
 epilogue once added 16 KB of scratch writes per tile). Each kernel's LDS must also fit the
-CU's 160 KB. The sources are compiled to AMDGPU assembly with the library's own flags and the
+CU's 160 KB. The sources are compiled to AMDGPU assembly with the library's own flags (per source) and the
 code-object metadata is read back.
 """
 import os
@@ -26,7 +26,7 @@ def _kernel_metadata(src):
         pytest.skip("hipcc not available")
     with tempfile.TemporaryDirectory() as d:
         out = os.path.join(d, "k.s")
-        cmd = [hipcc] + build.HIPCC_FLAGS + ["-I", build.CSRC, "--cuda-device-only", "-S",
+        cmd = [hipcc] + build.HIPCC_FLAGS + build.SOURCE_FLAGS.get(src, []) + ["-I", build.CSRC, "--cuda-device-only", "-S",
                                              os.path.join(build.CSRC, src), "-o", out]
         r = subprocess.run(cmd, capture_output=True, text=True)
         assert r.returncode == 0, r.stderr[-2000:]
