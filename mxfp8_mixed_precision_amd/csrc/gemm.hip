@@ -964,8 +964,8 @@ __device__ __forceinline__ void gemm_block(const GemmParams& p, uint32_t bid, ui
     // Within an expert every tile streams the whole K range, so what matters is how many A
     // row panels and B column panels each XCD's L2 must hold: block l of the expert runs on
     // XCD l % 8, each XCD takes a contiguous run of positions, and positions walk the tile
-    // grid in strips 4 tiles wide across the smaller dimension, so a run covers a compact
-    // patch (for 11 x 8 tiles: 60 panel streams in all instead of 96 for whole rows).
+    // grid in strips 3 tiles wide across the smaller dimension, so a run covers a compact
+    // patch instead of whole rows of the grid.
     // 32-bit arithmetic (as in the M-grouped order)
     const uint32_t mtn = (uint32_t)(p.M / BM);
     const uint32_t per = mtn * (uint32_t)ntn;
@@ -1009,7 +1009,9 @@ __device__ __forceinline__ void gemm_block(const GemmParams& p, uint32_t bid, ui
     // strips of width W across the smaller grid dimension; the longer one runs inside a strip
     const bool mlong = mtn >= (uint32_t)ntn;
     const uint32_t nlong = mlong ? mtn : ntn, nshort = mlong ? ntn : mtn;
-    constexpr uint32_t W = 4;
+    // W measured in the merged backward launch (settled clocks, three A/B pairs): 3 gives
+    // 354.4-355.6 us against 357.8-358.5 for 4; 2 and 4 are alike, 8 is 6 us slower
+    constexpr uint32_t W = 3;
     const uint32_t nstrip = (nshort + W - 1) / W;
     const uint32_t strip = min(pos / (W * nlong), nstrip - 1);
     const uint32_t sw = min(W, nshort - strip * W);  // width of this strip
