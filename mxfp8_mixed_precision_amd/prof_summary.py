@@ -214,6 +214,8 @@ def main():
     ap.add_argument("--mfma-only", action="store_true")
     ap.add_argument("--commands", required=True)
     ap.add_argument("--out", required=True)
+    ap.add_argument("--tail", type=int, default=20,
+                    help="launches at the end of the trace averaged apart (the serial pass bench.py times)")
     args = ap.parse_args()
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     os.makedirs(args.out, exist_ok=True)
@@ -240,8 +242,9 @@ def main():
     name = {"quant": "quantize", "mfma": "mfma_ceilings", "mlp": "mlp_fwd_bwd"}[group]
     md = [f"# {name} kernels, workload `{args.workload}` (rocprofv3)", "", "Commands (run from the repository root):",
           "", "```", cmds, "```", ""] + lines
-    md.append("| kernel | launches | avg us | median us | min us | max us | HBM read MB/launch | HBM write MB/launch |")
-    md.append("|---|---|---|---|---|---|---|---|")
+    md.append(f"| kernel | launches | avg us | avg us, last {args.tail} | median us | min us | max us | "
+              "HBM read MB/launch | HBM write MB/launch |")
+    md.append("|---|---|---|---|---|---|---|---|---|")
     order = {"quant": QUANT_ONLY, "mfma": MFMA_ONLY, "mlp": MLP_SEQUENCE}[group]
     for k in order:
         if k not in dur:
@@ -251,7 +254,9 @@ def main():
         rd = f"{t['fetch_bytes'] / 1e6:.1f}" if t else "-"
         wr = f"{t['write_bytes'] / 1e6:.1f}" if t else "-"
         med = sorted(v)[len(v) // 2]
-        md.append(f"| {k} | {len(v)} | {sum(v) / len(v):.2f} | {med:.2f} | {min(v):.2f} | {max(v):.2f} | {rd} | {wr} |")
+        tl = v[-args.tail:] if args.tail > 0 else v
+        md.append(f"| {k} | {len(v)} | {sum(v) / len(v):.2f} | {sum(tl) / len(tl):.2f} | {med:.2f} | {min(v):.2f} | "
+                  f"{max(v):.2f} | {rd} | {wr} |")
     md.append("")
     if comp:
         md.append("Compute counters (one rocprofv3 --pmc pass, " + ", ".join(COMPUTE_COUNTERS) + "): MFMA busy = "
